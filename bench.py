@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert NVFP4 MoE layer on one MI355X.
+
+Default workload: the Flash-Next-shaped decode layer (H=2560, I=640, E=512
+experts, top-10, one token per step).  A step is one pass of the whole hot
+path for one token through one layer: router GEMV + top-k, NVFP4 activation
+quantizer, W4A4 expert FFN (gate/up + SiLU, down with re-quantized h), and
+the weighted combine with residual.  To keep every step's expert weights
+coming from HBM (not the 256 MB Infinity Cache or L2), the steps cycle through
+`--layers` independent resident layers and a fresh token each step; the
+sequence of steps is captured once in a HIP graph and replayed.
+
+Prints one JSON line (rank 0) with the metric, the roofline object of the
+expert FFN (the dominant kernels: all weight bytes stream through them), and
+the CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, GB/s
+METRIC = "MoE-layer tok/s + achieved HBM GB/s (decode B=1); prefill tok/s at 64k"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("common.hpp", "decode.hip"):
+        with open(os.path.join(ROOT, "quantized_moe_routed_router_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    ent = d.get(kernel_key)
+    if not ent or ent.get("source_sha") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def build_layers(wl, n_layers, dev):
+    import synth
+    import quantized_moe_routed_router_amd as moe
+    import torch
+    layers = []
+    for li in range(n_layers):
+        L = moe.Layer(wl.E, wl.H, wl.I, wl.k, device=dev)
+        L.set_router(synth.router_weights_torch(wl, li, dev))
+        for e0 in range(0, wl.E, 64):
+            e1 = min(wl.E, e0 + 64)
+            g, u, d = synth.expert_weights_torch(wl, li, e0, e1, dev)
+            L.load_experts_fp32(e0, g, u, d)
+            del g, u, d
+        layers.append(L)
+        if li % 8 == 7:
+            torch.cuda.synchronize()
+            log(f"built {li + 1}/{n_layers} layers")
+    torch.cuda.synchronize()
+    return layers
+
+
+def cpu_baseline(wl, n_tokens: int, dev):
+    """The oracle on the host: n_tokens single-token steps through layer 0
+    (router, quantizer, expert FFN with on-the-fly dequantization, combine).
+    Weight quantization (preparation) is outside the timed region."""
+    import numpy as np
+    import synth
+    from oracle import ffn as offn, router as orouter
+    W_r = synth.router_weights_torch(wl, 0, dev).cpu().numpy()
+    xs = [synth.activations_torch(wl, 1, 10_000 + i, dev).view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+          for i in range(n_tokens)]
+    need = set()
+    for x in xs:
+        ids, *_ = orouter.route(x, W_r, wl.k)
+        need.update(int(e) for e in ids[0])
+    q = {}
+    for e in sorted(need):
+        g, u, d = synth.expert_weights_torch(wl, 0, e, e + 1, dev)
+        q[e] = offn.quantize_expert(g[0].cpu().numpy(), u[0].cpu().numpy(), d[0].cpu().numpy())
+    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
+    t0 = time.perf_counter()
+    for x in xs:
+        offn.layer(x, W_r, None, q, wl.k, residual=True)
+    dt = time.perf_counter() - t0
+    return dict(value=n_tokens / dt, unit="tok/s", cores=int(threads), kind="oracle",
+                sample=f"{n_tokens} single-token decode steps through one H2560/I640/E512/k10 layer "
+                       f"(numpy oracle, fp64 matmuls on dequantized weights, {dt:.1f} s)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=960)
+    ap.add_argument("--warmup", type=int, default=96)
+    ap.add_argument("--layers", type=int, default=24, help="distinct resident layers cycled")
+    ap.add_argument("--cpu-tokens", type=int, default=6)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import quantized_moe_routed_router_amd as moe
+
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS["decode"]
+    NL = args.layers
+    moe.moe_check_capacity(0, NL * (moe.moe_packed_bytes(moe.dims(wl.E, wl.H, wl.I, wl.k), 0)
+                                    + moe.moe_packed_bytes(moe.dims(wl.E, wl.H, wl.I, wl.k), 1)))
+    log(f"building {NL} layers on the device")
+    layers = build_layers(wl, NL, dev)
+    NX = 64
+    xs = torch.stack([synth.activations_torch(wl, 1, s, dev)[0] for s in range(NX)]).view(torch.int16)
+    bufs = [L.alloc(1, prefill=False) for L in layers]
+
+    stream = torch.cuda.Stream()
+    cycle = NL * max(1, (NX // NL))            # steps per captured graph
+    def step(i):
+        li = i % NL
+        layers[li].forward(xs[i % NX:i % NX + 1], bufs[li], residual=True, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(cycle):                 # eager warm-up, also loads the code objects
+            step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(cycle):
+            step(i)
+    torch.cuda.synchronize()
+
+    reps_w = max(1, args.warmup // cycle)
+    reps = max(1, args.steps // cycle)
+    steps = reps * cycle
+    with torch.cuda.stream(stream):
+        for _ in range(reps_w):
+            g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host0 = time.perf_counter()
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / steps
+    log(f"graph: {steps} steps in {ms_total:.3f} ms (host {t_host * 1e3:.1f} ms): {ms_step * 1e3:.2f} us/step")
+
+    # ---- the dominant kernels: the expert FFN call (gate/up + down), eager,
+    # events on its own stream around each launch, cycling layers and tokens
+    n_ffn = min(400, 4 * cycle)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ffn)]
+    with torch.cuda.stream(stream):
+        for i in range(n_ffn):
+            li = i % NL
+            L, b = layers[li], bufs[li]
+            xq = (b["x_codes"], b["x_scales"], b["x_ts"])
+            evs[i][0].record(stream)
+            moe.moe_expert_ffn_decode(L.d, L.experts(), xq, b["ids"], 1, b["out"], b["ws"],
+                                      b["ws_bytes"], None, stream)
+            evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ffn_us = float(np.mean([a.elapsed_time(c) for a, c in evs[4:]])) * 1e3
+    # distinct experts per step = k (one token): all of their gate/up/down bytes
+    exp_bytes = moe.moe_packed_bytes(layers[0].d, 0) // wl.E + moe.moe_packed_bytes(layers[0].d, 1) // wl.E
+    act_bytes = wl.H // 2 + wl.H // 16 + 4 + wl.k * wl.I * 4 * 2 + wl.k * wl.H * 4
+    ffn_bytes = wl.k * exp_bytes + act_bytes
+    achieved = ffn_bytes / (ffn_us * 1e-6) / 1e9
+    log(f"expert FFN: {ffn_us:.2f} us/launch, {ffn_bytes} B -> {achieved:.0f} GB/s")
+
+    # whole step's algorithmic HBM bytes: router weights + k experts + activations
+    step_bytes = wl.E * wl.H * 4 + ffn_bytes + wl.H * 2 * 2 + wl.k * wl.H * 4
+    layer_gbps = step_bytes / (ms_step * 1e-3) / 1e9
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        bb = torch.empty_like(a)
+        for _ in range(3):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies done")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
+        cpu = cpu_baseline(wl, args.cpu_tokens, dev)
+
+    traffic = stored_traffic("ffn_decode_b1")
+    out = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_step, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": reps_w * cycle,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4-w4a4 (e2m1/e4m3 codes, f16 dot, fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": "flash_next_decode_layer_b1", "H": wl.H, "I": wl.I, "E": wl.E,
+                   "k": wl.k, "tokens_per_step": 1, "resident_layers_cycled": NL,
+                   "hip_graph": True, "achieved_layer_hbm_gbps": round(layer_gbps, 1),
+                   "layer_bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "expert FFN decode (gate_up_decode_kernel + down_decode_kernel)",
+                     "bytes_per_launch": ffn_bytes, "us_per_launch": round(ffn_us, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

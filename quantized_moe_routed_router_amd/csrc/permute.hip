@@ -1,0 +1,156 @@
+// Token-by-expert permutation: stable counting sort of the T*k (token, slot)
+// pairs by expert, so each expert's weights are read once per batch and its
+// rows form one contiguous group for the grouped GEMM.  (Every picked expert
+// is computed: forum repost, paragraph "Where it stands".)
+//
+// Three passes, no host round trip:
+//   1. per 1024-entry chunk, a histogram over experts (LDS atomics);
+//   2. per expert, the exclusive prefix of its chunk counts (chunk order), and
+//      the exclusive prefix over experts -> offsets, counts, tile prefix;
+//   3. per chunk, one wave walks its entries 64 at a time in order; equal-
+//      expert lanes are found with ballots over the id bits, so ranks inside a
+//      step and across steps keep the original order (stable).
+// Ids outside [0, E) are sorted into a trailing bin after expert E-1.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int PCH = 1024;   // entries per chunk
+
+__global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restrict__ ids, int N,
+                                                         int E, int32_t* __restrict__ chunk_counts) {
+  extern __shared__ int hist[];                        // [E+1]
+  for (int e = threadIdx.x; e <= E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * PCH;
+  for (int i = threadIdx.x; i < PCH; i += 256) {
+    const int g = base + i;
+    if (g < N) {
+      int e = ids[g];
+      if ((unsigned)e >= (unsigned)E) e = E;
+      atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += 256) chunk_counts[(size_t)blockIdx.x * (E + 1) + e] = hist[e];
+}
+
+// One thread per bin: running prefix over chunks.
+__global__ __launch_bounds__(256) void perm_chunk_scan_kernel(const int32_t* __restrict__ chunk_counts,
+                                                              int nchunks, int E,
+                                                              int32_t* __restrict__ chunk_base,
+                                                              int32_t* __restrict__ totals) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e > E) return;
+  int run = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    const size_t o = (size_t)c * (E + 1) + e;
+    const int v = chunk_counts[o];
+    chunk_base[o] = run;
+    run += v;
+  }
+  totals[e] = run;
+}
+
+// Single block: exclusive scan over bins (E+1 <= 1025 values).
+__global__ __launch_bounds__(1024) void perm_offsets_kernel(const int32_t* __restrict__ totals, int E,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ bin_start,
+                                                            int32_t* __restrict__ tile_prefix,
+                                                            int BM) {
+  __shared__ int sc[2][1056];
+  __shared__ int st[2][1056];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < 1056; e += 1024) { sc[0][e] = 0; st[0][e] = 0; }
+  __syncthreads();
+  for (int e = tid; e <= E; e += 1024) {
+    const int v = totals[e];
+    sc[0][e] = v;
+    st[0][e] = (e < E && BM > 0) ? (v + BM - 1) / BM : 0;
+  }
+  __syncthreads();
+  // Hillis-Steele inclusive scan over 1056 slots, ping-pong buffers
+  int cur = 0;
+  for (int off = 1; off < 1056; off <<= 1) {
+    for (int e = tid; e < 1056; e += 1024) {
+      sc[cur ^ 1][e] = sc[cur][e] + (e >= off ? sc[cur][e - off] : 0);
+      st[cur ^ 1][e] = st[cur][e] + (e >= off ? st[cur][e - off] : 0);
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+  for (int e = tid; e <= E; e += 1024) {
+    const int excl = e ? sc[cur][e - 1] : 0;
+    bin_start[e] = excl;
+    if (e < E) counts[e] = totals[e];
+    offsets[e] = excl;                               // offsets[E] = entries with valid ids
+    if (tile_prefix) tile_prefix[e] = e ? st[cur][e - 1] : 0;
+  }
+}
+
+__global__ __launch_bounds__(64) void perm_scatter_kernel(const int32_t* __restrict__ ids, int N, int E,
+                                                          const int32_t* __restrict__ chunk_base,
+                                                          const int32_t* __restrict__ bin_start,
+                                                          int32_t* __restrict__ perm,
+                                                          int32_t* __restrict__ inv) {
+  extern __shared__ int run[];                          // [E+1]
+  const int lane = threadIdx.x;
+  for (int e = lane; e <= E; e += 64) run[e] = 0;
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) <= E) ++nbits;                   // bins 0..E need nbits bits
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int base = blockIdx.x * PCH;
+  for (int s = 0; s < PCH; s += 64) {
+    const int g = base + s + lane;
+    const bool valid = g < N;
+    int e = valid ? ids[g] : 0;
+    if ((unsigned)e >= (unsigned)E) e = E;
+    uint64_t mask = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      mask &= bit ? m : ~m;
+    }
+    if (valid) {
+      const int rank = __popcll(mask & below);
+      const int pos = bin_start[e] + chunk_base[(size_t)blockIdx.x * (E + 1) + e] + run[e] + rank;
+      perm[pos] = g;
+      inv[g] = pos;
+      const bool last = (mask >> lane) == 1ull;        // highest lane of its group
+      if (last) run[e] += __popcll(mask);
+    }
+    __syncthreads();
+  }
+}
+
+size_t permute_workspace_bytes(int T, int k, int E) {
+  const size_t N = (size_t)T * k;
+  const size_t nch = (N + PCH - 1) / PCH;
+  return (2 * nch * (E + 1) + 2 * (size_t)(E + 1)) * sizeof(int32_t) + 256;
+}
+
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
+                          int32_t* tile_prefix, int BM, hipStream_t s) {
+  const int N = T * k;
+  const int nch = (N + PCH - 1) / PCH;
+  int32_t* cc = reinterpret_cast<int32_t*>(ws);
+  int32_t* cb = cc + (size_t)nch * (E + 1);
+  int32_t* totals = cb + (size_t)nch * (E + 1);
+  int32_t* bin_start = totals + (E + 1);
+  if (nch > 0) {
+    perm_count_kernel<<<nch, 256, (E + 1) * sizeof(int), s>>>(ids, N, E, cc);
+    perm_chunk_scan_kernel<<<(E + 1 + 255) / 256, 256, 0, s>>>(cc, nch, E, cb, totals);
+  } else {
+    perm_chunk_scan_kernel<<<(E + 1 + 255) / 256, 256, 0, s>>>(cc, 0, E, cb, totals);
+  }
+  perm_offsets_kernel<<<1, 1024, 0, s>>>(totals, E, counts, offsets, bin_start, tile_prefix, BM);
+  if (nch > 0)
+    perm_scatter_kernel<<<nch, 64, (E + 1) * sizeof(int), s>>>(ids, N, E, cb, bin_start, perm, inv);
+  return hipGetLastError();
+}
+
+}  // namespace moe

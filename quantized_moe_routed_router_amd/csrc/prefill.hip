@@ -1,0 +1,346 @@
+// Prefill expert FFN: grouped GEMMs on matrix cores over the token-by-expert
+// permutation, W4A4 NVFP4 (or 3-bit fp16-codebook gate/up weights).
+//
+// The pages: routed experts with gate/up weights and down projections, and
+// 3-bit q3_g128_fp16 codebook weights as the alternative format (release post
+// "capy-flash v0.7.1", section "What shipped"); NVFP4 activations and weights
+// on the GPU's W4A4 path (section "Why it matters").
+//
+// Pipeline (one call, no host round trip):
+//   permute   stable counting sort of the (t, slot) pairs by expert, plus the
+//             per-expert count of BM-row tiles (prefix in tile_prefix)
+//   gate/up   per (expert, 128-row tile, 128-col tile): rows are the expert's
+//             pairs (x^ rows gathered through perm), cols 64-row packed weight
+//             tiles (32 gate rows + the same 32 up rows).  Operands are
+//             dequantized into LDS as f16 (E2M1 x E4M3 is exact in f16, so is a
+//             codebook entry) and multiplied with v_mfma_f32_32x32x16_f16 in fp32.
+//             Epilogue: h = SiLU(g ts_x ts_g) * (u ts_x ts_u), fp32, sorted order.
+//   h quant   NVFP4 of each h row (one tensor scale per (t, slot) row)
+//   down      same GEMM on h^ rows; epilogue scales by ts_h ts_down and
+//             scatters o rows back to (t, slot) through perm.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int BM = 128, BN = 128, BK = 64, LDSK = BK + 8;   // +8 halves: bank spread
+constexpr int PF_THREADS = 256;
+
+struct PrefillWs {
+  int32_t* perm_ws;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv;
+  int32_t* tile_prefix;
+  float* h;
+  uint8_t* hq_codes;
+  uint8_t* hq_scales;
+  float* hq_ts;
+};
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+static PrefillWs carve(void* ws, int E, int I, int k, int T, size_t* total) {
+  const size_t N = (size_t)T * k;
+  uint8_t* p = reinterpret_cast<uint8_t*>(ws);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { uint8_t* q = p ? p + off : nullptr; off += align256(bytes); return q; };
+  PrefillWs w;
+  w.perm_ws = (int32_t*)take(permute_workspace_bytes(T, k, E));
+  w.counts = (int32_t*)take((size_t)E * 4);
+  w.offsets = (int32_t*)take((size_t)(E + 1) * 4);
+  w.perm = (int32_t*)take(N * 4);
+  w.inv = (int32_t*)take(N * 4);
+  w.tile_prefix = (int32_t*)take((size_t)(E + 1) * 4);
+  w.h = (float*)take(N * I * 4);
+  w.hq_codes = take(N * I / 2);
+  w.hq_scales = take(N * I / 16);
+  w.hq_ts = (float*)take(N * 4);
+  if (total) *total = off;
+  return w;
+}
+
+size_t prefill_workspace_bytes(int E, int H, int I, int k, int T) {
+  (void)H;
+  size_t total = 0;
+  carve(nullptr, E, I, k, T, &total);
+  return total;
+}
+
+// expert e and its local m-tile for global m-tile gm (binary search)
+__device__ __forceinline__ int find_expert(const int32_t* __restrict__ tile_prefix, int E, int gm) {
+  int lo = 0, hi = E;                       // tile_prefix[lo] <= gm < tile_prefix[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (tile_prefix[mid] <= gm) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// 32 NVFP4 elements (16 code bytes, 2 E4M3 scales) -> 32 f16 values e2m1*s
+__device__ __forceinline__ void dequant32_nvfp4(u32x4 cw, uint32_t sw, half2_t (&o)[16]) {
+  const _Float16 s0 = (_Float16)e4m3_to_f32(sw & 0xFF), s1 = (_Float16)e4m3_to_f32((sw >> 8) & 0xFF);
+  const half2_t a = {s0, s0}, b = {s1, s1};
+  o[0] = fp4x2_to_f16x2<0>(cw.x) * a; o[1] = fp4x2_to_f16x2<1>(cw.x) * a;
+  o[2] = fp4x2_to_f16x2<2>(cw.x) * a; o[3] = fp4x2_to_f16x2<3>(cw.x) * a;
+  o[4] = fp4x2_to_f16x2<0>(cw.y) * a; o[5] = fp4x2_to_f16x2<1>(cw.y) * a;
+  o[6] = fp4x2_to_f16x2<2>(cw.y) * a; o[7] = fp4x2_to_f16x2<3>(cw.y) * a;
+  o[8] = fp4x2_to_f16x2<0>(cw.z) * b; o[9] = fp4x2_to_f16x2<1>(cw.z) * b;
+  o[10] = fp4x2_to_f16x2<2>(cw.z) * b; o[11] = fp4x2_to_f16x2<3>(cw.z) * b;
+  o[12] = fp4x2_to_f16x2<0>(cw.w) * b; o[13] = fp4x2_to_f16x2<1>(cw.w) * b;
+  o[14] = fp4x2_to_f16x2<2>(cw.w) * b; o[15] = fp4x2_to_f16x2<3>(cw.w) * b;
+}
+
+// 32 codebook elements: 3-bit indices from three bit-plane words, 8 fp16
+// entries in cb (4 dwords)
+__device__ __forceinline__ void dequant32_cb(uint32_t p0, uint32_t p1, uint32_t p2, u32x4 cb,
+                                             half2_t (&o)[16]) {
+  uint32_t ent[4] = {cb.x, cb.y, cb.z, cb.w};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int b = 2 * i + h;
+      const uint32_t idx = ((p0 >> b) & 1u) | (((p1 >> b) & 1u) << 1) | (((p2 >> b) & 1u) << 2);
+      const uint32_t pair = ent[idx >> 1];
+      v[h] = (idx & 1u) ? (pair >> 16) : (pair & 0xFFFFu);
+    }
+    const uint32_t word = v[0] | (v[1] << 16);
+    o[i] = *reinterpret_cast<const half2_t*>(&word);
+  }
+}
+
+__device__ __forceinline__ void store32(_Float16* dst, const half2_t (&o)[16]) {
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = *reinterpret_cast<const u32x4*>(&o[4 * i]);
+}
+
+__device__ __forceinline__ void zero32(_Float16* dst) {
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = u32x4{0, 0, 0, 0};
+}
+
+// MODE 0: gate/up NVFP4, 1: gate/up codebook, 2: down
+template <int MODE>
+__global__ __launch_bounds__(PF_THREADS) void grouped_gemm_kernel(FfnArgs a, PrefillWs w, int n_ntiles) {
+  __shared__ __align__(16) _Float16 As[BM][LDSK];
+  __shared__ __align__(16) _Float16 Bs[BN][LDSK];
+  __shared__ int row_pos[BM];          // sorted position of each tile row, -1 if padding
+  __shared__ float row_scale[BM];      // ts of the row's activation (x or h)
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int gm = blockIdx.x / n_ntiles, nt = blockIdx.x % n_ntiles;
+  const int total_tiles = w.tile_prefix[a.E];
+  if (gm >= total_tiles) return;
+  const int e = find_expert(w.tile_prefix, a.E, gm);
+  const int mt = gm - w.tile_prefix[e];
+  const int row0 = w.offsets[e] + mt * BM, row_end = w.offsets[e + 1];
+
+  const bool down = MODE == 2;
+  const int K = down ? a.I : a.H;               // contraction length
+  const size_t w_tile_bytes = (MODE == 1) ? cb_tile_bytes(K) : tile_bytes(K);
+  const size_t w_expert_bytes = down ? down_expert_bytes(a.H, a.I)
+                                     : (MODE == 1 ? cb_gate_up_expert_bytes(a.H, a.I) : gate_up_expert_bytes(a.H, a.I));
+  const uint8_t* wbase = (down ? a.down : a.gate_up) + (size_t)e * w_expert_bytes + (size_t)(nt * 2) * w_tile_bytes;
+
+  if (tid < BM) {
+    const int pos = row0 + tid;
+    int rp = -1;
+    float sc = 0.0f;
+    if (pos < row_end) {
+      rp = pos;
+      sc = down ? w.hq_ts[pos] : a.x_ts[w.perm[pos] / a.k];
+    }
+    row_pos[tid] = rp;
+    row_scale[tid] = sc;
+  }
+  __syncthreads();
+
+  // A-load role: row ar, half ah (32 elements); B-load role: tile jj, chunk c, lane bl
+  const int ar = tid >> 1, ah = tid & 1;
+  const int arow_pos = row_pos[ar];
+  const uint8_t* acodes = nullptr;
+  const uint8_t* ascales = nullptr;
+  if (arow_pos >= 0) {
+    if (down) {
+      acodes = w.hq_codes + (size_t)arow_pos * (a.I / 2);
+      ascales = w.hq_scales + (size_t)arow_pos * (a.I / 16);
+    } else {
+      const int t = w.perm[arow_pos] / a.k;
+      acodes = a.x_codes + (size_t)t * (a.H / 2);
+      ascales = a.x_scales + (size_t)t * (a.H / 16);
+    }
+  }
+  const int bj = tid >> 7, bc = (tid >> 6) & 1, bl = tid & 63;
+  const uint8_t* btile = wbase + (size_t)bj * w_tile_bytes;
+
+  float16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    // ---- A: activation rows (NVFP4), gathered through perm
+    {
+      half2_t o[16];
+      _Float16* dst = &As[ar][32 * ah];
+      if (acodes) {
+        const int kk = k0 + 32 * ah;
+        u32x4 cw = *reinterpret_cast<const u32x4*>(acodes + kk / 2);
+        uint32_t sw = *reinterpret_cast<const uint16_t*>(ascales + kk / 16);
+        dequant32_nvfp4(cw, sw, o);
+        store32(dst, o);
+      } else {
+        zero32(dst);
+      }
+    }
+    // ---- B: packed weight tile (two 64-row tiles), chunk k0/32 + bc
+    {
+      half2_t o[16];
+      const int ck = k0 / 32 + bc;
+      if (MODE == 1) {
+        const uint8_t* grp = btile + (size_t)(ck >> 2) * cb_group_bytes();
+        const uint32_t* planes = reinterpret_cast<const uint32_t*>(grp + bl * 48);
+        const int d = ck & 3;
+        u32x4 cb = *reinterpret_cast<const u32x4*>(grp + 64 * 48 + bl * 16);
+        dequant32_cb(planes[d], planes[4 + d], planes[8 + d], cb, o);
+      } else {
+        u32x4 cw = *reinterpret_cast<const u32x4*>(btile + (size_t)ck * 1024 + bl * 16);
+        uint32_t sw = *reinterpret_cast<const uint16_t*>(btile + tile_scale_offset(K) + (size_t)(ck >> 2) * 512 + bl * 8 + (ck & 3) * 2);
+        dequant32_nvfp4(cw, sw, o);
+      }
+      store32(&Bs[bj * 64 + bl][32 * bc], o);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      half8_t af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const half8_t*>(&As[wm * 64 + i * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *reinterpret_cast<const half8_t*>(&Bs[wn * 64 + j * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue.  acc[i][j][r]: row wm*64 + i*32 + (r%4) + 8*(r/4) + 4*(lane/32),
+  // col wn*64 + j*32 + lane%32 of the 128x128 tile.
+  if (!down) {
+    const float tsg = (MODE == 0) ? a.ts_gate[e] : 1.0f;
+    const float tsu = (MODE == 0) ? a.ts_up[e] : 1.0f;
+    const int n = (nt * 2 + wn) * 32 + (lane & 31);           // h column (gate/up row)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = wm * 64 + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+        const int pos = row_pos[rl];
+        if (pos < 0) continue;
+        const float sx = row_scale[rl];
+        const float g = acc[i][0][r] * (sx * tsg);
+        const float u = acc[i][1][r] * (sx * tsu);
+        const float h = g / (1.0f + expf(-g)) * u;
+        w.h[(size_t)pos * a.I + n] = h;
+      }
+  } else {
+    const float tsd = a.ts_down[e];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = nt * BN + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * 64 + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+          const int pos = row_pos[rl];
+          if (pos < 0) continue;
+          const int pair = w.perm[pos];
+          a.out[(size_t)pair * a.H + n] = acc[i][j][r] * (row_scale[rl] * tsd);
+        }
+      }
+  }
+}
+
+// NVFP4 of each h row (sorted order), one wave per row; also the optional
+// debug copies in (t, slot) order.
+__global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, int N) {
+  const int lane = threadIdx.x & 63;
+  const int pos = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pos >= N) return;
+  if (pos >= w.offsets[a.E]) return;                     // pair with an invalid id
+  const int I = a.I, nblk = I / 16;
+  const float* hr = w.h + (size_t)pos * I;
+  const int pair = w.perm[pos];
+  float amax = 0.0f;
+  for (int c = lane; c < I; c += 64) {
+    const float v = hr[c];
+    amax = fmaxf(amax, fabsf(v));
+    if (a.dbg_h) a.dbg_h[(size_t)pair * I + c] = v;
+  }
+  amax = wave_max(amax);
+  const float ts = tensor_scale_from_amax(amax);
+  for (int b = lane; b < nblk; b += 64) {
+    float v[16];
+    const float4_t* src = reinterpret_cast<const float4_t*>(hr + b * 16);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float4_t f = src[r];
+      v[4 * r] = f.x; v[4 * r + 1] = f.y; v[4 * r + 2] = f.z; v[4 * r + 3] = f.w;
+    }
+    uint32_t pk[2];
+    const uint32_t sb = quantize_block16(v, ts, pk);
+    *reinterpret_cast<u32x2*>(w.hq_codes + (size_t)pos * (I / 2) + b * 8) = u32x2{pk[0], pk[1]};
+    w.hq_scales[(size_t)pos * nblk + b] = (uint8_t)sb;
+    if (a.dbg_h_codes) *reinterpret_cast<u32x2*>(a.dbg_h_codes + (size_t)pair * (I / 2) + b * 8) = u32x2{pk[0], pk[1]};
+    if (a.dbg_h_scales) a.dbg_h_scales[(size_t)pair * nblk + b] = (uint8_t)sb;
+  }
+  if (lane == 0) {
+    w.hq_ts[pos] = ts;
+    if (a.dbg_h_ts) a.dbg_h_ts[pair] = ts;
+  }
+}
+
+// Pairs whose id is outside [0, E): zero output rows (they sit after
+// offsets[E] in sorted order).
+__global__ void zero_invalid_kernel(FfnArgs a, PrefillWs w, int N) {
+  const int pos = w.offsets[a.E] + blockIdx.x;
+  if (pos >= N) return;
+  const int pair = w.perm[pos];
+  for (int c = threadIdx.x; c < a.H; c += blockDim.x) a.out[(size_t)pair * a.H + c] = 0.0f;
+}
+
+hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
+  const int N = a.T * a.k;
+  PrefillWs w = carve(ws, a.E, a.I, a.k, a.T, nullptr);
+  hipError_t err = launch_permute(a.ids, a.T, a.k, a.E, w.counts, w.offsets, w.perm, w.inv,
+                                  w.perm_ws, w.tile_prefix, BM, s);
+  if (err != hipSuccess) return err;
+  const int max_mtiles = (N + BM - 1) / BM + a.E;
+  const int nt_gu = (2 * a.I) / BN;                  // 64-row packed tiles, two per block
+  if (a.fmt == FMT_CB3G128)
+    grouped_gemm_kernel<1><<<max_mtiles * nt_gu, PF_THREADS, 0, s>>>(a, w, nt_gu);
+  else
+    grouped_gemm_kernel<0><<<max_mtiles * nt_gu, PF_THREADS, 0, s>>>(a, w, nt_gu);
+  h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
+  const int nt_dn = a.H / BN;
+  grouped_gemm_kernel<2><<<max_mtiles * nt_dn, PF_THREADS, 0, s>>>(a, w, nt_dn);
+  zero_invalid_kernel<<<N, 256, 0, s>>>(a, w, N);
+  return hipGetLastError();
+}
+
+}  // namespace moe

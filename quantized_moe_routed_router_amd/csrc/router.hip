@@ -1,0 +1,179 @@
+// Softmax top-k router: fp32 logits of the bf16 hidden state against fp32
+// router weights (+ optional per-expert bias), then per token the k largest
+// logits (ties to the lower expert id) and their softmax renormalised over the
+// selected k.  The pages: every token activates a subset of the experts (blog
+// "Capy Flash ...", section "Where the experts live"); picked experts are
+// ranked (forum repost, paragraph "Where it stands").
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+// ---------------------------------------------------------------- small T: GEMV
+// One wave per block, two router rows per wave, lanes along H (each lane reads
+// float4s at 4*lane + 256*i, 1 KiB per wave-wide load).  x for up to 8 tokens
+// is staged in LDS as bf16 and read back with broadcast-free strided reads.
+constexpr int RG_ROWS = 2;
+constexpr int RG_TOK = 8;
+
+__global__ __launch_bounds__(64) void router_gemv_kernel(const uint16_t* __restrict__ x,
+                                                         const float* __restrict__ W,
+                                                         const float* __restrict__ bias, int T,
+                                                         int E, int H,
+                                                         float* __restrict__ logits) {
+  extern __shared__ uint16_t xs[];                    // [RG_TOK][H]
+  const int lane = threadIdx.x;
+  const int e0 = blockIdx.x * RG_ROWS;
+  const int n4 = H / 256;                             // float4s per lane (H % 256 == 0 here)
+  for (int t0 = 0; t0 < T; t0 += RG_TOK) {
+    const int nt = min(RG_TOK, T - t0);
+    __syncthreads();
+    for (int i = lane; i < nt * H / 8; i += 64)
+      reinterpret_cast<u32x4*>(xs)[i] = reinterpret_cast<const u32x4*>(x + (size_t)t0 * H)[i];
+    __syncthreads();
+    float acc[RG_ROWS][RG_TOK];
+#pragma unroll
+    for (int r = 0; r < RG_ROWS; ++r)
+#pragma unroll
+      for (int t = 0; t < RG_TOK; ++t) acc[r][t] = 0.0f;
+    for (int i = 0; i < n4; ++i) {
+      float4_t wv[RG_ROWS];
+#pragma unroll
+      for (int r = 0; r < RG_ROWS; ++r) {
+        const int e = min(e0 + r, E - 1);
+        wv[r] = reinterpret_cast<const float4_t*>(W + (size_t)e * H)[lane + 64 * i];
+      }
+#pragma unroll
+      for (int t = 0; t < RG_TOK; ++t) {
+        if (t < nt) {
+          u32x2 xb = reinterpret_cast<const u32x2*>(xs + t * H)[lane + 64 * i];
+          float x0 = bf16_to_f32(xb.x & 0xFFFF), x1 = bf16_to_f32(xb.x >> 16);
+          float x2 = bf16_to_f32(xb.y & 0xFFFF), x3 = bf16_to_f32(xb.y >> 16);
+#pragma unroll
+          for (int r = 0; r < RG_ROWS; ++r)
+            acc[r][t] = fmaf(wv[r].w, x3, fmaf(wv[r].z, x2, fmaf(wv[r].y, x1, fmaf(wv[r].x, x0, acc[r][t]))));
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RG_ROWS; ++r) {
+      const int e = e0 + r;
+#pragma unroll
+      for (int t = 0; t < RG_TOK; ++t) {
+        float v = wave_sum(acc[r][t]);
+        if (lane == 0 && t < nt && e < E) logits[(size_t)(t0 + t) * E + e] = v + (bias ? bias[e] : 0.0f);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- large T: GEMM
+// 64 tokens x 64 experts per 256-thread block, K step 32, fp32 FMA from LDS
+// tiles; each thread owns a 4x4 patch.
+__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ W,
+                                                          const float* __restrict__ bias, int T,
+                                                          int E, int H,
+                                                          float* __restrict__ logits) {
+  __shared__ float As[32][65];
+  __shared__ float Bs[32][65];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
+  const int tr = tid / 16, tc = tid % 16;               // 16 x 16 threads, 4x4 each
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < H; k0 += 32) {
+    // A: 64 tokens x 32 k (bf16) -> As[k][t]; B: 64 experts x 32 k -> Bs[k][e]
+    for (int i = tid; i < 64 * 32; i += 256) {
+      int r = i / 32, c = i % 32;
+      int t = t0 + r, e = e0 + r;
+      As[c][r] = t < T ? bf16_to_f32(x[(size_t)t * H + k0 + c]) : 0.0f;
+      Bs[c][r] = e < E ? W[(size_t)e * H + k0 + c] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < 32; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = As[kk][tr * 4 + i]; b[i] = Bs[kk][tc * 4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int t = t0 + tr * 4 + i, e = e0 + tc * 4 + j;
+      if (t < T && e < E) logits[(size_t)t * E + e] = acc[i][j] + (bias ? bias[e] : 0.0f);
+    }
+}
+
+// ---------------------------------------------------------------- top-k
+// One wave per token.  Lane l holds logits l, l+64, ...; k rounds of a wave
+// arg-max over (value desc, id asc); then the softmax over the k winners.
+constexpr int TK_MAXPER = 16;   // E <= 1024
+
+__device__ __forceinline__ bool better(float v, int id, float v2, int id2) {
+  return v > v2 || (v == v2 && id < id2);
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int k, int32_t* __restrict__ ids,
+                                                   float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;                                  // wave-uniform; no block barrier below
+  float v[TK_MAXPER];
+  const int per = (E + 63) / 64;
+#pragma unroll
+  for (int i = 0; i < TK_MAXPER; ++i) {
+    int e = lane + 64 * i;
+    v[i] = (i < per && e < E) ? logits[(size_t)t * E + e] : -INFINITY;
+  }
+  uint32_t taken = 0;
+  float myv = 0.0f, l0 = 0.0f;
+  int myi = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < TK_MAXPER; ++i) {
+      int e = lane + 64 * i;
+      if (i < per && e < E && !((taken >> i) & 1u) && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      float ov = __shfl_xor(bv, off, 64);
+      int oi = __shfl_xor(bi, off, 64);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    // every lane now holds the round's winner
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == r) { myv = bv; myi = bi; }
+    if (r == 0) l0 = bv;
+  }
+  float z = lane < k ? expf(myv - l0) : 0.0f;
+  float sum = wave_sum(z);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = myi;
+    w[(size_t)t * k + lane] = z / sum;
+  }
+}
+
+hipError_t launch_router(const uint16_t* x, const float* W_r, const float* bias, int T, int E,
+                         int H, int k, int32_t* ids, float* w, float* logits, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (T <= 16 && H % 256 == 0 && H <= 4096) {
+    size_t lds = (size_t)RG_TOK * H * sizeof(uint16_t);
+    router_gemv_kernel<<<(E + RG_ROWS - 1) / RG_ROWS, 64, lds, s>>>(x, W_r, bias, T, E, H, logits);
+  } else {
+    router_gemm_kernel<<<dim3((E + 63) / 64, (T + 63) / 64), 256, 0, s>>>(x, W_r, bias, T, E, H, logits);
+  }
+  topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, ids, w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,108 @@
+"""GPU parity: prefill expert FFN (grouped MFMA GEMMs over the permutation),
+NVFP4 and codebook gate/up, stage by stage against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import quantized_moe_routed_router_amd as moe
+from oracle import ffn as offn, router as orouter
+from tests.gpu_helpers import (say, t2n, rowwise_rel, case, run_layer, check_stages)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.mark.parametrize("T", [1, 4, 37, 300])
+def test_prefill_tiny(T):
+    c = case("tiny", "host")
+    x = synth.activations(c.wl, T=T, stream=300 + T)
+    g = run_layer(c, x, prefill=True, residual=True)
+    say("prefill tiny", T, check_stages(c, x, g, residual=True))
+
+
+def test_prefill_matches_decode_path():
+    """Same tokens through both paths: identical ids and h^ codes (modulo
+    accumulation-order flips), outputs within fp32 accumulation noise."""
+    c = case("tiny", "host")
+    x = synth.activations(c.wl, T=16, stream=77)
+    gd = run_layer(c, x, prefill=False)
+    gp = run_layer(c, x, prefill=True)
+    assert np.array_equal(gd["ids"], gp["ids"])
+    assert rowwise_rel(gp["dbg_h"], gd["dbg_h"]).max() <= 1e-5
+    same = np.all(gd["dbg_h_codes"] == gp["dbg_h_codes"], axis=1)
+    assert same.mean() >= 0.9
+    r = rowwise_rel(gp["out"].reshape(-1, c.wl.H)[same], gd["out"].reshape(-1, c.wl.H)[same])
+    assert r.max() <= 1e-5
+
+
+def test_prefill_skewed_ids_many_tiles():
+    """One expert holds most pairs (many m-tiles, ragged last tile), others
+    few or none; includes ids outside [0, E) which give zero rows."""
+    c = case("tiny", "host")
+    T = 700
+    x = synth.activations(c.wl, T=T, stream=78)
+    r = np.random.default_rng(1)
+    ids = np.stack([np.array([5, r.integers(0, 16)]) for _ in range(T)]).astype(np.int32)
+    ids[ids[:, 1] == 5, 1] = 6
+    g = run_layer(c, x, prefill=True, ids_override=ids)
+    check_stages(c, x, g, check_tokens=range(0, T, 7))
+    ids2 = ids.copy()
+    ids2[3, 1] = -4
+    ids2[9, 0] = 16
+    g2 = run_layer(c, x, prefill=True, ids_override=ids2)
+    assert np.all(g2["out"][3, 1] == 0) and np.all(g2["out"][9, 0] == 0)
+    ok = np.ones(ids.shape, bool)
+    ok[3, 1] = ok[9, 0] = False
+    assert np.array_equal(g2["out"][ok], g["out"][ok])
+
+
+def test_prefill_codebook_tiny():
+    c = case("tiny", "host", moe.MOE_FMT_CB3G128)
+    x = synth.activations(c.wl, T=40, stream=79)
+    g = run_layer(c, x, prefill=True, residual=True)
+    say("prefill codebook tiny", check_stages(c, x, g, residual=True))
+
+
+def test_prefill_zipf_8k_sampled():
+    """The 8192-token Zipf-routed layer at full size; oracle on sampled tokens
+    (one on the most popular expert, others spread)."""
+    c = case("decode", "device")
+    wl = synth.WORKLOADS["prefill8k"]
+    c.L.set_router(torch.from_numpy(synth.router_weights(wl)).to(DEV),
+                   torch.from_numpy(synth.router_bias(wl)).to(DEV))
+    try:
+        x = synth.activations(wl, T=wl.T)
+        g = run_layer(c, x, prefill=True)
+        counts = np.bincount(g["ids"].reshape(-1), minlength=wl.E)
+        say("zipf top counts", np.sort(counts)[::-1][:5], "zero experts", int((counts == 0).sum()))
+        assert counts.max() > 1000 and (counts == 0).sum() > 100
+        top = int(counts.argmax())
+        t_top = int(np.nonzero((g["ids"] == top).any(1))[0][-1])
+        say("zipf stages", check_stages(c, x, g, check_tokens=[0, t_top, wl.T - 1]))
+        # router ids vs the oracle on the sampled tokens
+        oids, _, near, _, _ = orouter.route(x[[0, t_top]], synth.router_weights(wl), wl.k, synth.router_bias(wl))
+        for i, t in enumerate([0, t_top]):
+            if not near[i]:
+                assert set(g["ids"][t]) == set(oids[i])
+    finally:
+        c.L.set_router(torch.from_numpy(c.W_r).to(DEV), None)
+
+
+@pytest.mark.parametrize("fmt", [moe.MOE_FMT_NVFP4, moe.MOE_FMT_CB3G128])
+def test_prefill_64k_sampled(fmt):
+    """65536 tokens with uniform routing at full size (the long-prefill
+    workload); oracle on two sampled tokens, properties on all rows."""
+    c = case("decode", "device", fmt)
+    wl = synth.WORKLOADS["prefill64k"]
+    c.L.set_router(torch.from_numpy(synth.router_weights(wl)).to(DEV), None)
+    try:
+        xt = synth.activations_torch(wl, wl.T, 0, DEV)
+        xb = xt.view(torch.int16).cpu().numpy().view(np.uint16)
+        g = run_layer(c, xb, prefill=True)
+        assert np.isfinite(g["out"]).all()
+        counts = np.bincount(g["ids"].reshape(-1), minlength=wl.E)
+        assert counts.min() > 900 and counts.max() < 1700          # ~1280 each
+        say("64k stages", fmt, check_stages(c, xb, g, check_tokens=[12345, wl.T - 1]))
+    finally:
+        c.L.set_router(torch.from_numpy(c.W_r).to(DEV), None)
