@@ -112,6 +112,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=96)
     ap.add_argument("--layers", type=int, default=24, help="distinct resident layers cycled")
     ap.add_argument("--cpu-tokens", type=int, default=6)
+    ap.add_argument("--path", choices=["fused", "separate"], default="fused",
+                    help="fused: moe_layer_decode (3 kernels); separate: the 4 entry points (6 kernels)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
@@ -136,12 +138,17 @@ def main():
     NX = 64
     xs = torch.stack([synth.activations_torch(wl, 1, s, dev)[0] for s in range(NX)]).view(torch.int16)
     bufs = [L.alloc(1, prefill=False) for L in layers]
+    fbufs = [L.alloc_fused(1) for L in layers]
 
     stream = torch.cuda.Stream()
     cycle = NL * max(1, (NX // NL))            # steps per captured graph
     def step(i):
         li = i % NL
-        layers[li].forward(xs[i % NX:i % NX + 1], bufs[li], residual=True, stream=stream)
+        x = xs[i % NX:i % NX + 1]
+        if args.path == "fused":
+            layers[li].forward_fused(x, fbufs[li], residual=True, stream=stream)
+        else:
+            layers[li].forward(x, bufs[li], residual=True, stream=stream)
 
     with torch.cuda.stream(stream):
         for i in range(cycle):                 # eager warm-up, also loads the code objects
@@ -174,6 +181,10 @@ def main():
     ms_step = ms_total / steps
     log(f"graph: {steps} steps in {ms_total:.3f} ms (host {t_host * 1e3:.1f} ms): {ms_step * 1e3:.2f} us/step")
 
+    with torch.cuda.stream(stream):            # inputs of the standalone FFN calls below
+        for li in range(NL):
+            layers[li].forward(xs[li % NX:li % NX + 1], bufs[li], residual=True, stream=stream)
+    torch.cuda.synchronize()
     # ---- the dominant kernels: the expert FFN call (gate/up + down), eager,
     # events on its own stream around each launch, cycling layers and tokens
     n_ffn = min(400, 4 * cycle)
@@ -229,7 +240,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "flash_next_decode_layer_b1", "H": wl.H, "I": wl.I, "E": wl.E,
                    "k": wl.k, "tokens_per_step": 1, "resident_layers_cycled": NL,
-                   "hip_graph": True, "achieved_layer_hbm_gbps": round(layer_gbps, 1),
+                   "hip_graph": True, "path": args.path,
+                   "achieved_layer_hbm_gbps": round(layer_gbps, 1),
                    "layer_bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -151,6 +151,23 @@ int moe_expert_ffn_prefill(const moe_dims* dims, const moe_experts* experts,
                            void* ws, size_t ws_bytes, const moe_ffn_debug* dbg,
                            void* stream);
 
+/* The whole decode layer for 1 <= T <= MOE_DECODE_MAX_T tokens in three
+ * kernels: router logits + NVFP4 of x; top-k (ranked in every gate/up block)
+ * + gate/up; down + weighted combine.  Same arithmetic as moe_router_topk,
+ * moe_quantize_act, moe_expert_ffn_decode and moe_combine in sequence:
+ *   y = bf16_rne( [x if add_residual] + sum_i w_i * FFN_{ids_i}(x^) ).
+ * x [T, H] bf16 (also the residual), W_r [E, H] fp32, bias [E] or NULL,
+ * y [T, H] bf16 out; ids [T, k] int32 and w [T, k] fp32 outputs, or NULL.
+ * ws: at least moe_layer_decode_workspace_bytes(dims, T) bytes, ZERO-FILLED
+ * before its first use (it holds arrival counters that every call leaves at
+ * zero); one workspace per stream - calls sharing a workspace must not
+ * overlap.  NVFP4 gate/up only; H % 256 == 0, H <= 4096, I <= 2560. */
+size_t moe_layer_decode_workspace_bytes(const moe_dims* dims, int T);
+int moe_layer_decode(const moe_dims* dims, const moe_experts* experts, const uint16_t* x,
+                     const float* W_r, const float* bias, int T, int add_residual,
+                     uint16_t* y, int32_t* ids, float* w, void* ws, size_t ws_bytes,
+                     void* stream);
+
 /* Weighted combine (release post, "Why it matters": partial sums are kept in
  * FP32): y[t, :] = bf16_rne( r[t, :] + sum_i w[t, i] * out[t, i, :] ), summed
  * in fp32 in slot order and rounded once.  out [T, k, H] fp32, w [T, k] fp32,

@@ -73,6 +73,9 @@ _SIGS = {
                                     ctypes.POINTER(moe_actq), _P, _I, _P, _P, _SZ,
                                     ctypes.POINTER(moe_ffn_debug), _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
+    "moe_layer_decode_workspace_bytes": (_SZ, [ctypes.POINTER(moe_dims), _I]),
+    "moe_layer_decode": (_I, [ctypes.POINTER(moe_dims), ctypes.POINTER(moe_experts), _P, _P, _P, _I,
+                              _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
 }
 
@@ -202,6 +205,18 @@ def moe_expert_ffn_prefill(d: moe_dims, experts: dict, xq, ids, T: int, out, ws,
 def moe_combine(out, w, residual, T: int, k: int, H: int, y, stream=None):
     _check(lib().moe_combine(_ptr(out), _ptr(w), _ptr(residual), T, k, H, _ptr(y),
                              _stream(stream)))
+
+
+def moe_layer_decode_workspace_bytes(d: moe_dims, T: int) -> int:
+    return lib().moe_layer_decode_workspace_bytes(ctypes.byref(d), T)
+
+
+def moe_layer_decode(d: moe_dims, experts: dict, x, W_r, bias, T: int, add_residual: bool, y,
+                     ids, w, ws, ws_bytes: int, stream=None):
+    ex = _experts(experts)
+    _check(lib().moe_layer_decode(ctypes.byref(d), ctypes.byref(ex), _ptr(x), _ptr(W_r), _ptr(bias),
+                                  T, 1 if add_residual else 0, _ptr(y), _ptr(ids), _ptr(w),
+                                  _ptr(ws), ws_bytes, _stream(stream)))
 
 
 # ------------------------------------------------------------------ preparation

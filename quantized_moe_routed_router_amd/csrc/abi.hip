@@ -268,7 +268,45 @@ int moe_expert_ffn_decode(const moe_dims* d, const moe_experts* ex, const moe_ac
     return fail(MOE_ERR_UNSUPPORTED, "%s: gate/up format %d is prefill-only", fn, d->fmt_gate_up);
   if (T > 1 && d->H > 3072)
     return fail(MOE_ERR_SHAPE, "%s: H = %d above 3072 needs T = 1 (activation staging is 8*H*2 bytes of LDS)", fn, d->H);
+  if (d->H > 10240 || d->I > 2560)
+    return fail(MOE_ERR_SHAPE, "%s: H = %d, I = %d: decode takes H <= 10240, I <= 2560", fn, d->H, d->I);
   return hip_status(moe::launch_ffn_decode(make_args(d, ex, xq, ids, T, out, dbg), ws, as_stream(stream)), fn);
+}
+
+size_t moe_layer_decode_workspace_bytes(const moe_dims* d, int T) {
+  if (check_dims("moe_layer_decode_workspace_bytes", d) != MOE_OK) return 0;
+  if (T < 1 || T > MOE_DECODE_MAX_T) return 0;
+  return moe::layer_decode_workspace_bytes(d->E, d->H, d->I, d->k, T);
+}
+
+int moe_layer_decode(const moe_dims* d, const moe_experts* ex, const uint16_t* x, const float* W_r,
+                     const float* bias, int T, int add_residual, uint16_t* y, int32_t* ids, float* w,
+                     void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_layer_decode";
+  int st = check_dims(fn, d);
+  if (st) return st;
+  if (T < 1 || T > MOE_DECODE_MAX_T)
+    return fail(MOE_ERR_SHAPE, "%s: T = %d outside [1, %d]", fn, T, MOE_DECODE_MAX_T);
+  if (d->fmt_gate_up != MOE_FMT_NVFP4)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: gate/up format %d is prefill-only", fn, d->fmt_gate_up);
+  if (d->H % 256 || d->H > 4096)
+    return fail(MOE_ERR_SHAPE, "%s: H = %d must be a multiple of 256 and <= 4096", fn, d->H);
+  if (d->I > 2560) return fail(MOE_ERR_SHAPE, "%s: I = %d above 2560", fn, d->I);
+  if (T > 1 && d->H > 3072)
+    return fail(MOE_ERR_SHAPE, "%s: H = %d above 3072 needs T = 1", fn, d->H);
+  if (!ex) return fail(MOE_ERR_INVALID, "%s: experts is NULL", fn);
+  NEED_PTR(ex->gate_up); NEED_PTR(ex->down); NEED_PTR(ex->ts_gate); NEED_PTR(ex->ts_up); NEED_PTR(ex->ts_down);
+  NEED_PTR(x); NEED_PTR(W_r); OPT_PTR(bias); NEED_PTR(y); OPT_PTR(ids); OPT_PTR(w); NEED_PTR(ws);
+  const size_t need = moe::layer_decode_workspace_bytes(d->E, d->H, d->I, d->k, T);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace is %zu bytes, %zu needed for T = %d", fn, ws_bytes, need, T);
+  moe::LayerArgs L{};
+  L.E = d->E; L.H = d->H; L.I = d->I; L.k = d->k; L.T = T;
+  L.x = x; L.W_r = W_r; L.bias = bias; L.residual = add_residual != 0;
+  L.gate_up = (const uint8_t*)ex->gate_up; L.down = (const uint8_t*)ex->down;
+  L.ts_gate = ex->ts_gate; L.ts_up = ex->ts_up; L.ts_down = ex->ts_down;
+  L.y = y; L.ids_out = ids; L.w_out = w;
+  return hip_status(moe::launch_layer_decode(L, ws, as_stream(stream)), fn);
 }
 
 int moe_expert_ffn_prefill(const moe_dims* d, const moe_experts* ex, const moe_actq* xq,

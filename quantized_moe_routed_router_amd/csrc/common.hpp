@@ -117,7 +117,21 @@ __device__ __forceinline__ float tensor_scale_from_amax(float amax) {
   return amax == 0.0f ? 0.0f : __fdiv_rn(amax, TS_DIVISOR);
 }
 
+// SwiGLU gate: SiLU(g) * u with SiLU(z) = z / (1 + e^-z), fp32, hardware
+// exp and reciprocal (a few ulp; the NVFP4 quantizer downstream is exact on
+// whatever h this produces).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // ---------------------------------------------------------------- wave ops
+// Make this wave's LDS stores visible to its other lanes' later LDS loads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, WAVE));
@@ -128,6 +142,171 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, WAVE);
   return v;
+}
+
+// Cross-lane reductions on DPP (gfx9 family): quad permutes and row mirrors
+// reduce within 16-lane rows, row broadcasts (15, 31) fold the rows; lane 63
+// ends with the full-wave result, read back as a wave-uniform scalar.  Lanes
+// a DPP move does not write (masked rows) take `old`, the operation's identity.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_mov(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+template <typename Op>
+__device__ __forceinline__ int dpp_wave_reduce(int v, int ident, Op op) {
+  v = op(v, dpp_mov<0xB1>(ident, v));          // quad_perm [1,0,3,2]
+  v = op(v, dpp_mov<0x4E>(ident, v));          // quad_perm [2,3,0,1]
+  v = op(v, dpp_mov<0x141>(ident, v));         // row_half_mirror
+  v = op(v, dpp_mov<0x140>(ident, v));         // row_mirror
+  v = op(v, dpp_mov<0x142, 0xA>(ident, v));    // row_bcast:15 into rows 1, 3
+  v = op(v, dpp_mov<0x143, 0xC>(ident, v));    // row_bcast:31 into rows 2, 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ float dpp_wave_max(float v) {
+  return __int_as_float(dpp_wave_reduce(__float_as_int(v), __float_as_int(-INFINITY),
+      [](int a, int b) { return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b))); }));
+}
+
+__device__ __forceinline__ int dpp_wave_min(int v) {
+  return dpp_wave_reduce(v, 0x7FFFFFFF, [](int a, int b) { return min(a, b); });
+}
+
+__device__ __forceinline__ float dpp_wave_sum(float v) {
+  return __int_as_float(dpp_wave_reduce(__float_as_int(v), 0,
+      [](int a, int b) { return __float_as_int(__int_as_float(a) + __int_as_float(b)); }));
+}
+
+// Top-k of one token's logits by one wave; lane l holds logits l, l+64, ...
+// (E <= 1024).  Each of the k rounds takes the wave maximum (DPP), then the
+// lowest expert id holding it (exact ties go to the lower id), and retires
+// that entry.  The winners' softmax, renormalised over the k, is summed on
+// DPP as well.  Lane r < k returns winner r (descending logit order).
+constexpr int TK_MAXPER = 16;
+
+__device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, int E, int k, int lane,
+                                          int* out_id, float* out_w) {
+  float v[TK_MAXPER];
+  const int per = (E + 63) / 64;
+#pragma unroll
+  for (int i = 0; i < TK_MAXPER; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = (i < per && e < E) ? lrow[e] : -INFINITY;
+  }
+  float myv = -INFINITY, l0 = 0.0f;
+  int myi = 0;
+  for (int r = 0; r < k; ++r) {
+    float lm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < TK_MAXPER; ++i) lm = fmaxf(lm, v[i]);
+    const float M = dpp_wave_max(lm);
+    int cand = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = TK_MAXPER - 1; i >= 0; --i)
+      if (v[i] == M) cand = lane + 64 * i;
+    const int id = dpp_wave_min(cand);
+    if ((id & 63) == lane) {
+#pragma unroll
+      for (int i = 0; i < TK_MAXPER; ++i)
+        if (i == (id >> 6)) v[i] = -INFINITY;
+    }
+    if (lane == r) { myv = M; myi = id; }
+    if (r == 0) l0 = M;
+  }
+  const float z = lane < k ? expf(myv - l0) : 0.0f;
+  const float sum = dpp_wave_sum(z);
+  *out_id = myi;
+  *out_w = z / sum;
+}
+
+
+// NVFP4 of one bf16 row by one wave (one tensor scale for the row): pass 1
+// takes the row amax, pass 2 quantizes whole 16-element blocks per lane.
+__device__ __forceinline__ void quantize_row_bf16_wave(const uint16_t* __restrict__ xr, int H,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales,
+                                                       float* __restrict__ ts_out, int lane) {
+  constexpr int MAXB = 4;                             // 16-element blocks per lane held (H <= 4096)
+  const int nblk = H / 16;
+  if (nblk <= 64 * MAXB) {                            // the row fits in registers: one read
+    const int b0 = 0;
+    u32x4 raw[MAXB][2];
+#pragma unroll
+    for (int i = 0; i < MAXB; ++i) {
+      const int b = b0 + lane + 64 * i;
+      if (b < nblk) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(xr + b * 16);
+        raw[i][0] = p[0];
+        raw[i][1] = p[1];
+      }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXB; ++i) {
+      if (b0 + lane + 64 * i < nblk) {
+        const uint32_t w[8] = {raw[i][0].x, raw[i][0].y, raw[i][0].z, raw[i][0].w,
+                               raw[i][1].x, raw[i][1].y, raw[i][1].z, raw[i][1].w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          amax = fmaxf(amax, fabsf(__uint_as_float(w[k] << 16)));
+          amax = fmaxf(amax, fabsf(__uint_as_float(w[k] & 0xFFFF0000u)));
+        }
+      }
+    }
+    amax = dpp_wave_max(amax);
+    const float ts = tensor_scale_from_amax(amax);
+#pragma unroll
+    for (int i = 0; i < MAXB; ++i) {
+      const int b = b0 + lane + 64 * i;
+      if (b < nblk) {
+        const uint32_t w[8] = {raw[i][0].x, raw[i][0].y, raw[i][0].z, raw[i][0].w,
+                               raw[i][1].x, raw[i][1].y, raw[i][1].z, raw[i][1].w};
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          v[2 * k] = __uint_as_float(w[k] << 16);
+          v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+        uint32_t pk[2];
+        const uint32_t sb = quantize_block16(v, ts, pk);
+        *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{pk[0], pk[1]};
+        scales[b] = (uint8_t)sb;
+      }
+    }
+    if (lane == 0) *ts_out = ts;
+    return;
+  }
+  // rows longer than 64 * MAXB blocks: two passes over memory
+  float amax = 0.0f;
+  for (int b = lane; b < nblk; b += 64) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(xr + b * 16);
+    u32x4 a = p[0], c = p[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      amax = fmaxf(amax, fabsf(__uint_as_float(w[i] << 16)));
+      amax = fmaxf(amax, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+    }
+  }
+  amax = dpp_wave_max(amax);
+  const float ts = tensor_scale_from_amax(amax);
+  for (int b = lane; b < nblk; b += 64) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(xr + b * 16);
+    u32x4 a = p[0], c = p[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+    uint32_t pk[2];
+    const uint32_t sb = quantize_block16(v, ts, pk);
+    *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{pk[0], pk[1]};
+    scales[b] = (uint8_t)sb;
+  }
+  if (lane == 0) *ts_out = ts;
 }
 
 // E2M1 pair (one byte, low nibble first) -> f16x2, exact.

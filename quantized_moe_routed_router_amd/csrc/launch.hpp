@@ -42,6 +42,24 @@ struct FfnArgs {
 };
 
 size_t decode_workspace_bytes(int E, int H, int I, int k, int T);
+
+struct LayerArgs {
+  int E, H, I, k, T;
+  const uint16_t* x;
+  const float* W_r;
+  const float* bias;
+  bool residual;
+  const uint8_t* gate_up;
+  const uint8_t* down;
+  const float* ts_gate;
+  const float* ts_up;
+  const float* ts_down;
+  uint16_t* y;
+  int32_t* ids_out;
+  float* w_out;
+};
+size_t layer_decode_workspace_bytes(int E, int H, int I, int k, int T);
+hipError_t launch_layer_decode(const LayerArgs& L, void* ws, hipStream_t s);
 hipError_t launch_ffn_decode(const FfnArgs& a, void* ws, hipStream_t s);
 
 size_t prefill_workspace_bytes(int E, int H, int I, int k, int T);

@@ -254,8 +254,7 @@ __global__ __launch_bounds__(PF_THREADS) void grouped_gemm_kernel(FfnArgs a, Pre
         const float sx = row_scale[rl];
         const float g = acc[i][0][r] * (sx * tsg);
         const float u = acc[i][1][r] * (sx * tsu);
-        const float h = g / (1.0f + expf(-g)) * u;
-        w.h[(size_t)pos * a.I + n] = h;
+        w.h[(size_t)pos * a.I + n] = silu_mul(g, u);
       }
   } else {
     const float tsd = a.ts_down[e];

@@ -23,37 +23,8 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= T) return;
-  const uint16_t* xr = x + (size_t)row * H;
-  const int nblk = H / 16;
-  float amax = 0.0f;
-  for (int b = lane; b < nblk; b += WAVE) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(xr + b * 16);
-    u32x4 a = p[0], c = p[1];
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      amax = fmaxf(amax, fabsf(bf16_to_f32(w[i] & 0xFFFF)));
-      amax = fmaxf(amax, fabsf(bf16_to_f32(w[i] >> 16)));
-    }
-  }
-  amax = wave_max(amax);
-  const float ts = tensor_scale_from_amax(amax);
-  for (int b = lane; b < nblk; b += WAVE) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(xr + b * 16);
-    u32x4 a = p[0], c = p[1];
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[2 * i] = bf16_to_f32(w[i] & 0xFFFF);
-      v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-    }
-    uint32_t pk[2];
-    uint32_t sb = quantize_block16(v, ts, pk);
-    *reinterpret_cast<u32x2*>(codes + (size_t)row * (H / 2) + b * 8) = u32x2{pk[0], pk[1]};
-    scales[(size_t)row * nblk + b] = (uint8_t)sb;
-  }
-  if (lane == 0) ts_out[row] = ts;
+  quantize_row_bf16_wave(x + (size_t)row * H, H, codes + (size_t)row * (H / 2),
+                         scales + (size_t)row * (H / 16), ts_out + row, lane);
 }
 
 hipError_t launch_act_quant(const uint16_t* x, int T, int H, uint8_t* codes, uint8_t* scales,

@@ -10,11 +10,11 @@
 namespace moe {
 
 // ---------------------------------------------------------------- small T: GEMV
-// One wave per block, two router rows per wave, lanes along H (each lane reads
-// float4s at 4*lane + 256*i, 1 KiB per wave-wide load).  x for up to 8 tokens
-// is staged in LDS as bf16 and read back with broadcast-free strided reads.
-constexpr int RG_ROWS = 2;
+// One wave per router row (one block each), lanes along H: lane l reads
+// float4s at 4l + 256i, 1 KiB per wave-wide load, all issued before x is
+// staged.  x for up to 8 tokens at a time sits in LDS as bf16.
 constexpr int RG_TOK = 8;
+constexpr int RG_MAXF4 = 16;          // H <= 4096
 
 __global__ __launch_bounds__(64) void router_gemv_kernel(const uint16_t* __restrict__ x,
                                                          const float* __restrict__ W,
@@ -23,46 +23,34 @@ __global__ __launch_bounds__(64) void router_gemv_kernel(const uint16_t* __restr
                                                          float* __restrict__ logits) {
   extern __shared__ uint16_t xs[];                    // [RG_TOK][H]
   const int lane = threadIdx.x;
-  const int e0 = blockIdx.x * RG_ROWS;
-  const int n4 = H / 256;                             // float4s per lane (H % 256 == 0 here)
+  const int e = blockIdx.x;
+  const int n4 = H / 256;
+  float4_t wv[RG_MAXF4];
+  const float4_t* wr = reinterpret_cast<const float4_t*>(W + (size_t)e * H);
+#pragma unroll
+  for (int i = 0; i < RG_MAXF4; ++i)
+    if (i < n4) wv[i] = wr[lane + 64 * i];
+  const float be = bias ? bias[e] : 0.0f;
   for (int t0 = 0; t0 < T; t0 += RG_TOK) {
     const int nt = min(RG_TOK, T - t0);
     __syncthreads();
     for (int i = lane; i < nt * H / 8; i += 64)
       reinterpret_cast<u32x4*>(xs)[i] = reinterpret_cast<const u32x4*>(x + (size_t)t0 * H)[i];
     __syncthreads();
-    float acc[RG_ROWS][RG_TOK];
+    for (int t = 0; t < nt; ++t) {
+      float acc = 0.0f;
 #pragma unroll
-    for (int r = 0; r < RG_ROWS; ++r)
-#pragma unroll
-      for (int t = 0; t < RG_TOK; ++t) acc[r][t] = 0.0f;
-    for (int i = 0; i < n4; ++i) {
-      float4_t wv[RG_ROWS];
-#pragma unroll
-      for (int r = 0; r < RG_ROWS; ++r) {
-        const int e = min(e0 + r, E - 1);
-        wv[r] = reinterpret_cast<const float4_t*>(W + (size_t)e * H)[lane + 64 * i];
-      }
-#pragma unroll
-      for (int t = 0; t < RG_TOK; ++t) {
-        if (t < nt) {
+      for (int i = 0; i < RG_MAXF4; ++i) {
+        if (i < n4) {
           u32x2 xb = reinterpret_cast<const u32x2*>(xs + t * H)[lane + 64 * i];
-          float x0 = bf16_to_f32(xb.x & 0xFFFF), x1 = bf16_to_f32(xb.x >> 16);
-          float x2 = bf16_to_f32(xb.y & 0xFFFF), x3 = bf16_to_f32(xb.y >> 16);
-#pragma unroll
-          for (int r = 0; r < RG_ROWS; ++r)
-            acc[r][t] = fmaf(wv[r].w, x3, fmaf(wv[r].z, x2, fmaf(wv[r].y, x1, fmaf(wv[r].x, x0, acc[r][t]))));
+          acc = fmaf(wv[i].x, bf16_to_f32(xb.x & 0xFFFF), acc);
+          acc = fmaf(wv[i].y, bf16_to_f32(xb.x >> 16), acc);
+          acc = fmaf(wv[i].z, bf16_to_f32(xb.y & 0xFFFF), acc);
+          acc = fmaf(wv[i].w, bf16_to_f32(xb.y >> 16), acc);
         }
       }
-    }
-#pragma unroll
-    for (int r = 0; r < RG_ROWS; ++r) {
-      const int e = e0 + r;
-#pragma unroll
-      for (int t = 0; t < RG_TOK; ++t) {
-        float v = wave_sum(acc[r][t]);
-        if (lane == 0 && t < nt && e < E) logits[(size_t)(t0 + t) * E + e] = v + (bias ? bias[e] : 0.0f);
-      }
+      const float v = dpp_wave_sum(acc);
+      if (lane == 0) logits[(size_t)(t0 + t) * E + e] = v + be;
     }
   }
 }
@@ -112,54 +100,22 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------- top-k
-// One wave per token.  Lane l holds logits l, l+64, ...; k rounds of a wave
-// arg-max over (value desc, id asc); then the softmax over the k winners.
-constexpr int TK_MAXPER = 16;   // E <= 1024
-
-__device__ __forceinline__ bool better(float v, int id, float v2, int id2) {
-  return v > v2 || (v == v2 && id < id2);
-}
-
+// One wave per token; lane l holds logits l, l+64, ... (E <= 1024).  Each of
+// the k rounds takes the wave maximum (DPP), then the lowest expert id holding
+// it (exact ties go to the lower id), and retires that entry.  The winners'
+// softmax, renormalised over the k, is summed on DPP as well.
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;                                  // wave-uniform; no block barrier below
-  float v[TK_MAXPER];
-  const int per = (E + 63) / 64;
-#pragma unroll
-  for (int i = 0; i < TK_MAXPER; ++i) {
-    int e = lane + 64 * i;
-    v[i] = (i < per && e < E) ? logits[(size_t)t * E + e] : -INFINITY;
-  }
-  uint32_t taken = 0;
-  float myv = 0.0f, l0 = 0.0f;
-  int myi = 0;
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < TK_MAXPER; ++i) {
-      int e = lane + 64 * i;
-      if (i < per && e < E && !((taken >> i) & 1u) && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      float ov = __shfl_xor(bv, off, 64);
-      int oi = __shfl_xor(bi, off, 64);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    // every lane now holds the round's winner
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == r) { myv = bv; myi = bi; }
-    if (r == 0) l0 = bv;
-  }
-  float z = lane < k ? expf(myv - l0) : 0.0f;
-  float sum = wave_sum(z);
+  int id;
+  float wt;
+  topk_wave(logits + (size_t)t * E, E, k, lane, &id, &wt);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = myi;
-    w[(size_t)t * k + lane] = z / sum;
+    ids[(size_t)t * k + lane] = id;
+    w[(size_t)t * k + lane] = wt;
   }
 }
 
@@ -168,7 +124,7 @@ hipError_t launch_router(const uint16_t* x, const float* W_r, const float* bias,
   if (T == 0) return hipSuccess;
   if (T <= 16 && H % 256 == 0 && H <= 4096) {
     size_t lds = (size_t)RG_TOK * H * sizeof(uint16_t);
-    router_gemv_kernel<<<(E + RG_ROWS - 1) / RG_ROWS, 64, lds, s>>>(x, W_r, bias, T, E, H, logits);
+    router_gemv_kernel<<<E, 64, lds, s>>>(x, W_r, bias, T, E, H, logits);
   } else {
     router_gemm_kernel<<<dim3((E + 63) / 64, (T + 63) / 64), 256, 0, s>>>(x, W_r, bias, T, E, H, logits);
   }

@@ -7,6 +7,8 @@ library's kernels.
     layer.load_experts_fp32(e0, gate, up, down)        # quantized + packed on device
     bufs = layer.alloc(T)                              # every per-step buffer
     y = layer.forward(x_bf16, bufs, residual=True)     # router -> quant -> FFN -> combine
+    fb = layer.alloc_fused(T)                          # decode: the three-kernel layer
+    y = layer.forward_fused(x_bf16, fb, residual=True)
 """
 from __future__ import annotations
 
@@ -16,8 +18,9 @@ import torch
 
 from . import (MOE_FMT_CB3G128, MOE_FMT_NVFP4, MOE_DECODE_MAX_T, dims, moe_combine,
                moe_expert_ffn_decode, moe_expert_ffn_prefill, moe_ffn_workspace_bytes,
-               moe_pack_codebook, moe_pack_nvfp4, moe_packed_bytes, moe_quantize_act,
-               moe_quantize_weights, moe_router_topk)
+               moe_layer_decode, moe_layer_decode_workspace_bytes, moe_pack_codebook,
+               moe_pack_nvfp4, moe_packed_bytes, moe_quantize_act, moe_quantize_weights,
+               moe_router_topk)
 
 
 class Layer:
@@ -114,4 +117,22 @@ class Layer:
         ffn = moe_expert_ffn_prefill if b["prefill"] else moe_expert_ffn_decode
         ffn(self.d, self.experts(), xq, b["ids"], T, b["out"], b["ws"], b["ws_bytes"], dbg, stream)
         moe_combine(b["out"], b["w"], xb if residual else None, T, self.k, self.H, b["y"], stream)
+        return b["y"]
+
+    # -------------------------------------------------------------- fused decode
+    def alloc_fused(self, T: int) -> dict:
+        """Buffers of the three-kernel decode layer (T <= 16).  The workspace is
+        zero-filled once here; every call leaves its counters at zero."""
+        dev = self.device
+        ws_bytes = moe_layer_decode_workspace_bytes(self.d, T)
+        return dict(T=T, ws_bytes=ws_bytes,
+                    ws=torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev),
+                    ids=torch.empty((T, self.k), dtype=torch.int32, device=dev),
+                    w=torch.empty((T, self.k), dtype=torch.float32, device=dev),
+                    y=torch.empty((T, self.H), dtype=torch.int16, device=dev))
+
+    def forward_fused(self, x: torch.Tensor, b: dict, residual: bool = False, stream=None):
+        xb = x.view(torch.int16) if x.dtype == torch.bfloat16 else x
+        moe_layer_decode(self.d, self.experts(), xb, self.W_r, self.bias, b["T"], residual,
+                         b["y"], b["ids"], b["w"], b["ws"], b["ws_bytes"], stream)
         return b["y"]
