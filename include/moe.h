@@ -158,10 +158,9 @@ int moe_expert_ffn_prefill(const moe_dims* dims, const moe_experts* experts,
  *   y = bf16_rne( [x if add_residual] + sum_i w_i * FFN_{ids_i}(x^) ).
  * x [T, H] bf16 (also the residual), W_r [E, H] fp32, bias [E] or NULL,
  * y [T, H] bf16 out; ids [T, k] int32 and w [T, k] fp32 outputs, or NULL.
- * ws: at least moe_layer_decode_workspace_bytes(dims, T) bytes, ZERO-FILLED
- * before its first use (it holds arrival counters that every call leaves at
- * zero); one workspace per stream - calls sharing a workspace must not
- * overlap.  NVFP4 gate/up only; H % 256 == 0, H <= 4096, I <= 2560. */
+ * ws: at least moe_layer_decode_workspace_bytes(dims, T) bytes (contents
+ * need not be initialised); calls sharing a workspace must not overlap.
+ * NVFP4 gate/up only; H % 256 == 0, H <= 4096, I <= 2560. */
 size_t moe_layer_decode_workspace_bytes(const moe_dims* dims, int T);
 int moe_layer_decode(const moe_dims* dims, const moe_experts* experts, const uint16_t* x,
                      const float* W_r, const float* bias, int T, int add_residual,

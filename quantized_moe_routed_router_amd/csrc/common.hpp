@@ -178,48 +178,174 @@ __device__ __forceinline__ float dpp_wave_sum(float v) {
       [](int a, int b) { return __float_as_int(__int_as_float(a) + __int_as_float(b)); }));
 }
 
-// Top-k of one token's logits by one wave; lane l holds logits l, l+64, ...
-// (E <= 1024).  Each of the k rounds takes the wave maximum (DPP), then the
-// lowest expert id holding it (exact ties go to the lower id), and retires
-// that entry.  The winners' softmax, renormalised over the k, is summed on
-// DPP as well.  Lane r < k returns winner r (descending logit order).
-constexpr int TK_MAXPER = 16;
+// Top-k of one token's logits by one wave (E <= 64 * PER).  Lane l holds
+// logits l*PER .. l*PER+PER-1 as order-preserving integer keys (-0 folded into
+// +0), kept sorted descending with the lower id first among equal keys.  Each
+// of the k rounds: the wave maximum of the lanes' heads (DPP), the lowest lane
+// holding it (ballot; lower lane = lower ids, so exact ties go to the lower
+// expert id), that lane pops its head.  The winners' softmax, renormalised
+// over the k, is summed on DPP as well.  Lane r < k returns winner r.
+__device__ __forceinline__ int float_order_key(float f) {
+  const int i = __float_as_int(f + 0.0f);             // -0 -> +0
+  return i ^ ((i >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float order_key_float(int k) {
+  return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
+}
 
+template <int PER>
 __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, int E, int k, int lane,
                                           int* out_id, float* out_w) {
-  float v[TK_MAXPER];
-  const int per = (E + 63) / 64;
+  constexpr int KMIN = (int)0x80000000;
+  int key[PER], id[PER];
 #pragma unroll
-  for (int i = 0; i < TK_MAXPER; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = (i < per && e < E) ? lrow[e] : -INFINITY;
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane * PER + i;
+    id[i] = e;
+    key[i] = e < E ? float_order_key(lrow[e]) : KMIN;
   }
-  float myv = -INFINITY, l0 = 0.0f;
-  int myi = 0;
-  for (int r = 0; r < k; ++r) {
-    float lm = -INFINITY;
+  // sort descending by (key desc, id asc): odd-even transposition network
 #pragma unroll
-    for (int i = 0; i < TK_MAXPER; ++i) lm = fmaxf(lm, v[i]);
-    const float M = dpp_wave_max(lm);
-    int cand = 0x7FFFFFFF;
+  for (int pass = 0; pass < PER; ++pass) {
 #pragma unroll
-    for (int i = TK_MAXPER - 1; i >= 0; --i)
-      if (v[i] == M) cand = lane + 64 * i;
-    const int id = dpp_wave_min(cand);
-    if ((id & 63) == lane) {
-#pragma unroll
-      for (int i = 0; i < TK_MAXPER; ++i)
-        if (i == (id >> 6)) v[i] = -INFINITY;
+    for (int i = pass & 1; i + 1 < PER; i += 2) {
+      const bool sw = key[i + 1] > key[i];            // equal keys keep id order
+      const int k0 = sw ? key[i + 1] : key[i], k1 = sw ? key[i] : key[i + 1];
+      const int i0 = sw ? id[i + 1] : id[i], i1 = sw ? id[i] : id[i + 1];
+      key[i] = k0; key[i + 1] = k1; id[i] = i0; id[i + 1] = i1;
     }
-    if (lane == r) { myv = M; myi = id; }
-    if (r == 0) l0 = M;
   }
-  const float z = lane < k ? expf(myv - l0) : 0.0f;
+  int mykey = KMIN, myid = 0, key0 = 0;
+  for (int r = 0; r < k; ++r) {
+    const int M = dpp_wave_reduce(key[0], KMIN, [](int a, int b) { return max(a, b); });
+    const uint64_t hit = __ballot(key[0] == M);
+    const int wl = __ffsll((unsigned long long)hit) - 1;        // lowest lane holding M
+    const int wid = __builtin_amdgcn_readlane(id[0], wl);
+    if (lane == r) { mykey = M; myid = wid; }
+    if (r == 0) key0 = M;
+    if (lane == wl) {                                            // pop the head
+#pragma unroll
+      for (int i = 0; i + 1 < PER; ++i) { key[i] = key[i + 1]; id[i] = id[i + 1]; }
+      key[PER - 1] = KMIN;
+    }
+  }
+  const float z = lane < k ? __expf(order_key_float(mykey) - order_key_float(key0)) : 0.0f;
   const float sum = dpp_wave_sum(z);
-  *out_id = myi;
+  *out_id = myid;
   *out_w = z / sum;
 }
 
+// One router logit row (expert `row`) for T <= 16 tokens by a 256-thread
+// block: thread t reads float4s t, t+256, ... of the fp32 row (all loads
+// issued first) and the matching bf16 x; fp32 FMAs, a DPP sum per wave and a
+// fixed-order sum of the four waves through LDS (red: 4*T floats).
+constexpr int RROW_MAXF4 = 4;            // H <= 4096
+__device__ __forceinline__ void router_row_block(const uint16_t* __restrict__ x,
+                                                 const float* __restrict__ W,
+                                                 const float* __restrict__ bias, int T, int E, int H,
+                                                 int row, float* __restrict__ logits, int tid,
+                                                 float* red) {
+  const int nf4 = H / 4;
+  float4_t wv[RROW_MAXF4];
+  const float4_t* wr = reinterpret_cast<const float4_t*>(W + (size_t)row * H);
+#pragma unroll
+  for (int i = 0; i < RROW_MAXF4; ++i)
+    if (tid + 256 * i < nf4) wv[i] = wr[tid + 256 * i];
+  for (int t = 0; t < T; ++t) {
+    const u32x2* xr = reinterpret_cast<const u32x2*>(x + (size_t)t * H);
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RROW_MAXF4; ++i) {
+      if (tid + 256 * i < nf4) {
+        const u32x2 xb = xr[tid + 256 * i];
+        acc = fmaf(wv[i].x, bf16_to_f32(xb.x & 0xFFFF), acc);
+        acc = fmaf(wv[i].y, bf16_to_f32(xb.x >> 16), acc);
+        acc = fmaf(wv[i].z, bf16_to_f32(xb.y & 0xFFFF), acc);
+        acc = fmaf(wv[i].w, bf16_to_f32(xb.y >> 16), acc);
+      }
+    }
+    acc = dpp_wave_sum(acc);
+    if ((tid & 63) == 0) red[(tid >> 6) * 16 + t] = acc;
+  }
+  __syncthreads();
+  if (tid < T) {
+    const float v = ((red[tid] + red[16 + tid]) + red[32 + tid]) + red[48 + tid];
+    logits[(size_t)tid * E + row] = v + (bias ? bias[row] : 0.0f);
+  }
+}
+
+// Runtime dispatch on E (E <= 1024).
+__device__ __forceinline__ void topk_wave_any(const float* __restrict__ lrow, int E, int k, int lane,
+                                              int* out_id, float* out_w) {
+  if (E <= 64) topk_wave<1>(lrow, E, k, lane, out_id, out_w);
+  else if (E <= 128) topk_wave<2>(lrow, E, k, lane, out_id, out_w);
+  else if (E <= 256) topk_wave<4>(lrow, E, k, lane, out_id, out_w);
+  else if (E <= 512) topk_wave<8>(lrow, E, k, lane, out_id, out_w);
+  else topk_wave<16>(lrow, E, k, lane, out_id, out_w);
+}
+
+// NVFP4 of one bf16 row by a whole block (one tensor scale for the row): each
+// thread loads its 16-element blocks once, the row amax goes through DPP and
+// LDS (red: one float per wave), then each thread quantizes its blocks.
+// Every thread of the block must call it.
+__device__ __forceinline__ void quantize_row_bf16_block(const uint16_t* __restrict__ xr, int H,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales,
+                                                        float* __restrict__ ts_out, int tid,
+                                                        int nthreads, float* red) {
+  constexpr int MAXB = 4;
+  const int nblk = H / 16;
+  u32x4 raw[MAXB][2];
+#pragma unroll
+  for (int i = 0; i < MAXB; ++i) {
+    const int b = tid + nthreads * i;
+    if (b < nblk) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(xr + b * 16);
+      raw[i][0] = p[0];
+      raw[i][1] = p[1];
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < MAXB; ++i) {
+    if (tid + nthreads * i < nblk) {
+      const uint32_t w[8] = {raw[i][0].x, raw[i][0].y, raw[i][0].z, raw[i][0].w,
+                             raw[i][1].x, raw[i][1].y, raw[i][1].z, raw[i][1].w};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        amax = fmaxf(amax, fabsf(__uint_as_float(w[kk] << 16)));
+        amax = fmaxf(amax, fabsf(__uint_as_float(w[kk] & 0xFFFF0000u)));
+      }
+    }
+  }
+  amax = dpp_wave_max(amax);
+  const int nw = nthreads >> 6;
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = red[0];
+  for (int w = 1; w < nw; ++w) amax = fmaxf(amax, red[w]);
+  const float ts = tensor_scale_from_amax(amax);
+#pragma unroll
+  for (int i = 0; i < MAXB; ++i) {
+    const int b = tid + nthreads * i;
+    if (b < nblk) {
+      const uint32_t w[8] = {raw[i][0].x, raw[i][0].y, raw[i][0].z, raw[i][0].w,
+                             raw[i][1].x, raw[i][1].y, raw[i][1].z, raw[i][1].w};
+      float v[16];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        v[2 * kk] = __uint_as_float(w[kk] << 16);
+        v[2 * kk + 1] = __uint_as_float(w[kk] & 0xFFFF0000u);
+      }
+      uint32_t pk[2];
+      const uint32_t sb = quantize_block16(v, ts, pk);
+      *reinterpret_cast<u32x2*>(codes + b * 8) = u32x2{pk[0], pk[1]};
+      scales[b] = (uint8_t)sb;
+    }
+  }
+  if (tid == 0) *ts_out = ts;
+}
 
 // NVFP4 of one bf16 row by one wave (one tensor scale for the row): pass 1
 // takes the row amax, pass 2 quantizes whole 16-element blocks per lane.

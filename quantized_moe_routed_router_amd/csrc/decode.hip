@@ -22,12 +22,13 @@
 //             summed through LDS in a fixed order.  Writes raw partial dot
 //             sums per K-split (no scales).  In the fused layer it first ranks
 //             the router logits itself (every block the same, deterministic).
-//   down      block = (pair p, 64-row tile j).  Issues its weight loads, then
+//   down      block = 16 output columns of every pair (few pairs) or one
+//             (pair, 64-row tile) (many pairs).  Issues its weight loads, then
 //             finishes h from the gate/up partials (sum over splits, scales,
 //             SiLU), quantizes it to NVFP4 (bit-exact quantizer) into LDS and
-//             runs the down GEMV.  In the fused layer the last block to finish
-//             a 64-column slice of every pair also does the weighted combine of
-//             that slice (per-slice arrival counters, left at zero).
+//             runs the down GEMV.  In the fused layer the column-slice kernel
+//             also does the weighted combine of its columns; with many pairs
+//             a separate combine kernel follows.
 // The block of the first pair routed to an expert serves every pair routed
 // to it, so each distinct expert's weights are read once per call.
 #include "../../include/moe.h"
@@ -100,11 +101,12 @@ __device__ __forceinline__ void load_chunks(const uint8_t* __restrict__ tile, in
   }
 }
 
-// acc[q] += dot of this lane's row slice with activation row q (LDS, f16 A*s)
+// acc[q] += dot of this lane's row slice with activation row slot[q] (LDS,
+// f16 A*s); slot[] is wave-uniform.
 template <int CPW, int MAXP>
 __device__ __forceinline__ void dot_chunks(const u32x4 (&cw)[CPW], const uint32_t (&sw)[CPW], int c0,
                                            int nc, int n, const half2_t* __restrict__ act,
-                                           int act_stride, float (&acc)[MAXP]) {
+                                           int act_stride, const int (&slot)[MAXP], float (&acc)[MAXP]) {
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     if (i < nc) {
@@ -114,23 +116,72 @@ __device__ __forceinline__ void dot_chunks(const u32x4 (&cw)[CPW], const uint32_
       const float s0 = e4m3_to_f32(sw[i] & 0xFF), s1 = e4m3_to_f32(sw[i] >> 8);
 #pragma unroll
       for (int q = 0; q < MAXP; ++q)
-        if (q < n) acc[q] = chunk_dot(w0, w1, s0, s1, act + (size_t)q * act_stride + (c0 + i) * 16, acc[q]);
+        if (q < n) acc[q] = chunk_dot(w0, w1, s0, s1, act + (size_t)slot[q] * act_stride + (c0 + i) * 16, acc[q]);
     }
   }
 }
 
-// Pairs of expert e from qstart on, at most MAXP; returns the count, writes
-// them to list (thread 0) and the next unserved pair to *qnext.
+// All pair ids of the call in registers (lane l holds pair l + 64 i), so the
+// owner test and the pair lists come from ballots, not from dependent loads.
+constexpr int PID_CH = (MOE_DECODE_MAX_T * MOE_MAX_K + 63) / 64;    // 8 chunks of 64 pairs
+
+struct PairIds {
+  int v[PID_CH];
+};
+
+__device__ __forceinline__ PairIds load_pair_ids(const int32_t* ids, int npairs, int lane) {
+  PairIds p;
+#pragma unroll
+  for (int i = 0; i < PID_CH; ++i) {
+    const int q = lane + 64 * i;
+    p.v[i] = q < npairs ? ids[q] : 0;
+  }
+  return p;
+}
+
+// Expert of pair p (wave-uniform).
+__device__ __forceinline__ int pair_expert(const PairIds& P, int p) {
+  int sel = 0;
+#pragma unroll
+  for (int i = 0; i < PID_CH; ++i)
+    if (i == (p >> 6)) sel = P.v[i];
+  return __builtin_amdgcn_readlane(sel, p & 63);
+}
+
+// Ballot masks of the pairs routed to expert e (wave-uniform).
+__device__ __forceinline__ void pair_masks(const PairIds& P, int npairs, int e, int lane,
+                                           uint64_t (&m)[PID_CH]) {
+#pragma unroll
+  for (int i = 0; i < PID_CH; ++i) m[i] = __ballot(lane + 64 * i < npairs && P.v[i] == e);
+}
+
+__device__ __forceinline__ int first_pair(const uint64_t (&m)[PID_CH]) {
+#pragma unroll
+  for (int i = 0; i < PID_CH; ++i)
+    if (m[i]) return 64 * i + __ffsll((unsigned long long)m[i]) - 1;
+  return -1;
+}
+
+// Up to MAXP pairs from the masks at or after qstart, written to list by
+// thread 0; returns the count and the next unserved pair (or npairs).
 template <int MAXP>
-__device__ __forceinline__ int next_pairs(const int32_t* ids, int npairs, int e, int qstart,
-                                          int* list, int* qnext, int tid) {
+__device__ __forceinline__ int masked_pairs(const uint64_t (&m)[PID_CH], int npairs, int qstart,
+                                            int* list, int* qnext, int tid) {
   int n = 0;
   *qnext = npairs;
-  for (int q = qstart; q < npairs; ++q) {
-    if (ids[q] != e) continue;
-    if (n == MAXP) { *qnext = q; break; }
-    if (tid == 0) list[n] = q;
-    ++n;
+#pragma unroll
+  for (int i = 0; i < PID_CH; ++i) {
+    uint64_t mm = m[i];
+    const int lo = qstart - 64 * i;
+    if (lo >= 64) mm = 0;
+    else if (lo > 0) mm &= ~((1ull << lo) - 1ull);
+    while (mm) {
+      const int q = 64 * i + __ffsll((unsigned long long)mm) - 1;
+      if (n == MAXP) { if (*qnext == npairs) *qnext = q; mm = 0; break; }
+      if (tid == 0) list[n] = q;
+      ++n;
+      mm &= mm - 1;
+    }
   }
   return n;
 }
@@ -151,7 +202,6 @@ __host__ __device__ inline int dec_waves(int nchunk_block) {
 
 struct DecodeWs {
   float* gu;          // [KS][T*k][2][I] raw gate/up partial dot sums
-  int32_t* counters;  // [H/64] combine arrival counters (fused layer only)
 };
 
 // ---------------------------------------------------------------- gate/up
@@ -170,12 +220,17 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int npairs = a.T * a.k, p = blockIdx.x, j = blockIdx.y, split = blockIdx.z;
   const int KS = gridDim.z;
+  // x^ of every token staged once (slot t) when the call has few tokens;
+  // otherwise per batch of pairs (slot = batch index)
+  const bool by_token = a.T <= MAXP;
   const int32_t* ids;
   if (TOPK) {
+    // waves 0..T-1 rank the logits; the other waves stage x^ meanwhile
+    const int nrank = min(a.T, nw);
     for (int t = wv; t < a.T; t += nw) {
       int id;
       float wt;
-      topk_wave(logits + (size_t)t * a.E, a.E, a.k, lane, &id, &wt);
+      topk_wave_any(logits + (size_t)t * a.E, a.E, a.k, lane, &id, &wt);
       if (lane < a.k) {
         sids[t * a.k + lane] = id;
         if (p == 0 && j == 0 && split == 0) {
@@ -184,19 +239,26 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
         }
       }
     }
+    if (by_token && nrank < nw && wv >= nrank) {
+      for (int t = 0; t < a.T; ++t)
+        stage_act_f16(a.x_codes + (size_t)t * (a.H / 2), a.x_scales + (size_t)t * (a.H / 16), a.H,
+                      xs + (size_t)t * (a.H / 2), tid - 64 * nrank, blockDim.x - 64 * nrank);
+    }
     __syncthreads();
     ids = sids;
   } else {
     ids = a.ids;
   }
-  const int e = ids[p];
-  for (int q = 0; q < p; ++q)
-    if (ids[q] == e) return;                                  // another block owns e
+  const PairIds P = load_pair_ids(ids, npairs, lane);
+  const int e = pair_expert(P, p);
+  uint64_t pm[PID_CH];
+  pair_masks(P, npairs, e, lane, pm);
+  if (first_pair(pm) != p) return;                            // another block owns e
   const size_t part_stride = (size_t)npairs * 2 * a.I;
   float* gu = ws.gu + (size_t)split * part_stride;
   if ((unsigned)e >= (unsigned)a.E) {                         // not an expert: partials 0
     for (int q = p; q < npairs; ++q)
-      if (ids[q] == e && tid < 64) gu[(size_t)q * 2 * a.I + (tid >> 5) * a.I + 32 * j + (tid & 31)] = 0.0f;
+      if (((pm[q >> 6] >> (q & 63)) & 1) && tid < 64) gu[(size_t)q * 2 * a.I + (tid >> 5) * a.I + 32 * j + (tid & 31)] = 0.0f;
     return;
   }
   const uint8_t* tile = a.gate_up + (size_t)e * gate_up_expert_bytes(a.H, a.I) + (size_t)j * tile_bytes(a.H);
@@ -207,21 +269,31 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
   u32x4 cw[CPW];
   uint32_t sw[CPW];
   load_chunks<CPW>(tile, a.H, c0, nc, lane, cw, sw);          // all weight loads in flight
+  if (by_token && !(TOPK && min(a.T, nw) < nw)) {
+    for (int t = 0; t < a.T; ++t)
+      stage_act_f16(a.x_codes + (size_t)t * (a.H / 2), a.x_scales + (size_t)t * (a.H / 16), a.H,
+                    xs + (size_t)t * (a.H / 2), tid, blockDim.x);
+  }
   int qstart = p;
   while (true) {
     int qnext;
-    const int n = next_pairs<MAXP>(ids, npairs, e, qstart, list, &qnext, tid);
+    const int n = masked_pairs<MAXP>(pm, npairs, qstart, list, &qnext, tid);
     __syncthreads();
-    for (int i = 0; i < n; ++i) {
-      const int t = list[i] / a.k;
-      stage_act_f16(a.x_codes + (size_t)t * (a.H / 2), a.x_scales + (size_t)t * (a.H / 16), a.H,
-                    xs + (size_t)i * (a.H / 2), tid, blockDim.x);
+    if (!by_token) {
+      for (int i = 0; i < n; ++i) {
+        const int t = list[i] / a.k;
+        stage_act_f16(a.x_codes + (size_t)t * (a.H / 2), a.x_scales + (size_t)t * (a.H / 16), a.H,
+                      xs + (size_t)i * (a.H / 2), tid, blockDim.x);
+      }
+      __syncthreads();
     }
-    __syncthreads();
+    int slot[MAXP];
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) slot[i] = (i < n) ? (by_token ? list[i] / a.k : i) : 0;
     float acc[MAXP];
 #pragma unroll
     for (int i = 0; i < MAXP; ++i) acc[i] = 0.0f;
-    dot_chunks<CPW, MAXP>(cw, sw, c0, nc, n, xs, a.H / 2, acc);
+    dot_chunks<CPW, MAXP>(cw, sw, c0, nc, n, xs, a.H / 2, slot, acc);
 #pragma unroll
     for (int i = 0; i < MAXP; ++i) red[(wv * MAXP + i) * 64 + lane] = acc[i];
     __syncthreads();
@@ -229,8 +301,11 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
       for (int i = 0; i < n; ++i) {
         float v = 0.0f;
         for (int w = 0; w < nw; ++w) v += red[(w * MAXP + i) * 64 + lane];
-        // lane < 32: gate row 32j + lane; lane >= 32: up row 32j + lane - 32
-        gu[(size_t)list[i] * 2 * a.I + (lane >> 5) * a.I + 32 * j + (lane & 31)] = v;
+        // lane < 32: gate row 32j + lane; lane >= 32: up row 32j + lane - 32;
+        // the partial carries its tensor scales (x row, weight matrix)
+        const int q = list[i];
+        const float sc = a.x_ts[q / a.k] * (lane < 32 ? a.ts_gate[e] : a.ts_up[e]);
+        gu[(size_t)q * 2 * a.I + (lane >> 5) * a.I + 32 * j + (lane & 31)] = v * sc;
       }
     }
     if (qnext >= npairs) break;
@@ -240,10 +315,8 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
 }
 
 // ---------------------------------------------------------------- down
-template <int MAXP, int CPW, bool COMBINE>
-__global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(
-    FfnArgs a, DecodeWs ws, const float* __restrict__ w_comb, const uint16_t* __restrict__ residual,
-    uint16_t* __restrict__ y) {
+template <int MAXP, int CPW>
+__global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(FfnArgs a, DecodeWs ws) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int nw = blockDim.x >> 6;
   half2_t* hs = reinterpret_cast<half2_t*>(smem);                          // [MAXP][I/2]
@@ -251,20 +324,17 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(
   float* red = hrow + (size_t)nw * a.I;                                    // [nw][MAXP][64]
   __shared__ int list[MAXP];
   __shared__ float hts[MAXP];
-  __shared__ int last;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int npairs = a.T * a.k, p = blockIdx.x, j = blockIdx.y;
   const int KS = dec_ksplit(a.H);
-  const int e = a.ids[p];
-  for (int q = 0; q < p; ++q)
-    if (a.ids[q] == e) return;
-  int served = 0;
+  const PairIds P = load_pair_ids(a.ids, npairs, lane);
+  const int e = pair_expert(P, p);
+  uint64_t pm[PID_CH];
+  pair_masks(P, npairs, e, lane, pm);
+  if (first_pair(pm) != p) return;                            // another block owns e
   if ((unsigned)e >= (unsigned)a.E) {                         // not an expert: o = 0
     for (int q = p; q < npairs; ++q)
-      if (a.ids[q] == e) {
-        if (tid < 64) a.out[(size_t)q * a.H + 64 * j + tid] = 0.0f;
-        ++served;
-      }
+      if (((pm[q >> 6] >> (q & 63)) & 1) && tid < 64) a.out[(size_t)q * a.H + 64 * j + tid] = 0.0f;
   } else {
     const uint8_t* tile = a.down + (size_t)e * down_expert_bytes(a.H, a.I) + (size_t)j * tile_bytes(a.I);
     const int nchunk = a.I / 32;
@@ -279,13 +349,12 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(
     int qstart = p;
     while (true) {
       int qnext;
-      const int n = next_pairs<MAXP>(a.ids, npairs, e, qstart, list, &qnext, tid);
+      const int n = masked_pairs<MAXP>(pm, npairs, qstart, list, &qnext, tid);
       __syncthreads();
       // h of pair i (wave i % nw): finish the dot products, SiLU-gate, then
       // NVFP4 with the row's own tensor scale
       for (int i = wv; i < n; i += nw) {
-        const int q = list[i], t = q / a.k;
-        const float sg = a.x_ts[t] * a.ts_gate[e], su = a.x_ts[t] * a.ts_up[e];
+        const int q = list[i];
         float* hr = hrow + (size_t)wv * a.I;
         float amax = 0.0f;
         // all partial loads of a 640-column batch first, then the arithmetic
@@ -312,8 +381,6 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(
 #pragma unroll
               for (int s = 1; s < 4; ++s)
                 if (s < KS) { g += gp[r][s]; u += up[r][s]; }
-              g *= sg;
-              u *= su;
               const float h = silu_mul(g, u);
               hr[c] = h;
               amax = fmaxf(amax, fabsf(h));
@@ -348,10 +415,13 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(
         }
       }
       __syncthreads();
+      int slot[MAXP];
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) slot[i] = i;
       float acc[MAXP];
 #pragma unroll
       for (int i = 0; i < MAXP; ++i) acc[i] = 0.0f;
-      dot_chunks<CPW, MAXP>(cw, sw, c0, nc, n, hs, a.I / 2, acc);
+      dot_chunks<CPW, MAXP>(cw, sw, c0, nc, n, hs, a.I / 2, slot, acc);
 #pragma unroll
       for (int i = 0; i < MAXP; ++i) red[(wv * MAXP + i) * 64 + lane] = acc[i];
       __syncthreads();
@@ -362,78 +432,232 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(
           a.out[(size_t)list[i] * a.H + 64 * j + lane] = v * (hts[i] * a.ts_down[e]);
         }
       }
-      served += n;
       if (qnext >= npairs) break;
       qstart = qnext;
       __syncthreads();
     }
   }
-  if (COMBINE) {
-    // the block that completes this 64-column slice for all pairs combines it
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const int old = atomicAdd(ws.counters + j, served);
-      last = (old + served == npairs);
-    }
-    __syncthreads();
-    if (last) {
-      __threadfence();
-      for (int idx = tid; idx < a.T * 64; idx += blockDim.x) {
-        const int t = idx / 64, c = 64 * j + (idx & 63);
-        float acc = 0.0f;
-        for (int i = 0; i < a.k; ++i)
-          acc = fmaf(w_comb[t * a.k + i], __builtin_nontemporal_load(a.out + ((size_t)t * a.k + i) * a.H + c), acc);
-        if (residual) acc += bf16_to_f32(residual[(size_t)t * a.H + c]);
-        y[(size_t)t * a.H + c] = (uint16_t)f32_to_bf16_rne(acc);
+}
+
+// ---------------------------------------------------------------- down + combine
+// Fused layer, kernel 3, for small pair counts: a block owns 16 output
+// columns n0..n0+15 of every pair and does the weighted combine of them
+// itself, so no cross-block step is needed.  Lane (r = lane & 15, quarter
+// qt = lane >> 4) reads row n0 + r of a 64-row down tile at chunks
+// qt, qt+4, ...; the four quarters are summed with lane shuffles.  Each wave
+// owns the experts first seen at its pairs (q = wave, wave + nw, ...), issues
+// their weight loads, then rebuilds h^ of its pairs into LDS (bit-exact
+// quantizer) while the loads are in flight.
+constexpr int SL_OWN_MAX = 4;            // experts a wave can own (npairs <= SL_OWN * waves)
+constexpr int SL_CPQ = 5;                // chunks per quarter held in registers (I <= 640)
+constexpr int SL_KSMAX = 2;              // gate/up K-splits the slice kernel sums
+
+template <bool COMBINE, int SL_OWN, int JOBS>
+__global__ __launch_bounds__(512) void down_slice_kernel(FfnArgs a, DecodeWs ws,
+                                                         const float* __restrict__ w_comb,
+                                                         const uint16_t* __restrict__ residual,
+                                                         uint16_t* __restrict__ y) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nw = blockDim.x >> 6;
+  const int npairs = a.T * a.k;
+  half2_t* hs = reinterpret_cast<half2_t*>(smem);                              // [npairs][I/2]
+  float* obuf = reinterpret_cast<float*>(smem + (size_t)npairs * a.I * 2);     // [npairs][16]
+  float* bmaxs = obuf + (size_t)npairs * 16;                                   // [npairs][I/16]
+  __shared__ float hts[MOE_DECODE_MAX_T * MOE_MAX_K];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int r = lane & 15, qt = lane >> 4;
+  const int jt = n0 >> 6, lit = (n0 & 63) + r;               // down tile, lane within it
+  const int KS = dec_ksplit(a.H);
+  const int nchunk = a.I / 32;
+  // ---- the scaled gate/up partials of this thread's h jobs: loads first,
+  // they do not depend on the routing
+  const size_t part_stride = (size_t)npairs * 2 * a.I;
+  const int nblk = a.I / 16;
+  const int njobs = npairs * nblk;
+  float4_t g4[JOBS][SL_KSMAX][4], u4[JOBS][SL_KSMAX][4];
+#pragma unroll
+  for (int jj = 0; jj < JOBS; ++jj) {
+    const int job = tid + jj * blockDim.x;
+    if (job < njobs) {
+      const int q = job / nblk, b = job % nblk;
+#pragma unroll
+      for (int sp = 0; sp < SL_KSMAX; ++sp) {
+        if (sp < KS) {
+          const float4_t* gp = reinterpret_cast<const float4_t*>(ws.gu + (size_t)sp * part_stride + (size_t)q * 2 * a.I + b * 16);
+          const float4_t* upp = gp + a.I / 4;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) { g4[jj][sp][r4] = gp[r4]; u4[jj][sp][r4] = upp[r4]; }
+        }
       }
-      if (tid == 0) ws.counters[j] = 0;                       // ready for the next call
     }
+  }
+  const PairIds P = load_pair_ids(a.ids, npairs, lane);
+
+  // ---- experts owned by this wave, and their weight loads
+  int own_e[SL_OWN];
+  u32x4 cw[SL_OWN][SL_CPQ];
+  uint32_t sw[SL_OWN][SL_CPQ];
+#pragma unroll
+  for (int o = 0; o < SL_OWN; ++o) {
+    own_e[o] = -1;
+    const int q = wv + nw * o;
+    if (q < npairs) {
+      const int e = pair_expert(P, q);
+      uint64_t pm[PID_CH];
+      pair_masks(P, npairs, e, lane, pm);
+      if (first_pair(pm) == q && (unsigned)e < (unsigned)a.E) {
+        own_e[o] = e;
+        const uint8_t* tile = a.down + (size_t)e * down_expert_bytes(a.H, a.I) + (size_t)jt * tile_bytes(a.I);
+#pragma unroll
+        for (int m = 0; m < SL_CPQ; ++m) {
+          const int c = qt + 4 * m;
+          if (c < nchunk) {
+            cw[o][m] = *reinterpret_cast<const u32x4*>(tile + (size_t)c * 1024 + lit * 16);
+            sw[o][m] = *reinterpret_cast<const uint16_t*>(tile + tile_scale_offset(a.I) + (size_t)(c >> 2) * 512 + lit * 8 + (c & 3) * 2);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- h^ of every pair, element-parallel: job (pair q, 16-element block b)
+  // per thread (at most two): scaled partial sums -> h (SiLU-gated) -> block
+  // max; the row amax comes from the jobs' block maxima in LDS; then the
+  // bit-exact quantizer writes f16 A*s into LDS.  (Pairs with an id outside
+  // [0, E) have zero partials, so h = 0.)
+  float hv[JOBS][16];
+  int jq[JOBS], jb[JOBS];
+#pragma unroll
+  for (int jj = 0; jj < JOBS; ++jj) {
+    const int job = tid + jj * blockDim.x;
+    jq[jj] = -1;
+    if (job < njobs) {
+      const int q = job / nblk, b = job % nblk;
+      jq[jj] = q;
+      jb[jj] = b;
+      float bmax = 0.0f;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float g = g4[jj][0][r4][c], u = u4[jj][0][r4][c];
+#pragma unroll
+          for (int sp = 1; sp < SL_KSMAX; ++sp)
+            if (sp < KS) { g += g4[jj][sp][r4][c]; u += u4[jj][sp][r4][c]; }
+          const float h = silu_mul(g, u);
+          hv[jj][4 * r4 + c] = h;
+          bmax = fmaxf(bmax, fabsf(h));
+        }
+      }
+      bmaxs[job] = bmax;
+      if (blockIdx.x == 0 && a.dbg_h) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) a.dbg_h[(size_t)q * a.I + b * 16 + c] = hv[jj][c];
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int jj = 0; jj < JOBS; ++jj) {
+    if (jq[jj] < 0) continue;
+    const int q = jq[jj], b = jb[jj];
+    float amax = 0.0f;
+    for (int bb = 0; bb < nblk; ++bb) amax = fmaxf(amax, bmaxs[q * nblk + bb]);
+    const float ts = tensor_scale_from_amax(amax);
+    uint32_t pk[2];
+    const uint32_t sb = quantize_block16(hv[jj], ts, pk);
+    if (blockIdx.x == 0) {
+      if (a.dbg_h_codes) *reinterpret_cast<u32x2*>(a.dbg_h_codes + (size_t)q * (a.I / 2) + b * 8) = u32x2{pk[0], pk[1]};
+      if (a.dbg_h_scales) a.dbg_h_scales[(size_t)q * nblk + b] = (uint8_t)sb;
+      if (b == 0 && a.dbg_h_ts) a.dbg_h_ts[q] = ts;
+    }
+    if (b == 0) hts[q] = ts;
+    _Float16 sc = (_Float16)e4m3_to_f32(sb);
+    half2_t s2 = {sc, sc};
+    half2_t wq[8];
+    cvt16(pk[0], pk[1], wq);
+    half2_t* d = hs + (size_t)q * (a.I / 2) + b * 8;
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) d[rr] = wq[rr] * s2;
+  }
+  __syncthreads();
+
+  // ---- down dots of the owned experts for all their pairs
+#pragma unroll
+  for (int o = 0; o < SL_OWN; ++o) {
+    if (own_e[o] < 0) continue;
+    const int e = own_e[o];
+    uint64_t pm[PID_CH];
+    pair_masks(P, npairs, e, lane, pm);
+    for (int i = 0; i < PID_CH; ++i) {
+      uint64_t mm = pm[i];
+      while (mm) {
+        const int q = 64 * i + __ffsll((unsigned long long)mm) - 1;
+        mm &= mm - 1;
+        float acc = 0.0f;
+#pragma unroll
+        for (int m = 0; m < SL_CPQ; ++m) {
+          const int c = qt + 4 * m;
+          if (c < nchunk) {
+            half2_t w0[8], w1[8];
+            cvt16(cw[o][m].x, cw[o][m].y, w0);
+            cvt16(cw[o][m].z, cw[o][m].w, w1);
+            acc = chunk_dot(w0, w1, e4m3_to_f32(sw[o][m] & 0xFF), e4m3_to_f32(sw[o][m] >> 8),
+                            hs + (size_t)q * (a.I / 2) + c * 16, acc);
+          }
+        }
+        acc += __shfl_xor(acc, 16, 64);
+        acc += __shfl_xor(acc, 32, 64);
+        if (lane < 16) {
+          const float ov = acc * (hts[q] * a.ts_down[e]);
+          obuf[q * 16 + r] = ov;
+          a.out[(size_t)q * a.H + n0 + r] = ov;
+        }
+      }
+    }
+  }
+  // pairs with an id outside [0, E): o = 0
+  for (int q = tid; q < npairs; q += blockDim.x) {
+    const int e = a.ids[q];
+    if ((unsigned)e >= (unsigned)a.E) {
+      for (int rr = 0; rr < 16; ++rr) { obuf[q * 16 + rr] = 0.0f; a.out[(size_t)q * a.H + n0 + rr] = 0.0f; }
+    }
+  }
+  __syncthreads();
+
+  // ---- combine these 16 columns: fp32 in slot order, one bf16 rounding
+  if (!COMBINE) return;
+  for (int idx = tid; idx < a.T * 16; idx += blockDim.x) {
+    const int t = idx >> 4, c = idx & 15;
+    float acc = 0.0f;
+    for (int i = 0; i < a.k; ++i) acc = fmaf(w_comb[t * a.k + i], obuf[(t * a.k + i) * 16 + c], acc);
+    if (residual) acc += bf16_to_f32(residual[(size_t)t * a.H + n0 + c]);
+    y[(size_t)t * a.H + n0 + c] = (uint16_t)f32_to_bf16_rne(acc);
   }
 }
 
 // ---------------------------------------------------------------- router + x quant
-// Fused layer, kernel 1: blocks 0..E-1 compute one router logit row each
-// (all its weight loads issued first), blocks E.. quantize one token each.
-__global__ __launch_bounds__(64) void router_quant_kernel(const uint16_t* __restrict__ x,
-                                                          const float* __restrict__ W,
-                                                          const float* __restrict__ bias, int T, int E,
-                                                          int H, float* __restrict__ logits,
-                                                          uint8_t* __restrict__ xc,
-                                                          uint8_t* __restrict__ xsc,
-                                                          float* __restrict__ xts) {
-  const int lane = threadIdx.x;
+// Fused layer, kernel 1 (256 threads): blocks 0..E-1 compute one router logit
+// row each (the same routine as the standalone router), the T blocks after
+// them quantize one token row each.
+__global__ __launch_bounds__(256) void router_quant_kernel(const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ W,
+                                                           const float* __restrict__ bias, int T, int E,
+                                                           int H, float* __restrict__ logits,
+                                                           uint8_t* __restrict__ xc,
+                                                           uint8_t* __restrict__ xsc,
+                                                           float* __restrict__ xts) {
+  __shared__ float red[64];
+  const int tid = threadIdx.x;
   const int blk = blockIdx.x;
   if (blk >= E) {
     const int t = blk - E;
-    quantize_row_bf16_wave(x + (size_t)t * H, H, xc + (size_t)t * (H / 2), xsc + (size_t)t * (H / 16),
-                           xts + t, lane);
+    quantize_row_bf16_block(x + (size_t)t * H, H, xc + (size_t)t * (H / 2), xsc + (size_t)t * (H / 16),
+                            xts + t, tid, 256, red);
     return;
   }
-  constexpr int MAXF4 = 16;                                   // H <= 4096
-  const int n4 = H / 256;
-  float4_t wv[MAXF4];
-  const float4_t* wr = reinterpret_cast<const float4_t*>(W + (size_t)blk * H);
-#pragma unroll
-  for (int i = 0; i < MAXF4; ++i)
-    if (i < n4) wv[i] = wr[lane + 64 * i];
-  const float be = bias ? bias[blk] : 0.0f;
-  for (int t = 0; t < T; ++t) {
-    const u32x2* xr = reinterpret_cast<const u32x2*>(x + (size_t)t * H);
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < MAXF4; ++i) {
-      if (i < n4) {
-        const u32x2 xb = xr[lane + 64 * i];
-        acc = fmaf(wv[i].x, bf16_to_f32(xb.x & 0xFFFF), acc);
-        acc = fmaf(wv[i].y, bf16_to_f32(xb.x >> 16), acc);
-        acc = fmaf(wv[i].z, bf16_to_f32(xb.y & 0xFFFF), acc);
-        acc = fmaf(wv[i].w, bf16_to_f32(xb.y >> 16), acc);
-      }
-    }
-    const float v = dpp_wave_sum(acc);
-    if (lane == 0) logits[(size_t)t * E + blk] = v + be;
-  }
+  router_row_block(x, W, bias, T, E, H, blk, logits, tid, red);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -444,31 +668,59 @@ size_t decode_workspace_bytes(int E, int H, int I, int k, int T) {
   return al256((size_t)dec_ksplit(H) * T * k * 2 * I * sizeof(float));
 }
 
+// The down step: the 16-column slice kernel when its LDS and register
+// budget fits (then the combine can run inside it), else one block per
+// (pair, 64-row tile) followed by the combine kernel when a combine is asked for.
+static size_t slice_lds_bytes(int npairs, int I, int nw) {
+  (void)nw;
+  return (size_t)npairs * I * 2 + (size_t)npairs * 16 * 4 + (size_t)npairs * (I / 16) * 4;
+}
+static int slice_waves(int npairs) { return npairs < 8 ? npairs : 8; }
+static bool slice_fits(int npairs, int H, int I) {
+  const int nw = slice_waves(npairs);
+  return I <= 32 * 4 * SL_CPQ && H % 16 == 0 && dec_ksplit(H) <= SL_KSMAX && npairs <= SL_OWN_MAX * nw &&
+         npairs * (I / 16) <= 2 * 64 * nw && slice_lds_bytes(npairs, I, nw) <= 56 * 1024;
+}
+
 template <int MAXP, bool FUSED>
 static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logits, int32_t* ids_out,
                                float* w_out, const uint16_t* residual, uint16_t* y, hipStream_t s) {
   const int npairs = a.T * a.k;
   const int KS = dec_ksplit(a.H);
-  const int nw1 = dec_waves(a.H / 32 / KS), nw2 = dec_waves(a.I / 32);
+  const int nw1 = dec_waves(a.H / 32 / KS);
   const size_t lds1 = (size_t)MAXP * a.H * 2 + (size_t)nw1 * MAXP * 64 * 4;
-  const size_t lds2 = (size_t)MAXP * a.I * 2 + (size_t)nw2 * a.I * 4 + (size_t)nw2 * MAXP * 64 * 4;
-  const dim3 g1(npairs, a.I / 32, KS), g2(npairs, a.H / 64);
-  gate_up_decode_kernel<MAXP, DEC_CPW, FUSED><<<g1, 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out);
-  down_decode_kernel<MAXP, DEC_CPW, FUSED><<<g2, 64 * nw2, lds2, s>>>(a, ws, w_out, residual, y);
+  gate_up_decode_kernel<MAXP, DEC_CPW, FUSED><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out);
+  if (slice_fits(npairs, a.H, a.I)) {
+    const int nw = slice_waves(npairs);
+    const size_t lds = slice_lds_bytes(npairs, a.I, nw);
+    const int own = (npairs + nw - 1) / nw;
+    const int jobs = (npairs * (a.I / 16) + 64 * nw - 1) / (64 * nw);
+    if (own <= 2 && jobs <= 1) {
+      if (FUSED) down_slice_kernel<true, 2, 1><<<a.H / 16, 64 * nw, lds, s>>>(a, ws, w_out, residual, y);
+      else down_slice_kernel<false, 2, 1><<<a.H / 16, 64 * nw, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
+    } else {
+      if (FUSED) down_slice_kernel<true, 4, 2><<<a.H / 16, 64 * nw, lds, s>>>(a, ws, w_out, residual, y);
+      else down_slice_kernel<false, 4, 2><<<a.H / 16, 64 * nw, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
+    }
+  } else {
+    const int nw2 = dec_waves(a.I / 32);
+    const size_t lds2 = (size_t)MAXP * a.I * 2 + (size_t)nw2 * a.I * 4 + (size_t)nw2 * MAXP * 64 * 4;
+    down_decode_kernel<MAXP, DEC_CPW><<<dim3(npairs, a.H / 64), 64 * nw2, lds2, s>>>(a, ws);
+    if (FUSED) (void)launch_combine(a.out, w_out, residual, a.T, a.k, a.H, y, s);
+  }
 }
 
 hipError_t launch_ffn_decode(const FfnArgs& a, void* ws, hipStream_t s) {
-  DecodeWs w{reinterpret_cast<float*>(ws), nullptr};
+  DecodeWs w{reinterpret_cast<float*>(ws)};
   if (a.T == 1) launch_decode_pair<1, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
   else launch_decode_pair<8, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
   return hipGetLastError();
 }
 
-// Fused layer workspace: combine counters (first, so their offset does not
-// depend on T), logits, x^ (codes, scales, ts), gate/up partials, o.  The
-// counters must start at zero; every call leaves them at zero.
+// Fused layer workspace: logits, ids, w, x^ (codes, scales, ts), gate/up
+// partials, o.
 struct LayerWs {
-  int32_t* counters; float* logits; int32_t* ids; float* w; uint8_t* xc; uint8_t* xs; float* xts;
+  float* logits; int32_t* ids; float* w; uint8_t* xc; uint8_t* xs; float* xts;
   float* gu; float* out;
 };
 
@@ -477,7 +729,6 @@ static LayerWs carve_layer(void* ws, int E, int H, int I, int k, int T, size_t* 
   size_t off = 0;
   auto take = [&](size_t b) { uint8_t* q = p ? p + off : nullptr; off += al256(b); return q; };
   LayerWs w;
-  w.counters = (int32_t*)take((size_t)(H / 64) * 4);
   w.logits = (float*)take((size_t)T * E * 4);
   w.ids = (int32_t*)take((size_t)T * k * 4);
   w.w = (float*)take((size_t)T * k * 4);
@@ -498,7 +749,7 @@ size_t layer_decode_workspace_bytes(int E, int H, int I, int k, int T) {
 
 hipError_t launch_layer_decode(const LayerArgs& L, void* ws, hipStream_t s) {
   LayerWs w = carve_layer(ws, L.E, L.H, L.I, L.k, L.T, nullptr);
-  router_quant_kernel<<<L.E + L.T, 64, 0, s>>>(L.x, L.W_r, L.bias, L.T, L.E, L.H, w.logits, w.xc, w.xs, w.xts);
+  router_quant_kernel<<<L.E + L.T, 256, 0, s>>>(L.x, L.W_r, L.bias, L.T, L.E, L.H, w.logits, w.xc, w.xs, w.xts);
   FfnArgs a{};
   a.E = L.E; a.H = L.H; a.I = L.I; a.k = L.k; a.T = L.T; a.fmt = FMT_NVFP4;
   a.gate_up = L.gate_up; a.down = L.down;
@@ -508,7 +759,7 @@ hipError_t launch_layer_decode(const LayerArgs& L, void* ws, hipStream_t s) {
   float* w_out = L.w_out ? L.w_out : w.w;
   a.ids = ids_out;
   a.out = w.out;
-  DecodeWs dw{w.gu, w.counters};
+  DecodeWs dw{w.gu};
   const uint16_t* res = L.residual ? L.x : nullptr;
   if (L.T == 1)
     launch_decode_pair<1, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s);

@@ -10,49 +10,15 @@
 namespace moe {
 
 // ---------------------------------------------------------------- small T: GEMV
-// One wave per router row (one block each), lanes along H: lane l reads
-// float4s at 4l + 256i, 1 KiB per wave-wide load, all issued before x is
-// staged.  x for up to 8 tokens at a time sits in LDS as bf16.
-constexpr int RG_TOK = 8;
-constexpr int RG_MAXF4 = 16;          // H <= 4096
-
-__global__ __launch_bounds__(64) void router_gemv_kernel(const uint16_t* __restrict__ x,
-                                                         const float* __restrict__ W,
-                                                         const float* __restrict__ bias, int T,
-                                                         int E, int H,
-                                                         float* __restrict__ logits) {
-  extern __shared__ uint16_t xs[];                    // [RG_TOK][H]
-  const int lane = threadIdx.x;
-  const int e = blockIdx.x;
-  const int n4 = H / 256;
-  float4_t wv[RG_MAXF4];
-  const float4_t* wr = reinterpret_cast<const float4_t*>(W + (size_t)e * H);
-#pragma unroll
-  for (int i = 0; i < RG_MAXF4; ++i)
-    if (i < n4) wv[i] = wr[lane + 64 * i];
-  const float be = bias ? bias[e] : 0.0f;
-  for (int t0 = 0; t0 < T; t0 += RG_TOK) {
-    const int nt = min(RG_TOK, T - t0);
-    __syncthreads();
-    for (int i = lane; i < nt * H / 8; i += 64)
-      reinterpret_cast<u32x4*>(xs)[i] = reinterpret_cast<const u32x4*>(x + (size_t)t0 * H)[i];
-    __syncthreads();
-    for (int t = 0; t < nt; ++t) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int i = 0; i < RG_MAXF4; ++i) {
-        if (i < n4) {
-          u32x2 xb = reinterpret_cast<const u32x2*>(xs + t * H)[lane + 64 * i];
-          acc = fmaf(wv[i].x, bf16_to_f32(xb.x & 0xFFFF), acc);
-          acc = fmaf(wv[i].y, bf16_to_f32(xb.x >> 16), acc);
-          acc = fmaf(wv[i].z, bf16_to_f32(xb.y & 0xFFFF), acc);
-          acc = fmaf(wv[i].w, bf16_to_f32(xb.y >> 16), acc);
-        }
-      }
-      const float v = dpp_wave_sum(acc);
-      if (lane == 0) logits[(size_t)(t0 + t) * E + e] = v + be;
-    }
-  }
+// One 256-thread block per router row (router_row_block in common.hpp; the
+// fused decode layer uses the same routine, so both give identical logits).
+__global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ W,
+                                                          const float* __restrict__ bias, int T,
+                                                          int E, int H,
+                                                          float* __restrict__ logits) {
+  __shared__ float red[64];
+  router_row_block(x, W, bias, T, E, H, blockIdx.x, logits, threadIdx.x, red);
 }
 
 // ---------------------------------------------------------------- large T: GEMM
@@ -112,7 +78,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (t >= T) return;                                  // wave-uniform; no block barrier below
   int id;
   float wt;
-  topk_wave(logits + (size_t)t * E, E, k, lane, &id, &wt);
+  topk_wave_any(logits + (size_t)t * E, E, k, lane, &id, &wt);
   if (lane < k) {
     ids[(size_t)t * k + lane] = id;
     w[(size_t)t * k + lane] = wt;
@@ -122,9 +88,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 hipError_t launch_router(const uint16_t* x, const float* W_r, const float* bias, int T, int E,
                          int H, int k, int32_t* ids, float* w, float* logits, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (T <= 16 && H % 256 == 0 && H <= 4096) {
-    size_t lds = (size_t)RG_TOK * H * sizeof(uint16_t);
-    router_gemv_kernel<<<E, 64, lds, s>>>(x, W_r, bias, T, E, H, logits);
+  if (T <= 16 && H % 4 == 0 && H <= 4096) {
+    router_gemv_kernel<<<E, 256, 0, s>>>(x, W_r, bias, T, E, H, logits);
   } else {
     router_gemm_kernel<<<dim3((E + 63) / 64, (T + 63) / 64), 256, 0, s>>>(x, W_r, bias, T, E, H, logits);
   }

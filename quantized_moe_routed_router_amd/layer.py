@@ -121,12 +121,11 @@ class Layer:
 
     # -------------------------------------------------------------- fused decode
     def alloc_fused(self, T: int) -> dict:
-        """Buffers of the three-kernel decode layer (T <= 16).  The workspace is
-        zero-filled once here; every call leaves its counters at zero."""
+        """Buffers of the fused decode layer (T <= 16)."""
         dev = self.device
         ws_bytes = moe_layer_decode_workspace_bytes(self.d, T)
         return dict(T=T, ws_bytes=ws_bytes,
-                    ws=torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev),
+                    ws=torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev),
                     ids=torch.empty((T, self.k), dtype=torch.int32, device=dev),
                     w=torch.empty((T, self.k), dtype=torch.float32, device=dev),
                     y=torch.empty((T, self.H), dtype=torch.int16, device=dev))
