@@ -77,6 +77,64 @@ def build_layers(wl, n_layers, dev):
     return layers
 
 
+def prefill_64k(L0, dev, steps: int):
+    """The 65,536-token prefill layer (uniform routing): router GEMM + top-k,
+    x quantizer, grouped-GEMM expert FFN (NVFP4; then the 3-bit codebook
+    gate/up variant), combine.  Whole-layer tok/s and the expert FFN's share
+    of dense f16 MFMA peak (2.5 PFLOP/s)."""
+    import torch
+    import synth
+    import quantized_moe_routed_router_amd as moe
+    wl = synth.WORKLOADS["prefill64k"]
+    T = wl.T
+    res = {}
+    cb = moe.Layer(wl.E, wl.H, wl.I, wl.k, fmt_gate_up=moe.MOE_FMT_CB3G128, device=dev)
+    for e0 in range(0, wl.E, 64):
+        e1 = min(wl.E, e0 + 64)
+        _, _, d = synth.expert_weights_torch(wl, 0, e0, e1, dev)
+        cb.load_experts_fp32(e0, None, None, d)
+        g = synth.codebook_weights_torch(wl, 0, e0, e1, synth.PROJ_GATE, dev)
+        u = synth.codebook_weights_torch(wl, 0, e0, e1, synth.PROJ_UP, dev)
+        cb.load_codebook(e0, g[0], g[1], u[0], u[1])
+        del g, u, d
+    W_r = synth.router_weights_torch(wl, 0, dev)
+    x = synth.activations_torch(wl, T, 0, dev).view(torch.int16)
+    flops = 2.0 * T * wl.k * 3 * wl.H * wl.I
+    for name, L in (("nvfp4", L0), ("codebook_gate_up", cb)):
+        L.set_router(W_r)
+        b = L.alloc(T, prefill=True)
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                L.forward(x, b, residual=True, stream=stream)
+        torch.cuda.synchronize()
+        e0_, e1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0_.record(stream)
+        with torch.cuda.stream(stream):
+            for _ in range(steps):
+                L.forward(x, b, residual=True, stream=stream)
+        e1_.record(stream)
+        xq = (b["x_codes"], b["x_scales"], b["x_ts"])
+        f0.record(stream)
+        for _ in range(steps):
+            moe.moe_expert_ffn_prefill(L.d, L.experts(), xq, b["ids"], T, b["out"], b["ws"],
+                                       b["ws_bytes"], None, stream)
+        f1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0_.elapsed_time(e1_) / steps
+        ffn_ms = f0.elapsed_time(f1) / steps
+        res[name] = {"tok_s": round(T / (ms * 1e-3), 1), "ms_per_layer": round(ms, 3),
+                     "expert_ffn_ms": round(ffn_ms, 3),
+                     "expert_ffn_mfma_frac": round(flops / (ffn_ms * 1e-3) / 2.5e15, 4)}
+        log(f"prefill 64k {name}: {ms:.2f} ms/layer ({T / ms * 1e3:.0f} tok/s), expert FFN {ffn_ms:.2f} ms")
+        del b
+        torch.cuda.empty_cache()
+    del cb
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, n_tokens: int, dev):
     """The oracle on the host: n_tokens single-token steps through layer 0
     (router, quantizer, expert FFN with on-the-fly dequantization, combine).
@@ -115,6 +173,8 @@ def main():
     ap.add_argument("--path", choices=["fused", "separate"], default="fused",
                     help="fused: moe_layer_decode (3 kernels); separate: the 4 entry points (6 kernels)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 65,536-token prefill figures")
+    ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -219,6 +279,10 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device copies done")
 
+    prefill = None
+    if not args.no_prefill:
+        prefill = prefill_64k(layers[0], dev, args.prefill_steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
@@ -248,6 +312,7 @@ def main():
                      "traffic": traffic, "kernel": "expert FFN decode (gate_up_decode_kernel + down_decode_kernel)",
                      "bytes_per_launch": ffn_bytes, "us_per_launch": round(ffn_us, 3)},
         "cpu_baseline": cpu,
+        "prefill_64k": prefill,
     }
     print(json.dumps(out), flush=True)
 

@@ -180,11 +180,15 @@ __device__ __forceinline__ float dpp_wave_sum(float v) {
 
 // Top-k of one token's logits by one wave (E <= 64 * PER).  Lane l holds
 // logits l*PER .. l*PER+PER-1 as order-preserving integer keys (-0 folded into
-// +0), kept sorted descending with the lower id first among equal keys.  Each
-// of the k rounds: the wave maximum of the lanes' heads (DPP), the lowest lane
-// holding it (ballot; lower lane = lower ids, so exact ties go to the lower
-// expert id), that lane pops its head.  The winners' softmax, renormalised
-// over the k, is summed on DPP as well.  Lane r < k returns winner r.
+// +0), sorted descending with the lower id first among equal keys.  Each of
+// the k rounds: the wave maximum M of the lanes' heads (DPP), the lowest lane
+// whose head equals M (ballot; lower lane = lower ids, so exact ties go to the
+// lower expert id) pops its head and writes the head's id to LDS slot 64 + r
+// (every other lane writes its own dummy slot, so the store needs no exec
+// mask).  Keys and ids live in vector registers (ext_vector), which keeps the
+// compiler from turning the selects into indexed private-array accesses.
+// The winners' softmax, renormalised over the k, is summed on DPP as well.
+// Lane r < k returns winner r.  scr: 64 + k ints of LDS owned by this wave.
 __device__ __forceinline__ int float_order_key(float f) {
   const int i = __float_as_int(f + 0.0f);             // -0 -> +0
   return i ^ ((i >> 31) & 0x7FFFFFFF);
@@ -195,43 +199,60 @@ __device__ __forceinline__ float order_key_float(int k) {
 
 template <int PER>
 __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, int E, int k, int lane,
-                                          int* out_id, float* out_w) {
+                                          int* scr, int* out_id, float* out_w) {
+  typedef int ivec __attribute__((ext_vector_type(PER)));
   constexpr int KMIN = (int)0x80000000;
-  int key[PER], id[PER];
+  ivec key, id;
+  if (E == 64 * PER) {                       // full lanes: plain loads, all in flight at once
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane * PER + i;
-    id[i] = e;
-    key[i] = e < E ? float_order_key(lrow[e]) : KMIN;
+    for (int i = 0; i < PER; ++i) {
+      id[i] = lane * PER + i;
+      key[i] = float_order_key(lrow[lane * PER + i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane * PER + i;
+      id[i] = e;
+      key[i] = e < E ? float_order_key(lrow[e]) : KMIN;
+    }
   }
   // sort descending by (key desc, id asc): odd-even transposition network
 #pragma unroll
   for (int pass = 0; pass < PER; ++pass) {
 #pragma unroll
     for (int i = pass & 1; i + 1 < PER; i += 2) {
-      const bool sw = key[i + 1] > key[i];            // equal keys keep id order
-      const int k0 = sw ? key[i + 1] : key[i], k1 = sw ? key[i] : key[i + 1];
-      const int i0 = sw ? id[i + 1] : id[i], i1 = sw ? id[i] : id[i + 1];
-      key[i] = k0; key[i + 1] = k1; id[i] = i0; id[i + 1] = i1;
+      const int a = key[i], b = key[i + 1], ia = id[i], ib = id[i + 1];
+      const bool sw = b > a;                           // equal keys keep id order
+      key[i] = sw ? b : a;
+      key[i + 1] = sw ? a : b;
+      id[i] = sw ? ib : ia;
+      id[i + 1] = sw ? ia : ib;
     }
   }
-  int mykey = KMIN, myid = 0, key0 = 0;
+  int mykey = KMIN, key0 = KMIN;
   for (int r = 0; r < k; ++r) {
     const int M = dpp_wave_reduce(key[0], KMIN, [](int a, int b) { return max(a, b); });
     const uint64_t hit = __ballot(key[0] == M);
     const int wl = __ffsll((unsigned long long)hit) - 1;        // lowest lane holding M
-    const int wid = __builtin_amdgcn_readlane(id[0], wl);
-    if (lane == r) { mykey = M; myid = wid; }
-    if (r == 0) key0 = M;
-    if (lane == wl) {                                            // pop the head
+    const bool pop = lane == wl;
+    scr[pop ? 64 + r : lane] = id[0];
+    mykey = lane == r ? M : mykey;
+    key0 = r == 0 ? M : key0;
+    ivec ks, is;
 #pragma unroll
-      for (int i = 0; i + 1 < PER; ++i) { key[i] = key[i + 1]; id[i] = id[i + 1]; }
-      key[PER - 1] = KMIN;
+    for (int i = 0; i + 1 < PER; ++i) {
+      ks[i] = key[i + 1];
+      is[i] = id[i + 1];
     }
+    ks[PER - 1] = KMIN;
+    is[PER - 1] = id[PER - 1];
+    key = pop ? ks : key;
+    id = pop ? is : id;
   }
   const float z = lane < k ? __expf(order_key_float(mykey) - order_key_float(key0)) : 0.0f;
   const float sum = dpp_wave_sum(z);
-  *out_id = myid;
+  *out_id = scr[64 + (lane < k ? lane : 0)];
   *out_w = z / sum;
 }
 
@@ -274,14 +295,14 @@ __device__ __forceinline__ void router_row_block(const uint16_t* __restrict__ x,
   }
 }
 
-// Runtime dispatch on E (E <= 1024).
+// Runtime dispatch on E (E <= 1024).  scr: 64 + k ints of LDS for this wave.
 __device__ __forceinline__ void topk_wave_any(const float* __restrict__ lrow, int E, int k, int lane,
-                                              int* out_id, float* out_w) {
-  if (E <= 64) topk_wave<1>(lrow, E, k, lane, out_id, out_w);
-  else if (E <= 128) topk_wave<2>(lrow, E, k, lane, out_id, out_w);
-  else if (E <= 256) topk_wave<4>(lrow, E, k, lane, out_id, out_w);
-  else if (E <= 512) topk_wave<8>(lrow, E, k, lane, out_id, out_w);
-  else topk_wave<16>(lrow, E, k, lane, out_id, out_w);
+                                              int* scr, int* out_id, float* out_w) {
+  if (E <= 64) topk_wave<1>(lrow, E, k, lane, scr, out_id, out_w);
+  else if (E <= 128) topk_wave<2>(lrow, E, k, lane, scr, out_id, out_w);
+  else if (E <= 256) topk_wave<4>(lrow, E, k, lane, scr, out_id, out_w);
+  else if (E <= 512) topk_wave<8>(lrow, E, k, lane, scr, out_id, out_w);
+  else topk_wave<16>(lrow, E, k, lane, scr, out_id, out_w);
 }
 
 // NVFP4 of one bf16 row by a whole block (one tensor scale for the row): each

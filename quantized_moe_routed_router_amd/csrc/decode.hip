@@ -19,18 +19,21 @@
 //   gate/up   block = (pair p, 64-lane tile j, K-split s); each lane owns one
 //             gate or up weight row, the activation is an LDS broadcast, so no
 //             cross-lane reduction; waves split the block's K range and are
-//             summed through LDS in a fixed order.  Writes raw partial dot
-//             sums per K-split (no scales).  In the fused layer it first ranks
-//             the router logits itself (every block the same, deterministic).
+//             summed through LDS in a fixed order.  Writes partial dot sums
+//             per K-split with the tensor scales applied.  In the fused layer
+//             it first ranks the router logits itself (every block the same,
+//             deterministic).
+//   h^        block = one pair: sums the K-splits, SiLU-gates, and quantizes
+//             h to NVFP4 (bit-exact quantizer) once, for every down block.
 //   down      block = 16 output columns of every pair (few pairs) or one
-//             (pair, 64-row tile) (many pairs).  Issues its weight loads, then
-//             finishes h from the gate/up partials (sum over splits, scales,
-//             SiLU), quantizes it to NVFP4 (bit-exact quantizer) into LDS and
-//             runs the down GEMV.  In the fused layer the column-slice kernel
-//             also does the weighted combine of its columns; with many pairs
-//             a separate combine kernel follows.
+//             (pair, 64-row tile) (many pairs).  Issues its weight loads,
+//             stages h^ into LDS as f16 and runs the down GEMV.  In the fused
+//             layer the column-slice kernel also does the weighted combine of
+//             its columns; with many pairs a separate combine kernel follows.
 // The block of the first pair routed to an expert serves every pair routed
-// to it, so each distinct expert's weights are read once per call.
+// to it, so each distinct expert's weights are read once per call (the
+// column-slice down kernel reads an expert once per pair; duplicates only
+// occur with several tokens and hit in cache).
 #include "../../include/moe.h"
 #include "common.hpp"
 #include "launch.hpp"
@@ -58,6 +61,49 @@ __device__ __forceinline__ void stage_act_f16(const uint8_t* __restrict__ codes,
     d[0] = *reinterpret_cast<u32x4*>(&v[0]);
     d[1] = *reinterpret_cast<u32x4*>(&v[4]);
   }
+}
+
+// The first XREG blocks per thread of a run of `total` 16-element activation
+// blocks (rows contiguous), loaded into registers before the weight loads
+// (straight-line: slots past the end re-read the last block) and written to
+// LDS as f16 A*s after them, so the staging does not wait for the weights.
+constexpr int XREG = 2;
+struct ActRegs {
+  u32x2 c[XREG];
+  uint32_t s[XREG];
+};
+__device__ __forceinline__ void act_load(ActRegs& r, const uint8_t* __restrict__ codes,
+                                         const uint8_t* __restrict__ scales, int total, int tid,
+                                         int nthreads) {
+#pragma unroll
+  for (int i = 0; i < XREG; ++i) {
+    const int b = min(tid + i * nthreads, total - 1);
+    r.c[i] = *reinterpret_cast<const u32x2*>(codes + (size_t)b * 8);
+    r.s[i] = scales[b];
+  }
+}
+__device__ __forceinline__ void act_store(const ActRegs& r, const uint8_t* __restrict__ codes,
+                                          const uint8_t* __restrict__ scales, int total,
+                                          half2_t* dst, int tid, int nthreads) {
+#pragma unroll
+  for (int i = 0; i < XREG; ++i) {
+    const int b = tid + i * nthreads;
+    if (b < total) {
+      const _Float16 s = (_Float16)e4m3_to_f32(r.s[i]);
+      const half2_t s2 = {s, s};
+      half2_t v[8];
+      v[0] = fp4x2_to_f16x2<0>(r.c[i].x) * s2; v[1] = fp4x2_to_f16x2<1>(r.c[i].x) * s2;
+      v[2] = fp4x2_to_f16x2<2>(r.c[i].x) * s2; v[3] = fp4x2_to_f16x2<3>(r.c[i].x) * s2;
+      v[4] = fp4x2_to_f16x2<0>(r.c[i].y) * s2; v[5] = fp4x2_to_f16x2<1>(r.c[i].y) * s2;
+      v[6] = fp4x2_to_f16x2<2>(r.c[i].y) * s2; v[7] = fp4x2_to_f16x2<3>(r.c[i].y) * s2;
+      u32x4* d = reinterpret_cast<u32x4*>(dst + (size_t)b * 8);
+      d[0] = *reinterpret_cast<u32x4*>(&v[0]);
+      d[1] = *reinterpret_cast<u32x4*>(&v[4]);
+    }
+  }
+  // blocks beyond the register slots: the plain loop
+  if (total > XREG * nthreads)
+    stage_act_f16(codes, scales, total * 16, dst, tid + XREG * nthreads, nthreads);
 }
 
 // 16 weight codes (one u32x2 half of a lane's chunk) -> 8 f16x2
@@ -88,16 +134,19 @@ __device__ __forceinline__ float chunk_dot(const half2_t (&w0)[8], const half2_t
   return fmaf(s1, b1, acc);
 }
 
+// The CPW chunks c0 .. c0+nc-1 of a lane's row.  Straight-line: slots past
+// nc re-read a chunk of the same tile (a cache hit, never used), so the
+// compiler can count these loads exactly and later waits on earlier loads
+// do not also wait for them.
 template <int CPW>
 __device__ __forceinline__ void load_chunks(const uint8_t* __restrict__ tile, int K, int c0, int nc,
                                             int lane, u32x4 (&cw)[CPW], uint32_t (&sw)[CPW]) {
+  const int clast = K / 32 - 1;
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
-    if (i < nc) {
-      const int c = c0 + i;
-      cw[i] = *reinterpret_cast<const u32x4*>(tile + (size_t)c * 1024 + lane * 16);
-      sw[i] = *reinterpret_cast<const uint16_t*>(tile + tile_scale_offset(K) + (size_t)(c >> 2) * 512 + lane * 8 + (c & 3) * 2);
-    }
+    const int c = min(i < nc ? c0 + i : c0, clast);
+    cw[i] = *reinterpret_cast<const u32x4*>(tile + (size_t)c * 1024 + lane * 16);
+    sw[i] = *reinterpret_cast<const uint16_t*>(tile + tile_scale_offset(K) + (size_t)(c >> 2) * 512 + lane * 8 + (c & 3) * 2);
   }
 }
 
@@ -132,9 +181,10 @@ struct PairIds {
 __device__ __forceinline__ PairIds load_pair_ids(const int32_t* ids, int npairs, int lane) {
   PairIds p;
 #pragma unroll
-  for (int i = 0; i < PID_CH; ++i) {
+  for (int i = 0; i < PID_CH; ++i) {             // every load issued before the first use
     const int q = lane + 64 * i;
-    p.v[i] = q < npairs ? ids[q] : 0;
+    const int v = ids[q < npairs ? q : npairs - 1];
+    p.v[i] = q < npairs ? v : 0;
   }
   return p;
 }
@@ -201,7 +251,10 @@ __host__ __device__ inline int dec_waves(int nchunk_block) {
 }
 
 struct DecodeWs {
-  float* gu;          // [KS][T*k][2][I] raw gate/up partial dot sums
+  float* gu;          // [KS][T*k][2][I] gate/up partial dot sums, tensor scales applied
+  uint8_t* hc;        // [T*k][I/2]  h^ codes
+  uint8_t* hsc;       // [T*k][I/16] h^ block scales (E4M3)
+  float* hts;         // [T*k]       h^ tensor scales
 };
 
 // ---------------------------------------------------------------- gate/up
@@ -217,6 +270,7 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
   float* red = reinterpret_cast<float*>(smem + (size_t)MAXP * a.H * 2);   // [nw][MAXP][64]
   __shared__ int list[MAXP];
   __shared__ int sids[MOE_DECODE_MAX_T * MOE_MAX_K];
+  __shared__ int tscr[TOPK ? DEC_MAX_WAVES : 1][64 + MOE_MAX_K];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int npairs = a.T * a.k, p = blockIdx.x, j = blockIdx.y, split = blockIdx.z;
   const int KS = gridDim.z;
@@ -230,7 +284,7 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
     for (int t = wv; t < a.T; t += nw) {
       int id;
       float wt;
-      topk_wave_any(logits + (size_t)t * a.E, a.E, a.k, lane, &id, &wt);
+      topk_wave_any(logits + (size_t)t * a.E, a.E, a.k, lane, tscr[wv], &id, &wt);
       if (lane < a.k) {
         sids[t * a.k + lane] = id;
         if (p == 0 && j == 0 && split == 0) {
@@ -250,6 +304,9 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
     ids = a.ids;
   }
   const PairIds P = load_pair_ids(ids, npairs, lane);
+  const int xtot = a.T * (a.H / 16);
+  ActRegs xr;
+  if (!TOPK) act_load(xr, a.x_codes, a.x_scales, xtot, tid, blockDim.x);
   const int e = pair_expert(P, p);
   uint64_t pm[PID_CH];
   pair_masks(P, npairs, e, lane, pm);
@@ -269,10 +326,14 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
   u32x4 cw[CPW];
   uint32_t sw[CPW];
   load_chunks<CPW>(tile, a.H, c0, nc, lane, cw, sw);          // all weight loads in flight
-  if (by_token && !(TOPK && min(a.T, nw) < nw)) {
-    for (int t = 0; t < a.T; ++t)
-      stage_act_f16(a.x_codes + (size_t)t * (a.H / 2), a.x_scales + (size_t)t * (a.H / 16), a.H,
-                    xs + (size_t)t * (a.H / 2), tid, blockDim.x);
+  if (by_token) {
+    if (!TOPK) {
+      act_store(xr, a.x_codes, a.x_scales, xtot, xs, tid, blockDim.x);
+    } else if (min(a.T, nw) >= nw) {                            // every wave ranked: stage now
+      for (int t = 0; t < a.T; ++t)
+        stage_act_f16(a.x_codes + (size_t)t * (a.H / 2), a.x_scales + (size_t)t * (a.H / 16), a.H,
+                      xs + (size_t)t * (a.H / 2), tid, blockDim.x);
+    }
   }
   int qstart = p;
   while (true) {
@@ -314,19 +375,88 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
   }
 }
 
+// ---------------------------------------------------------------- h^
+// h = SiLU(g) * u of every pair from the gate/up partials (summed over the
+// K-splits in split order), then NVFP4 with the row's own tensor scale.
+// Block = one pair, thread = one 16-element block of its row.  h^ is written
+// once here and read by every down block, so the down step does no
+// quantization arithmetic of its own.
+__global__ __launch_bounds__(256) void h_quant_decode_kernel(FfnArgs a, DecodeWs ws) {
+  __shared__ float wmax[4];
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  const int nblk = a.I / 16;
+  const int KS = dec_ksplit(a.H);
+  const size_t part_stride = (size_t)a.T * a.k * 2 * a.I;
+  const int b = tid < nblk ? tid : nblk - 1;               // extra threads redo the last block
+  float g[16], u[16];
+  for (int sp0 = 0; sp0 < KS; sp0 += 2) {                  // two splits' loads in flight at once
+    float4_t g4[2][4], u4[2][4];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int spc = min(sp0 + s2, KS - 1);
+      const float4_t* gp = reinterpret_cast<const float4_t*>(ws.gu + (size_t)spc * part_stride + (size_t)q * 2 * a.I + b * 16);
+      const float4_t* upp = gp + a.I / 4;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) { g4[s2][r4] = gp[r4]; u4[s2][r4] = upp[r4]; }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      if (sp0 + s2 < KS) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int i = 4 * r4 + c;
+            g[i] = (sp0 + s2 == 0) ? g4[s2][r4][c] : g[i] + g4[s2][r4][c];
+            u[i] = (sp0 + s2 == 0) ? u4[s2][r4][c] : u[i] + u4[s2][r4][c];
+          }
+        }
+      }
+    }
+  }
+  float hv[16];
+  float bmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    hv[i] = silu_mul(g[i], u[i]);
+    bmax = fmaxf(bmax, fabsf(hv[i]));
+  }
+  const float m = dpp_wave_max(tid < nblk ? bmax : 0.0f);
+  if (lane == 0) wmax[wv] = m;
+  __syncthreads();
+  float amax = wmax[0];
+  for (int w = 1; w < nw; ++w) amax = fmaxf(amax, wmax[w]);
+  const float ts = tensor_scale_from_amax(amax);
+  if (tid < nblk) {
+    uint32_t pk[2];
+    const uint32_t sb = quantize_block16(hv, ts, pk);
+    *reinterpret_cast<u32x2*>(ws.hc + (size_t)q * (a.I / 2) + b * 8) = u32x2{pk[0], pk[1]};
+    ws.hsc[(size_t)q * nblk + b] = (uint8_t)sb;
+    if (a.dbg_h) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) a.dbg_h[(size_t)q * a.I + b * 16 + c] = hv[c];
+    }
+    if (a.dbg_h_codes) *reinterpret_cast<u32x2*>(a.dbg_h_codes + (size_t)q * (a.I / 2) + b * 8) = u32x2{pk[0], pk[1]};
+    if (a.dbg_h_scales) a.dbg_h_scales[(size_t)q * nblk + b] = (uint8_t)sb;
+  }
+  if (tid == 0) {
+    ws.hts[q] = ts;
+    if (a.dbg_h_ts) a.dbg_h_ts[q] = ts;
+  }
+}
+
 // ---------------------------------------------------------------- down
 template <int MAXP, int CPW>
 __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(FfnArgs a, DecodeWs ws) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int nw = blockDim.x >> 6;
   half2_t* hs = reinterpret_cast<half2_t*>(smem);                          // [MAXP][I/2]
-  float* hrow = reinterpret_cast<float*>(smem + (size_t)MAXP * a.I * 2);   // [nw][I]
-  float* red = hrow + (size_t)nw * a.I;                                    // [nw][MAXP][64]
+  float* red = reinterpret_cast<float*>(smem + (size_t)MAXP * a.I * 2);    // [nw][MAXP][64]
   __shared__ int list[MAXP];
   __shared__ float hts[MAXP];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int npairs = a.T * a.k, p = blockIdx.x, j = blockIdx.y;
-  const int KS = dec_ksplit(a.H);
   const PairIds P = load_pair_ids(a.ids, npairs, lane);
   const int e = pair_expert(P, p);
   uint64_t pm[PID_CH];
@@ -345,74 +475,17 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(FfnArgs
     uint32_t sw[CPW];
     load_chunks<CPW>(tile, a.I, c0, nc, lane, cw, sw);
     const int nblk = a.I / 16;
-    const size_t part_stride = (size_t)npairs * 2 * a.I;
     int qstart = p;
     while (true) {
       int qnext;
       const int n = masked_pairs<MAXP>(pm, npairs, qstart, list, &qnext, tid);
       __syncthreads();
-      // h of pair i (wave i % nw): finish the dot products, SiLU-gate, then
-      // NVFP4 with the row's own tensor scale
-      for (int i = wv; i < n; i += nw) {
+      // h^ of the batch's pairs (quantized once by the h^ kernel) as f16 A*s
+      for (int i = 0; i < n; ++i) {
         const int q = list[i];
-        float* hr = hrow + (size_t)wv * a.I;
-        float amax = 0.0f;
-        // all partial loads of a 640-column batch first, then the arithmetic
-        constexpr int HB = 10;                                // columns per lane per batch
-        for (int c0 = 0; c0 < a.I; c0 += 64 * HB) {
-          float gp[HB][4], up[HB][4];
-#pragma unroll
-          for (int r = 0; r < HB; ++r) {
-            const int c = c0 + lane + 64 * r;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              if (s < KS && c < a.I) {
-                const float* part = ws.gu + (size_t)s * part_stride + (size_t)q * 2 * a.I;
-                gp[r][s] = part[c];
-                up[r][s] = part[a.I + c];
-              }
-            }
-          }
-#pragma unroll
-          for (int r = 0; r < HB; ++r) {
-            const int c = c0 + lane + 64 * r;
-            if (c < a.I) {
-              float g = gp[r][0], u = up[r][0];
-#pragma unroll
-              for (int s = 1; s < 4; ++s)
-                if (s < KS) { g += gp[r][s]; u += up[r][s]; }
-              const float h = silu_mul(g, u);
-              hr[c] = h;
-              amax = fmaxf(amax, fabsf(h));
-              if (j == 0 && a.dbg_h) a.dbg_h[(size_t)q * a.I + c] = h;
-            }
-          }
-        }
-        amax = dpp_wave_max(amax);
-        const float ts = tensor_scale_from_amax(amax);
-        wave_lds_sync();                                      // hr written by other lanes
-        for (int b = lane; b < nblk; b += 64) {
-          float v[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) v[r] = hr[b * 16 + r];
-          uint32_t pk[2];
-          const uint32_t sb = quantize_block16(v, ts, pk);
-          if (j == 0) {
-            if (a.dbg_h_codes) *reinterpret_cast<u32x2*>(a.dbg_h_codes + (size_t)q * (a.I / 2) + b * 8) = u32x2{pk[0], pk[1]};
-            if (a.dbg_h_scales) a.dbg_h_scales[(size_t)q * nblk + b] = (uint8_t)sb;
-          }
-          _Float16 s = (_Float16)e4m3_to_f32(sb);
-          half2_t s2 = {s, s};
-          half2_t w[8];
-          cvt16(pk[0], pk[1], w);
-          half2_t* d = hs + (size_t)i * (a.I / 2) + b * 8;
-#pragma unroll
-          for (int r = 0; r < 8; ++r) d[r] = w[r] * s2;
-        }
-        if (lane == 0) {
-          hts[i] = ts;
-          if (j == 0 && a.dbg_h_ts) a.dbg_h_ts[q] = ts;
-        }
+        stage_act_f16(ws.hc + (size_t)q * (a.I / 2), ws.hsc + (size_t)q * nblk, a.I,
+                      hs + (size_t)i * (a.I / 2), tid, blockDim.x);
+        if (tid == 0) hts[i] = ws.hts[q];
       }
       __syncthreads();
       int slot[MAXP];
@@ -440,200 +513,115 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(FfnArgs
 }
 
 // ---------------------------------------------------------------- down + combine
-// Fused layer, kernel 3, for small pair counts: a block owns 16 output
-// columns n0..n0+15 of every pair and does the weighted combine of them
-// itself, so no cross-block step is needed.  Lane (r = lane & 15, quarter
-// qt = lane >> 4) reads row n0 + r of a 64-row down tile at chunks
-// qt, qt+4, ...; the four quarters are summed with lane shuffles.  Each wave
-// owns the experts first seen at its pairs (q = wave, wave + nw, ...), issues
-// their weight loads, then rebuilds h^ of its pairs into LDS (bit-exact
-// quantizer) while the loads are in flight.
-constexpr int SL_OWN_MAX = 4;            // experts a wave can own (npairs <= SL_OWN * waves)
+// Down step for few pairs (T*k <= SL_MAXP): a block owns 16 output columns
+// n0..n0+15 of every pair and wave q serves pair q.  Lane (r = lane & 15,
+// quarter qt = lane >> 4) reads row n0 + r of the pair's 64-row down tile at
+// chunks qt, qt+4, ...; the quarters are summed with lane shuffles.
+// Order of work: the pair ids, the combine inputs and this thread's block of
+// h^ are loaded first; the weight loads follow as soon as the ids are in;
+// h^ goes to LDS as f16 A*s while the weights are in flight.  All loads are
+// straight-line (clamped indices instead of branches), so each wait covers
+// exactly the loads it needs.  With COMBINE the block also does the weighted
+// combine of its 16 columns, so no cross-block step is needed.  A pair whose
+// id is outside [0, E) gets o = 0.
+constexpr int SL_MAXP = 16;              // pairs (= waves) per block
 constexpr int SL_CPQ = 5;                // chunks per quarter held in registers (I <= 640)
-constexpr int SL_KSMAX = 2;              // gate/up K-splits the slice kernel sums
 
-template <bool COMBINE, int SL_OWN, int JOBS>
-__global__ __launch_bounds__(512) void down_slice_kernel(FfnArgs a, DecodeWs ws,
-                                                         const float* __restrict__ w_comb,
-                                                         const uint16_t* __restrict__ residual,
-                                                         uint16_t* __restrict__ y) {
+template <bool COMBINE>
+__global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, DecodeWs ws,
+                                                                  const float* __restrict__ w_comb,
+                                                                  const uint16_t* __restrict__ residual,
+                                                                  uint16_t* __restrict__ y) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int nw = blockDim.x >> 6;
   const int npairs = a.T * a.k;
   half2_t* hs = reinterpret_cast<half2_t*>(smem);                              // [npairs][I/2]
   float* obuf = reinterpret_cast<float*>(smem + (size_t)npairs * a.I * 2);     // [npairs][16]
-  float* bmaxs = obuf + (size_t)npairs * 16;                                   // [npairs][I/16]
-  __shared__ float hts[MOE_DECODE_MAX_T * MOE_MAX_K];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ float hts[SL_MAXP];
+  __shared__ float wcs[SL_MAXP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int q = __builtin_amdgcn_readfirstlane(tid >> 6);    // this wave's pair
   const int n0 = blockIdx.x * 16;
   const int r = lane & 15, qt = lane >> 4;
   const int jt = n0 >> 6, lit = (n0 & 63) + r;               // down tile, lane within it
-  const int KS = dec_ksplit(a.H);
-  const int nchunk = a.I / 32;
-  // ---- the scaled gate/up partials of this thread's h jobs: loads first,
-  // they do not depend on the routing
-  const size_t part_stride = (size_t)npairs * 2 * a.I;
-  const int nblk = a.I / 16;
-  const int njobs = npairs * nblk;
-  float4_t g4[JOBS][SL_KSMAX][4], u4[JOBS][SL_KSMAX][4];
-#pragma unroll
-  for (int jj = 0; jj < JOBS; ++jj) {
-    const int job = tid + jj * blockDim.x;
-    if (job < njobs) {
-      const int q = job / nblk, b = job % nblk;
-#pragma unroll
-      for (int sp = 0; sp < SL_KSMAX; ++sp) {
-        if (sp < KS) {
-          const float4_t* gp = reinterpret_cast<const float4_t*>(ws.gu + (size_t)sp * part_stride + (size_t)q * 2 * a.I + b * 16);
-          const float4_t* upp = gp + a.I / 4;
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) { g4[jj][sp][r4] = gp[r4]; u4[jj][sp][r4] = upp[r4]; }
-        }
-      }
-    }
+  const int nchunk = a.I / 32, nblk = a.I / 16;
+  const int nitems = npairs * nblk;
+  // ---- loads that do not depend on the routing, ids first
+  const int qid = a.ids[lane < npairs ? lane : npairs - 1];
+  const float htl = ws.hts[lane < npairs ? lane : npairs - 1];
+  float wc = 0.0f;
+  uint16_t res = 0;
+  if (COMBINE) {
+    wc = w_comb[tid < npairs ? tid : npairs - 1];
+    const int cidx = tid < a.T * 16 ? tid : a.T * 16 - 1;
+    // no residual: read y's own column instead (unused), keeping the load unconditional
+    const uint16_t* rp = residual ? residual : y;
+    res = rp[(size_t)(cidx >> 4) * a.H + n0 + (cidx & 15)];
   }
-  const PairIds P = load_pair_ids(a.ids, npairs, lane);
+  const int item = tid < nitems ? tid : nitems - 1;
+  const int jq = item / nblk, jb = item % nblk;
+  const u32x2 hcw = *reinterpret_cast<const u32x2*>(ws.hc + (size_t)jq * (a.I / 2) + jb * 8);
+  const uint32_t hsw = ws.hsc[(size_t)jq * nblk + jb];
+  // ---- this pair's expert and its weight loads
+  const int e = __builtin_amdgcn_readlane(qid, q);
+  const bool valid = (unsigned)e < (unsigned)a.E;
+  const uint8_t* tile = a.down + (size_t)(valid ? e : 0) * down_expert_bytes(a.H, a.I) + (size_t)jt * tile_bytes(a.I);
+  u32x4 cw[SL_CPQ];
+  uint32_t sw[SL_CPQ];
+#pragma unroll
+  for (int m = 0; m < SL_CPQ; ++m) {
+    const int c = min(qt + 4 * m, nchunk - 1);
+    cw[m] = *reinterpret_cast<const u32x4*>(tile + (size_t)c * 1024 + lit * 16);
+    sw[m] = *reinterpret_cast<const uint16_t*>(tile + tile_scale_offset(a.I) + (size_t)(c >> 2) * 512 + lit * 8 + (c & 3) * 2);
+  }
+  const float tsd = a.ts_down[valid ? e : 0];
+  __builtin_amdgcn_sched_barrier(0);        // keep the weight loads ahead of the staging
 
-  // ---- experts owned by this wave, and their weight loads
-  int own_e[SL_OWN];
-  u32x4 cw[SL_OWN][SL_CPQ];
-  uint32_t sw[SL_OWN][SL_CPQ];
-#pragma unroll
-  for (int o = 0; o < SL_OWN; ++o) {
-    own_e[o] = -1;
-    const int q = wv + nw * o;
-    if (q < npairs) {
-      const int e = pair_expert(P, q);
-      uint64_t pm[PID_CH];
-      pair_masks(P, npairs, e, lane, pm);
-      if (first_pair(pm) == q && (unsigned)e < (unsigned)a.E) {
-        own_e[o] = e;
-        const uint8_t* tile = a.down + (size_t)e * down_expert_bytes(a.H, a.I) + (size_t)jt * tile_bytes(a.I);
-#pragma unroll
-        for (int m = 0; m < SL_CPQ; ++m) {
-          const int c = qt + 4 * m;
-          if (c < nchunk) {
-            cw[o][m] = *reinterpret_cast<const u32x4*>(tile + (size_t)c * 1024 + lit * 16);
-            sw[o][m] = *reinterpret_cast<const uint16_t*>(tile + tile_scale_offset(a.I) + (size_t)(c >> 2) * 512 + lit * 8 + (c & 3) * 2);
-          }
-        }
-      }
-    }
-  }
-
-  // ---- h^ of every pair, element-parallel: job (pair q, 16-element block b)
-  // per thread (at most two): scaled partial sums -> h (SiLU-gated) -> block
-  // max; the row amax comes from the jobs' block maxima in LDS; then the
-  // bit-exact quantizer writes f16 A*s into LDS.  (Pairs with an id outside
-  // [0, E) have zero partials, so h = 0.)
-  float hv[JOBS][16];
-  int jq[JOBS], jb[JOBS];
-#pragma unroll
-  for (int jj = 0; jj < JOBS; ++jj) {
-    const int job = tid + jj * blockDim.x;
-    jq[jj] = -1;
-    if (job < njobs) {
-      const int q = job / nblk, b = job % nblk;
-      jq[jj] = q;
-      jb[jj] = b;
-      float bmax = 0.0f;
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float g = g4[jj][0][r4][c], u = u4[jj][0][r4][c];
-#pragma unroll
-          for (int sp = 1; sp < SL_KSMAX; ++sp)
-            if (sp < KS) { g += g4[jj][sp][r4][c]; u += u4[jj][sp][r4][c]; }
-          const float h = silu_mul(g, u);
-          hv[jj][4 * r4 + c] = h;
-          bmax = fmaxf(bmax, fabsf(h));
-        }
-      }
-      bmaxs[job] = bmax;
-      if (blockIdx.x == 0 && a.dbg_h) {
-#pragma unroll
-        for (int c = 0; c < 16; ++c) a.dbg_h[(size_t)q * a.I + b * 16 + c] = hv[jj][c];
-      }
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int jj = 0; jj < JOBS; ++jj) {
-    if (jq[jj] < 0) continue;
-    const int q = jq[jj], b = jb[jj];
-    float amax = 0.0f;
-    for (int bb = 0; bb < nblk; ++bb) amax = fmaxf(amax, bmaxs[q * nblk + bb]);
-    const float ts = tensor_scale_from_amax(amax);
-    uint32_t pk[2];
-    const uint32_t sb = quantize_block16(hv[jj], ts, pk);
-    if (blockIdx.x == 0) {
-      if (a.dbg_h_codes) *reinterpret_cast<u32x2*>(a.dbg_h_codes + (size_t)q * (a.I / 2) + b * 8) = u32x2{pk[0], pk[1]};
-      if (a.dbg_h_scales) a.dbg_h_scales[(size_t)q * nblk + b] = (uint8_t)sb;
-      if (b == 0 && a.dbg_h_ts) a.dbg_h_ts[q] = ts;
-    }
-    if (b == 0) hts[q] = ts;
-    _Float16 sc = (_Float16)e4m3_to_f32(sb);
-    half2_t s2 = {sc, sc};
+  // ---- h^ into LDS as f16 A*s
+  if (tid < nitems) {
+    const _Float16 sc = (_Float16)e4m3_to_f32(hsw);
+    const half2_t s2 = {sc, sc};
     half2_t wq[8];
-    cvt16(pk[0], pk[1], wq);
-    half2_t* d = hs + (size_t)q * (a.I / 2) + b * 8;
+    cvt16(hcw.x, hcw.y, wq);
+    half2_t* d = hs + (size_t)jq * (a.I / 2) + jb * 8;
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) d[rr] = wq[rr] * s2;
   }
+  if (tid < npairs) {
+    hts[tid] = htl;
+    if (COMBINE) wcs[tid] = wc;
+  }
   __syncthreads();
 
-  // ---- down dots of the owned experts for all their pairs
+  // ---- down dot of pair q over this block's 16 rows
+  float acc = 0.0f;
 #pragma unroll
-  for (int o = 0; o < SL_OWN; ++o) {
-    if (own_e[o] < 0) continue;
-    const int e = own_e[o];
-    uint64_t pm[PID_CH];
-    pair_masks(P, npairs, e, lane, pm);
-    for (int i = 0; i < PID_CH; ++i) {
-      uint64_t mm = pm[i];
-      while (mm) {
-        const int q = 64 * i + __ffsll((unsigned long long)mm) - 1;
-        mm &= mm - 1;
-        float acc = 0.0f;
-#pragma unroll
-        for (int m = 0; m < SL_CPQ; ++m) {
-          const int c = qt + 4 * m;
-          if (c < nchunk) {
-            half2_t w0[8], w1[8];
-            cvt16(cw[o][m].x, cw[o][m].y, w0);
-            cvt16(cw[o][m].z, cw[o][m].w, w1);
-            acc = chunk_dot(w0, w1, e4m3_to_f32(sw[o][m] & 0xFF), e4m3_to_f32(sw[o][m] >> 8),
-                            hs + (size_t)q * (a.I / 2) + c * 16, acc);
-          }
-        }
-        acc += __shfl_xor(acc, 16, 64);
-        acc += __shfl_xor(acc, 32, 64);
-        if (lane < 16) {
-          const float ov = acc * (hts[q] * a.ts_down[e]);
-          obuf[q * 16 + r] = ov;
-          a.out[(size_t)q * a.H + n0 + r] = ov;
-        }
-      }
+  for (int m = 0; m < SL_CPQ; ++m) {
+    const int c = qt + 4 * m;
+    if (c < nchunk) {
+      half2_t w0[8], w1[8];
+      cvt16(cw[m].x, cw[m].y, w0);
+      cvt16(cw[m].z, cw[m].w, w1);
+      acc = chunk_dot(w0, w1, e4m3_to_f32(sw[m] & 0xFF), e4m3_to_f32(sw[m] >> 8),
+                      hs + (size_t)q * (a.I / 2) + c * 16, acc);
     }
   }
-  // pairs with an id outside [0, E): o = 0
-  for (int q = tid; q < npairs; q += blockDim.x) {
-    const int e = a.ids[q];
-    if ((unsigned)e >= (unsigned)a.E) {
-      for (int rr = 0; rr < 16; ++rr) { obuf[q * 16 + rr] = 0.0f; a.out[(size_t)q * a.H + n0 + rr] = 0.0f; }
-    }
+  acc += __shfl_xor(acc, 16, 64);
+  acc += __shfl_xor(acc, 32, 64);
+  if (lane < 16) {
+    const float ov = valid ? acc * (hts[q] * tsd) : 0.0f;
+    obuf[q * 16 + r] = ov;
+    a.out[(size_t)q * a.H + n0 + r] = ov;
   }
+  if (!COMBINE) return;
   __syncthreads();
 
   // ---- combine these 16 columns: fp32 in slot order, one bf16 rounding
-  if (!COMBINE) return;
-  for (int idx = tid; idx < a.T * 16; idx += blockDim.x) {
-    const int t = idx >> 4, c = idx & 15;
-    float acc = 0.0f;
-    for (int i = 0; i < a.k; ++i) acc = fmaf(w_comb[t * a.k + i], obuf[(t * a.k + i) * 16 + c], acc);
-    if (residual) acc += bf16_to_f32(residual[(size_t)t * a.H + n0 + c]);
-    y[(size_t)t * a.H + n0 + c] = (uint16_t)f32_to_bf16_rne(acc);
+  if (tid < a.T * 16) {
+    const int t = tid >> 4, c = tid & 15;
+    float accy = 0.0f;
+    for (int i = 0; i < a.k; ++i) accy = fmaf(wcs[t * a.k + i], obuf[(t * a.k + i) * 16 + c], accy);
+    if (residual) accy += bf16_to_f32(res);
+    y[(size_t)t * a.H + n0 + c] = (uint16_t)f32_to_bf16_rne(accy);
   }
 }
 
@@ -663,23 +651,36 @@ __global__ __launch_bounds__(256) void router_quant_kernel(const uint16_t* __res
 // ---------------------------------------------------------------- launchers
 static size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-size_t decode_workspace_bytes(int E, int H, int I, int k, int T) {
-  (void)E;
-  return al256((size_t)dec_ksplit(H) * T * k * 2 * I * sizeof(float));
+// Decode workspace: gate/up partials, then h^ (codes, block scales, tensor scales).
+static DecodeWs carve_decode(void* ws, int H, int I, int npairs, size_t* total) {
+  uint8_t* p = reinterpret_cast<uint8_t*>(ws);
+  size_t off = 0;
+  auto take = [&](size_t b) { uint8_t* q = p ? p + off : nullptr; off += al256(b); return q; };
+  DecodeWs w;
+  w.gu = (float*)take((size_t)dec_ksplit(H) * npairs * 2 * I * sizeof(float));
+  w.hc = take((size_t)npairs * I / 2);
+  w.hsc = take((size_t)npairs * I / 16);
+  w.hts = (float*)take((size_t)npairs * sizeof(float));
+  if (total) *total = off;
+  return w;
 }
 
-// The down step: the 16-column slice kernel when its LDS and register
-// budget fits (then the combine can run inside it), else one block per
-// (pair, 64-row tile) followed by the combine kernel when a combine is asked for.
-static size_t slice_lds_bytes(int npairs, int I, int nw) {
-  (void)nw;
-  return (size_t)npairs * I * 2 + (size_t)npairs * 16 * 4 + (size_t)npairs * (I / 16) * 4;
+size_t decode_workspace_bytes(int E, int H, int I, int k, int T) {
+  (void)E;
+  size_t total = 0;
+  carve_decode(nullptr, H, I, T * k, &total);
+  return total;
 }
-static int slice_waves(int npairs) { return npairs < 8 ? npairs : 8; }
+
+// The down step: the 16-column slice kernel when the pairs fit one block
+// (then the combine runs inside it), else one block per (pair, 64-row tile)
+// followed by the combine kernel when a combine is asked for.
+static size_t slice_lds_bytes(int npairs, int I) {
+  return (size_t)npairs * I * 2 + (size_t)npairs * 16 * 4;
+}
 static bool slice_fits(int npairs, int H, int I) {
-  const int nw = slice_waves(npairs);
-  return I <= 32 * 4 * SL_CPQ && H % 16 == 0 && dec_ksplit(H) <= SL_KSMAX && npairs <= SL_OWN_MAX * nw &&
-         npairs * (I / 16) <= 2 * 64 * nw && slice_lds_bytes(npairs, I, nw) <= 56 * 1024;
+  return npairs <= SL_MAXP && I <= 32 * 4 * SL_CPQ && I / 16 <= 64 && H % 16 == 0 &&
+         slice_lds_bytes(npairs, I) <= 56 * 1024;
 }
 
 template <int MAXP, bool FUSED>
@@ -690,35 +691,28 @@ static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logit
   const int nw1 = dec_waves(a.H / 32 / KS);
   const size_t lds1 = (size_t)MAXP * a.H * 2 + (size_t)nw1 * MAXP * 64 * 4;
   gate_up_decode_kernel<MAXP, DEC_CPW, FUSED><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out);
+  h_quant_decode_kernel<<<npairs, 64 * ((a.I / 16 + 63) / 64), 0, s>>>(a, ws);
   if (slice_fits(npairs, a.H, a.I)) {
-    const int nw = slice_waves(npairs);
-    const size_t lds = slice_lds_bytes(npairs, a.I, nw);
-    const int own = (npairs + nw - 1) / nw;
-    const int jobs = (npairs * (a.I / 16) + 64 * nw - 1) / (64 * nw);
-    if (own <= 2 && jobs <= 1) {
-      if (FUSED) down_slice_kernel<true, 2, 1><<<a.H / 16, 64 * nw, lds, s>>>(a, ws, w_out, residual, y);
-      else down_slice_kernel<false, 2, 1><<<a.H / 16, 64 * nw, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
-    } else {
-      if (FUSED) down_slice_kernel<true, 4, 2><<<a.H / 16, 64 * nw, lds, s>>>(a, ws, w_out, residual, y);
-      else down_slice_kernel<false, 4, 2><<<a.H / 16, 64 * nw, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
-    }
+    const size_t lds = slice_lds_bytes(npairs, a.I);
+    if (FUSED) down_slice_kernel<true><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y);
+    else down_slice_kernel<false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
   } else {
     const int nw2 = dec_waves(a.I / 32);
-    const size_t lds2 = (size_t)MAXP * a.I * 2 + (size_t)nw2 * a.I * 4 + (size_t)nw2 * MAXP * 64 * 4;
+    const size_t lds2 = (size_t)MAXP * a.I * 2 + (size_t)nw2 * MAXP * 64 * 4;
     down_decode_kernel<MAXP, DEC_CPW><<<dim3(npairs, a.H / 64), 64 * nw2, lds2, s>>>(a, ws);
     if (FUSED) (void)launch_combine(a.out, w_out, residual, a.T, a.k, a.H, y, s);
   }
 }
 
 hipError_t launch_ffn_decode(const FfnArgs& a, void* ws, hipStream_t s) {
-  DecodeWs w{reinterpret_cast<float*>(ws)};
+  DecodeWs w = carve_decode(ws, a.H, a.I, a.T * a.k, nullptr);
   if (a.T == 1) launch_decode_pair<1, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
   else launch_decode_pair<8, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
   return hipGetLastError();
 }
 
-// Fused layer workspace: logits, ids, w, x^ (codes, scales, ts), gate/up
-// partials, o.
+// Fused layer workspace: logits, ids, w, x^ (codes, scales, ts), the decode
+// workspace (gate/up partials, h^), o.
 struct LayerWs {
   float* logits; int32_t* ids; float* w; uint8_t* xc; uint8_t* xs; float* xts;
   float* gu; float* out;
@@ -759,7 +753,7 @@ hipError_t launch_layer_decode(const LayerArgs& L, void* ws, hipStream_t s) {
   float* w_out = L.w_out ? L.w_out : w.w;
   a.ids = ids_out;
   a.out = w.out;
-  DecodeWs dw{w.gu};
+  DecodeWs dw = carve_decode(w.gu, L.H, L.I, L.T * L.k, nullptr);
   const uint16_t* res = L.residual ? L.x : nullptr;
   if (L.T == 1)
     launch_decode_pair<1, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s);

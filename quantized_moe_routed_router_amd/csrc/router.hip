@@ -4,6 +4,7 @@
 // selected k.  The pages: every token activates a subset of the experts (blog
 // "Capy Flash ...", section "Where the experts live"); picked experts are
 // ranked (forum repost, paragraph "Where it stands").
+#include "../../include/moe.h"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -73,12 +74,13 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
+  __shared__ int scr[4][64 + MOE_MAX_K];
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;                                  // wave-uniform; no block barrier below
   int id;
   float wt;
-  topk_wave_any(logits + (size_t)t * E, E, k, lane, &id, &wt);
+  topk_wave_any(logits + (size_t)t * E, E, k, lane, scr[threadIdx.x >> 6], &id, &wt);
   if (lane < k) {
     ids[(size_t)t * k + lane] = id;
     w[(size_t)t * k + lane] = wt;
