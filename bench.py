@@ -163,6 +163,52 @@ def cpu_baseline(wl, n_tokens: int, dev):
                        f"(numpy oracle, fp64 matmuls on dequantized weights, {dt:.1f} s)")
 
 
+def time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream):
+    """The expert FFN call (gate/up, h^, down kernels) timed eagerly with
+    events on its own stream around each launch, cycling layers and tokens.
+    Returns (us per launch, algorithmic HBM bytes per launch)."""
+    import numpy as np
+    import torch
+    import quantized_moe_routed_router_amd as moe
+    with torch.cuda.stream(stream):            # inputs of the standalone FFN calls
+        for li in range(NL):
+            layers[li].forward(xs[li % NX:li % NX + 1], bufs[li], residual=True, stream=stream)
+    torch.cuda.synchronize()
+    n_ffn = min(400, 4 * cycle)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ffn)]
+    with torch.cuda.stream(stream):
+        for i in range(n_ffn):
+            li = i % NL
+            L, b = layers[li], bufs[li]
+            xq = (b["x_codes"], b["x_scales"], b["x_ts"])
+            evs[i][0].record(stream)
+            moe.moe_expert_ffn_decode(L.d, L.experts(), xq, b["ids"], 1, b["out"], b["ws"],
+                                      b["ws_bytes"], None, stream)
+            evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ffn_us = float(np.mean([a.elapsed_time(c) for a, c in evs[4:]])) * 1e3
+    # algorithmic bytes: the k distinct experts' packed gate/up/down (one
+    # token), x^ in and the k fp32 output rows out; the call's own
+    # intermediates (gate/up partials, h^) are not counted
+    exp_bytes = moe.moe_packed_bytes(layers[0].d, 0) // wl.E + moe.moe_packed_bytes(layers[0].d, 1) // wl.E
+    act_bytes = wl.H // 2 + wl.H // 16 + 4 + wl.k * wl.H * 4
+    ffn_bytes = wl.k * exp_bytes + act_bytes
+    log(f"expert FFN: {ffn_us:.2f} us/launch, {ffn_bytes} B -> {ffn_bytes / ffn_us / 1e3:.0f} GB/s")
+    return ffn_us, ffn_bytes
+
+
+def copy_calibration(dev):
+    """Three 1 GiB device-to-device copies: a kernel of known traffic for
+    scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    bb = torch.empty_like(a)
+    for _ in range(3):
+        bb.copy_(a)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 x 1 GiB device copies done")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +223,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--ffn-only", action="store_true",
+                    help="only the eager expert-FFN launches (for counter runs): no graph, no prefill")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -202,6 +250,12 @@ def main():
 
     stream = torch.cuda.Stream()
     cycle = NL * max(1, (NX // NL))            # steps per captured graph
+    if args.ffn_only:
+        ffn_us, ffn_bytes = time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream)
+        if args.copy_calibration:
+            copy_calibration(dev)
+        print(json.dumps({"ffn_us": round(ffn_us, 3), "ffn_bytes": ffn_bytes}), flush=True)
+        return
     def step(i):
         li = i % NL
         x = xs[i % NX:i % NX + 1]
@@ -241,43 +295,15 @@ def main():
     ms_step = ms_total / steps
     log(f"graph: {steps} steps in {ms_total:.3f} ms (host {t_host * 1e3:.1f} ms): {ms_step * 1e3:.2f} us/step")
 
-    with torch.cuda.stream(stream):            # inputs of the standalone FFN calls below
-        for li in range(NL):
-            layers[li].forward(xs[li % NX:li % NX + 1], bufs[li], residual=True, stream=stream)
-    torch.cuda.synchronize()
-    # ---- the dominant kernels: the expert FFN call (gate/up + down), eager,
-    # events on its own stream around each launch, cycling layers and tokens
-    n_ffn = min(400, 4 * cycle)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ffn)]
-    with torch.cuda.stream(stream):
-        for i in range(n_ffn):
-            li = i % NL
-            L, b = layers[li], bufs[li]
-            xq = (b["x_codes"], b["x_scales"], b["x_ts"])
-            evs[i][0].record(stream)
-            moe.moe_expert_ffn_decode(L.d, L.experts(), xq, b["ids"], 1, b["out"], b["ws"],
-                                      b["ws_bytes"], None, stream)
-            evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    ffn_us = float(np.mean([a.elapsed_time(c) for a, c in evs[4:]])) * 1e3
-    # distinct experts per step = k (one token): all of their gate/up/down bytes
-    exp_bytes = moe.moe_packed_bytes(layers[0].d, 0) // wl.E + moe.moe_packed_bytes(layers[0].d, 1) // wl.E
-    act_bytes = wl.H // 2 + wl.H // 16 + 4 + wl.k * wl.I * 4 * 2 + wl.k * wl.H * 4
-    ffn_bytes = wl.k * exp_bytes + act_bytes
+    ffn_us, ffn_bytes = time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream)
     achieved = ffn_bytes / (ffn_us * 1e-6) / 1e9
-    log(f"expert FFN: {ffn_us:.2f} us/launch, {ffn_bytes} B -> {achieved:.0f} GB/s")
 
     # whole step's algorithmic HBM bytes: router weights + k experts + activations
     step_bytes = wl.E * wl.H * 4 + ffn_bytes + wl.H * 2 * 2 + wl.k * wl.H * 4
     layer_gbps = step_bytes / (ms_step * 1e-3) / 1e9
 
     if args.copy_calibration:
-        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        bb = torch.empty_like(a)
-        for _ in range(3):
-            bb.copy_(a)
-        torch.cuda.synchronize()
-        log("copy calibration: 3 x 1 GiB device copies done")
+        copy_calibration(dev)
 
     prefill = None
     if not args.no_prefill:
@@ -309,7 +335,7 @@ def main():
                    "layer_bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "expert FFN decode (gate_up_decode_kernel + down_decode_kernel)",
+                     "traffic": traffic, "kernel": "moe_expert_ffn_decode (gate_up_decode_kernel, h_quant_decode_kernel, down_slice_kernel)",
                      "bytes_per_launch": ffn_bytes, "us_per_launch": round(ffn_us, 3)},
         "cpu_baseline": cpu,
         "prefill_64k": prefill,
