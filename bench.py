@@ -135,6 +135,71 @@ def prefill_64k(L0, dev, steps: int):
     return res
 
 
+def stack_decode(layers, dev, reps: int):
+    """The full-depth decode stack: one token (then eight) carried through all
+    resident layers, each layer with the residual add and its own router with
+    logits scaled to N(0, 1) (the 48-layer recipe), each output brought back
+    to the first layer's input RMS (moe_rms_norm) for the next layer; the
+    whole pass captured as one HIP graph.  The experts are the resident
+    layers' own."""
+    import copy
+    import numpy as np
+    import torch
+    import synth
+    swl = synth.WORKLOADS["stack48"]
+    st = []
+    for li, L in enumerate(layers):
+        S = copy.copy(L)                       # shares the resident experts
+        S.set_router(synth.router_weights_torch(swl, li, dev))
+        st.append(S)
+    res = {"layers": len(st)}
+    import quantized_moe_routed_router_amd as moe
+    for T in (1, 8):
+        fbs = [S.alloc_fused(T) for S in st]
+        xns = [torch.empty((T, swl.H), dtype=torch.int16, device=dev) for _ in st]
+        x0 = synth.activations_torch(swl, T, 950 + T, dev).view(torch.int16)
+        stream = torch.cuda.Stream()
+
+        def chain():
+            x = x0
+            for S, fb, xn in zip(st, fbs, xns):
+                S.forward_fused(x, fb, residual=True, stream=stream)
+                moe.moe_rms_norm(fb["y"], T, swl.H, synth.STACK_INPUT_RMS, xn, stream)
+                x = xn
+
+        with torch.cuda.stream(stream):
+            chain()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            chain()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                g.replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        with torch.cuda.stream(stream):
+            for _ in range(reps):
+                g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / reps
+        distinct = float(np.mean([len(torch.unique(fb["ids"])) for fb in fbs]))
+        E, H, I = st[0].E, st[0].H, st[0].I
+        exp_b = (3 * H * I) // 2 + (3 * H * I) // 16
+        step_bytes = distinct * exp_b + E * H * 4
+        res[f"b{T}"] = {"tok_s": round(T / (ms * 1e-3), 1), "us_per_layer": round(ms * 1e3 / len(st), 3),
+                        "distinct_experts_per_layer": round(distinct, 2),
+                        "layer_hbm_gbps": round(step_bytes / (ms * 1e-3 / len(st)) / 1e9, 1)}
+        log(f"stack {len(st)} layers, {T} token(s): {ms * 1e3:.1f} us per pass, "
+            f"{T / ms * 1e3:.0f} tok/s, {distinct:.1f} distinct experts per layer")
+        del fbs, xns, g
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, n_tokens: int, dev):
     """The oracle on the host: n_tokens single-token steps through layer 0
     (router, quantizer, expert FFN with on-the-fly dequantization, combine).
@@ -214,12 +279,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=960)
     ap.add_argument("--warmup", type=int, default=96)
-    ap.add_argument("--layers", type=int, default=24, help="distinct resident layers cycled")
-    ap.add_argument("--cpu-tokens", type=int, default=6)
+    ap.add_argument("--layers", type=int, default=48, help="distinct resident layers cycled")
+    ap.add_argument("--cpu-tokens", type=int, default=30)
     ap.add_argument("--path", choices=["fused", "separate"], default="fused",
                     help="fused: moe_layer_decode (3 kernels); separate: the 4 entry points (6 kernels)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 65,536-token prefill figures")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 48-layer stack figures")
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
@@ -305,6 +371,10 @@ def main():
     if args.copy_calibration:
         copy_calibration(dev)
 
+    stack = None
+    if not args.no_stack:
+        stack = stack_decode(layers, dev, reps=20)
+
     prefill = None
     if not args.no_prefill:
         prefill = prefill_64k(layers[0], dev, args.prefill_steps)
@@ -338,6 +408,7 @@ def main():
                      "traffic": traffic, "kernel": "moe_expert_ffn_decode (gate_up_decode_kernel, h_quant_decode_kernel, down_slice_kernel)",
                      "bytes_per_launch": ffn_bytes, "us_per_launch": round(ffn_us, 3)},
         "cpu_baseline": cpu,
+        "stack_decode": stack,
         "prefill_64k": prefill,
     }
     print(json.dumps(out), flush=True)

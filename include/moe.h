@@ -174,6 +174,16 @@ int moe_layer_decode(const moe_dims* dims, const moe_experts* experts, const uin
 int moe_combine(const float* out, const float* w, const uint16_t* residual, int T,
                 int k, int H, uint16_t* y, void* stream);
 
+/* Row-wise RMS rescale, the glue between the layers of the full-depth
+ * decode stack (48 layers, residual add, routing near uniform at every
+ * layer): y[t, :] = bf16_rne( x[t, :] * target_rms / sqrt(mean_h x[t, h]^2) ),
+ * fp32 sum of squares, IEEE division and square root; a zero row gives 0.
+ * Not one of the pages' steps: it keeps each layer's input at the first
+ * layer's scale, without which the residual stream of random-weight layers
+ * grows until the routing is one-hot and bf16 overflows.  x, y [T, H] bf16
+ * (may alias); H % 8 == 0; target_rms positive and finite. */
+int moe_rms_norm(const uint16_t* x, int T, int H, float target_rms, uint16_t* y, void* stream);
+
 /* ------------------------------------------------------------------ */
 /* Sizes, weight preparation, permute, capacity                        */
 /* ------------------------------------------------------------------ */

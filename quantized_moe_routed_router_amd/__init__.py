@@ -73,6 +73,7 @@ _SIGS = {
                                     ctypes.POINTER(moe_actq), _P, _I, _P, _P, _SZ,
                                     ctypes.POINTER(moe_ffn_debug), _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
+    "moe_rms_norm": (_I, [_P, _I, _I, ctypes.c_float, _P, _P]),
     "moe_layer_decode_workspace_bytes": (_SZ, [ctypes.POINTER(moe_dims), _I]),
     "moe_layer_decode": (_I, [ctypes.POINTER(moe_dims), ctypes.POINTER(moe_experts), _P, _P, _P, _I,
                               _I, _P, _P, _P, _P, _SZ, _P]),
@@ -205,6 +206,10 @@ def moe_expert_ffn_prefill(d: moe_dims, experts: dict, xq, ids, T: int, out, ws,
 def moe_combine(out, w, residual, T: int, k: int, H: int, y, stream=None):
     _check(lib().moe_combine(_ptr(out), _ptr(w), _ptr(residual), T, k, H, _ptr(y),
                              _stream(stream)))
+
+
+def moe_rms_norm(x, T: int, H: int, target_rms: float, y, stream=None):
+    _check(lib().moe_rms_norm(_ptr(x), T, H, float(target_rms), _ptr(y), _stream(stream)))
 
 
 def moe_layer_decode_workspace_bytes(d: moe_dims, T: int) -> int:

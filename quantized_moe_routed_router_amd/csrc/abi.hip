@@ -331,6 +331,17 @@ int moe_combine(const float* out, const float* w, const uint16_t* residual, int 
   return hip_status(moe::launch_combine(out, w, residual, T, k, H, y, as_stream(stream)), fn);
 }
 
+int moe_rms_norm(const uint16_t* x, int T, int H, float target_rms, uint16_t* y, void* stream) {
+  const char* fn = "moe_rms_norm";
+  if (T < 0) return fail(MOE_ERR_SHAPE, "%s: T = %d is negative", fn, T);
+  if (H < 8 || H % 8) return fail(MOE_ERR_SHAPE, "%s: H = %d is not a positive multiple of 8", fn, H);
+  if (!(target_rms > 0.0f) || !(target_rms < 3.0e38f))
+    return fail(MOE_ERR_INVALID, "%s: target_rms = %g must be positive and finite", fn, (double)target_rms);
+  if (T == 0) return ok();
+  NEED_PTR(x); NEED_PTR(y);
+  return hip_status(moe::launch_rms_norm(x, T, H, target_rms, y, as_stream(stream)), fn);
+}
+
 int moe_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
                 int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "moe_permute";

@@ -51,4 +51,49 @@ hipError_t launch_combine(const float* out, const float* w, const uint16_t* resi
   return hipGetLastError();
 }
 
+// Input rescaling between the layers of the full-depth decode stack (the
+// reading of "routing near uniform" at every layer: each layer's output is
+// brought back to the first layer's input RMS before the next layer; not one
+// of the pages' steps).  Block = one token row: fp32 sum of squares (per
+// thread, then a fixed-order DPP and cross-wave sum), s = target / sqrt(mean)
+// with IEEE division and square root, y = bf16_rne(x * s); a zero row gives 0.
+__global__ __launch_bounds__(256) void rms_norm_kernel(const uint16_t* __restrict__ x, int H,
+                                                       float target, uint16_t* __restrict__ y) {
+  __shared__ float red[4];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint16_t* xr = x + (size_t)t * H;
+  float ss = 0.0f;
+  for (int c = tid * 8; c < H; c += 256 * 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = bf16_to_f32(vw[i] & 0xFFFF), b = bf16_to_f32(vw[i] >> 16);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
+  }
+  ss = dpp_wave_sum(ss);
+  if (lane == 0) red[wv] = ss;
+  __syncthreads();
+  const float total = ((red[0] + red[1]) + red[2]) + red[3];
+  const float ms = __fdiv_rn(total, (float)H);
+  const float sc = ms > 0.0f ? __fdiv_rn(target, __fsqrt_rn(ms)) : 0.0f;
+  for (int c = tid * 8; c < H; c += 256 * 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = f32_to_bf16_rne(bf16_to_f32(vw[i] & 0xFFFF) * sc) | (f32_to_bf16_rne(bf16_to_f32(vw[i] >> 16) * sc) << 16);
+    *reinterpret_cast<u32x4*>(y + (size_t)t * H + c) = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
+hipError_t launch_rms_norm(const uint16_t* x, int T, int H, float target, uint16_t* y, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  rms_norm_kernel<<<T, 256, 0, s>>>(x, H, target, y);
+  return hipGetLastError();
+}
+
 }  // namespace moe

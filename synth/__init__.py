@@ -57,6 +57,9 @@ class Workload:
 # E[x^2] = 0.99 * 1 + 0.01 * 400 = 4.99.  A router std of 1/sqrt(H * E[x^2])
 # makes each logit ~N(0, 1) ("logits N(0,1)-scaled" for the 48-layer stack).
 _STACK_ROUTER_STD = 1.0 / math.sqrt(2560 * 4.99)
+# The first layer's input RMS, sqrt(E[x^2]): the scale every later layer's
+# input is brought back to in the 48-layer stack.
+STACK_INPUT_RMS = math.sqrt(4.99)
 
 WORKLOADS = {
     # Tiny single layer, small enough for exact brute force.

@@ -79,6 +79,14 @@ def test_validation_null_and_shape():
     assert code == m.MOE_ERR_WORKSPACE
     code, msg = _err(m.moe_pack_codebook, d, 0, 1, 1024, 1024, 1024, 1024, 1024, 0)
     assert code == m.MOE_ERR_INVALID and "MOE_FMT_CB3G128" in msg
+    code, msg = _err(m.moe_rms_norm, 1024, 2, 100, 1.0, 1024, 0)
+    assert code == m.MOE_ERR_SHAPE and "H = 100" in msg
+    code, msg = _err(m.moe_rms_norm, 1024, 2, 256, 0.0, 1024, 0)
+    assert code == m.MOE_ERR_INVALID and "target_rms" in msg
+    code, msg = _err(m.moe_rms_norm, 1024, 2, 256, float("nan"), 1024, 0)
+    assert code == m.MOE_ERR_INVALID and "target_rms" in msg
+    code, msg = _err(m.moe_rms_norm, None, 2, 256, 1.0, 1024, 0)
+    assert code == m.MOE_ERR_INVALID and "x is NULL" in msg
 
 
 def test_capacity_verdict_with_numbers():
@@ -96,4 +104,5 @@ def test_zero_sized_calls_enqueue_nothing():
     m.moe_quantize_act(None, 0, 256, None, None, None, 0)
     m.moe_router_topk(None, None, None, 0, d, None, None, None, 0)
     m.moe_combine(None, None, None, 0, 2, 256, None, 0)
+    m.moe_rms_norm(None, 0, 256, 1.0, None, 0)
     m.moe_quantize_weights(None, 0, 4, 16, None, None, None, 0)
