@@ -144,7 +144,7 @@ int moe_expert_ffn_decode(const moe_dims* dims, const moe_experts* experts,
 /* Expert FFN for any T >= 1 (prefill): same result as the decode entry, as a
  * grouped GEMM over the token-by-expert permutation (stable counting sort
  * of the (t, slot) pairs by expert) on matrix cores.  Takes both gate/up
- * formats.  ws: at least moe_ffn_workspace_bytes(dims, T, 1) bytes.
+ * formats; I <= 4096.  ws: at least moe_ffn_workspace_bytes(dims, T, 1) bytes.
  * Routing-dependent sizes never reach the host. */
 int moe_expert_ffn_prefill(const moe_dims* dims, const moe_experts* experts,
                            const moe_actq* xq, const int32_t* ids, int T, float* out,

@@ -314,6 +314,7 @@ int moe_expert_ffn_prefill(const moe_dims* d, const moe_experts* ex, const moe_a
                            const moe_ffn_debug* dbg, void* stream) {
   const char* fn = "moe_expert_ffn_prefill";
   if (T < 1) return fail(MOE_ERR_SHAPE, "%s: T = %d must be >= 1", fn, T);
+  if (d && d->I > 4096) return fail(MOE_ERR_SHAPE, "%s: I = %d above 4096", fn, d->I);
   if ((long long)T * (d ? d->k : 1) > (1LL << 30)) return fail(MOE_ERR_SHAPE, "%s: T = %d too large", fn, T);
   int st = check_ffn(fn, d, ex, xq, ids, T, out, ws, ws_bytes, dbg, true);
   if (st) return st;

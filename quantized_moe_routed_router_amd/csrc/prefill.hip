@@ -275,8 +275,11 @@ __global__ __launch_bounds__(PF_THREADS) void grouped_gemm_kernel(FfnArgs a, Pre
   }
 }
 
-// NVFP4 of each h row (sorted order), one wave per row; also the optional
-// debug copies in (t, slot) order.
+// NVFP4 of each h row (sorted order), one wave per row, one pass: lane l
+// holds the row's 16-element blocks l, l+64, ... (all loads first), the row
+// amax is a wave max of the block maxima; also the optional debug copies in
+// (t, slot) order.  I <= 64 * HQ_MAXB * 16.
+constexpr int HQ_MAXB = 4;
 __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, int N) {
   const int lane = threadIdx.x & 63;
   const int pos = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -285,26 +288,38 @@ __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, in
   const int I = a.I, nblk = I / 16;
   const float* hr = w.h + (size_t)pos * I;
   const int pair = w.perm[pos];
-  float amax = 0.0f;
-  for (int c = lane; c < I; c += 64) {
-    const float v = hr[c];
-    amax = fmaxf(amax, fabsf(v));
-    if (a.dbg_h) a.dbg_h[(size_t)pair * I + c] = v;
-  }
-  amax = wave_max(amax);
-  const float ts = tensor_scale_from_amax(amax);
-  for (int b = lane; b < nblk; b += 64) {
-    float v[16];
+  float v[HQ_MAXB][16];
+#pragma unroll
+  for (int j = 0; j < HQ_MAXB; ++j) {
+    const int b = min(lane + 64 * j, nblk - 1);          // clamped: straight-line loads
     const float4_t* src = reinterpret_cast<const float4_t*>(hr + b * 16);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float4_t f = src[r];
-      v[4 * r] = f.x; v[4 * r + 1] = f.y; v[4 * r + 2] = f.z; v[4 * r + 3] = f.w;
+      const float4_t f = src[r];
+      v[j][4 * r] = f.x; v[j][4 * r + 1] = f.y; v[j][4 * r + 2] = f.z; v[j][4 * r + 3] = f.w;
     }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < HQ_MAXB; ++j)
+    if (lane + 64 * j < nblk) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(v[j][c]));
+    }
+  amax = dpp_wave_max(amax);
+  const float ts = tensor_scale_from_amax(amax);
+#pragma unroll
+  for (int j = 0; j < HQ_MAXB; ++j) {
+    const int b = lane + 64 * j;
+    if (b >= nblk) continue;
     uint32_t pk[2];
-    const uint32_t sb = quantize_block16(v, ts, pk);
+    const uint32_t sb = quantize_block16(v[j], ts, pk);
     *reinterpret_cast<u32x2*>(w.hq_codes + (size_t)pos * (I / 2) + b * 8) = u32x2{pk[0], pk[1]};
     w.hq_scales[(size_t)pos * nblk + b] = (uint8_t)sb;
+    if (a.dbg_h) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) a.dbg_h[(size_t)pair * I + b * 16 + c] = v[j][c];
+    }
     if (a.dbg_h_codes) *reinterpret_cast<u32x2*>(a.dbg_h_codes + (size_t)pair * (I / 2) + b * 8) = u32x2{pk[0], pk[1]};
     if (a.dbg_h_scales) a.dbg_h_scales[(size_t)pair * nblk + b] = (uint8_t)sb;
   }
@@ -317,10 +332,10 @@ __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, in
 // Pairs whose id is outside [0, E): zero output rows (they sit after
 // offsets[E] in sorted order).
 __global__ void zero_invalid_kernel(FfnArgs a, PrefillWs w, int N) {
-  const int pos = w.offsets[a.E] + blockIdx.x;
-  if (pos >= N) return;
-  const int pair = w.perm[pos];
-  for (int c = threadIdx.x; c < a.H; c += blockDim.x) a.out[(size_t)pair * a.H + c] = 0.0f;
+  for (int pos = w.offsets[a.E] + blockIdx.x; pos < N; pos += gridDim.x) {
+    const int pair = w.perm[pos];
+    for (int c = threadIdx.x; c < a.H; c += blockDim.x) a.out[(size_t)pair * a.H + c] = 0.0f;
+  }
 }
 
 hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
@@ -338,7 +353,7 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
   h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
   const int nt_dn = a.H / BN;
   grouped_gemm_kernel<2><<<max_mtiles * nt_dn, PF_THREADS, 0, s>>>(a, w, nt_dn);
-  zero_invalid_kernel<<<N, 256, 0, s>>>(a, w, N);
+  zero_invalid_kernel<<<N < 256 ? N : 256, 256, 0, s>>>(a, w, N);
   return hipGetLastError();
 }
 
