@@ -18,6 +18,8 @@
 //   h quant   NVFP4 of each h row (one tensor scale per (t, slot) row)
 //   down      same GEMM on h^ rows; epilogue scales by ts_h ts_down and
 //             scatters o rows back to (t, slot) through perm.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -275,6 +277,195 @@ __global__ __launch_bounds__(PF_THREADS) void grouped_gemm_kernel(FfnArgs a, Pre
   }
 }
 
+// ---------------------------------------------------------------- 256 x 256 tiles
+// The main prefill GEMM: one 256 x 256 output tile per block of 8 waves
+// (2 x 4), each wave a 128 x 64 patch (4 x 2 tiles of v_mfma_f32_32x32x16_f16,
+// 128 accumulator registers), two waves per SIMD so one wave's dequantization
+// runs while the other's MFMAs execute.  LDS holds two K-step buffers of A
+// (256 activation rows) and B (256 weight columns) as f16 (147,456 B of the
+// 160 KiB), as four distinct objects.  Step s: the MFMAs on buffer s%2, the
+// registers fetched for step s+1 dequantized into buffer (s+1)%2, step s+2's
+// global loads issued, one barrier.  A buffer is rewritten only after every
+// wave has passed the barrier that ends the step reading it.  Loads are
+// straight-line: a padding row reads a valid row with scale 0.
+constexpr int BB = 256, BBK = 64, BLDK = BBK + 8, BTHREADS = 512;
+
+template <int MODE>
+__global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, PrefillWs w, int n_ntiles) {
+  __shared__ __align__(16) _Float16 As0[BB][BLDK], As1[BB][BLDK], Bs0[BB][BLDK], Bs1[BB][BLDK];
+  typedef _Float16 (*TileP)[BLDK];
+  __shared__ int row_pos[BB];
+  __shared__ int row_pair[BB];         // (t, slot) pair of the row: where down writes o
+  __shared__ float row_scale[BB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 2, wn = wv & 3;                    // wave patch: rows wm*128, cols wn*64
+  const int gm = blockIdx.x / n_ntiles, nt = blockIdx.x % n_ntiles;
+  const int total_tiles = w.tile_prefix[a.E];
+  if (gm >= total_tiles) return;
+  const int e = find_expert(w.tile_prefix, a.E, gm);
+  const int mt = gm - w.tile_prefix[e];
+  const int row0 = w.offsets[e] + mt * BB, row_end = w.offsets[e + 1];
+
+  const bool down = MODE == 2;
+  const int K = down ? a.I : a.H;
+  const int S = K / BBK;                                   // even, >= 4
+  const size_t w_tile_bytes = (MODE == 1) ? cb_tile_bytes(K) : tile_bytes(K);
+  const size_t w_expert_bytes = down ? down_expert_bytes(a.H, a.I)
+                                     : (MODE == 1 ? cb_gate_up_expert_bytes(a.H, a.I) : gate_up_expert_bytes(a.H, a.I));
+  const uint8_t* wbase = (down ? a.down : a.gate_up) + (size_t)e * w_expert_bytes + (size_t)(nt * 4) * w_tile_bytes;
+
+  if (tid < BB) {
+    const int pos = row0 + tid;
+    int rp = -1, pr = 0;
+    float sc = 0.0f;
+    if (pos < row_end) {
+      rp = pos;
+      pr = w.perm[pos];
+      sc = down ? w.hq_ts[pos] : a.x_ts[pr / a.k];
+    }
+    row_pos[tid] = rp;
+    row_pair[tid] = pr;
+    row_scale[tid] = sc;
+  }
+  __syncthreads();
+
+  // staging roles: A row sr, chunk sc (32 K-elements); B packed tile bj,
+  // lane bl, chunk sc
+  const int sr = tid >> 1, sc = tid & 1;
+  const bool avalid = row_pos[sr] >= 0;
+  const uint8_t* acodes;
+  const uint8_t* ascales;
+  {
+    const int rp = avalid ? row_pos[sr] : row0;         // row0 < row_end: a valid row
+    if (down) {
+      acodes = w.hq_codes + (size_t)rp * (a.I / 2);
+      ascales = w.hq_scales + (size_t)rp * (a.I / 16);
+    } else {
+      const int t = w.perm[rp] / a.k;
+      acodes = a.x_codes + (size_t)t * (a.H / 2);
+      ascales = a.x_scales + (size_t)t * (a.H / 16);
+    }
+  }
+  const int bj = sr >> 6, bl = sr & 63;
+  const uint8_t* btile = wbase + (size_t)bj * w_tile_bytes;
+
+  u32x4 acw, bcw;
+  uint32_t asw = 0, bsw = 0, p0 = 0, p1 = 0, p2 = 0;
+  auto load_step = [&](int st) {
+    const int k0 = st * BBK + 32 * sc;
+    acw = *reinterpret_cast<const u32x4*>(acodes + k0 / 2);
+    const uint32_t s1 = *reinterpret_cast<const uint16_t*>(ascales + k0 / 16);
+    asw = avalid ? s1 : 0u;                              // padding rows: scale 0 stages zeros
+    const int ck = k0 / 32;
+    if (MODE == 1) {
+      const uint8_t* grp = btile + (size_t)(ck >> 2) * cb_group_bytes();
+      const uint32_t* planes = reinterpret_cast<const uint32_t*>(grp + bl * 48);
+      const int d = ck & 3;
+      p0 = planes[d]; p1 = planes[4 + d]; p2 = planes[8 + d];
+      bcw = *reinterpret_cast<const u32x4*>(grp + 64 * 48 + bl * 16);
+    } else {
+      bcw = *reinterpret_cast<const u32x4*>(btile + (size_t)ck * 1024 + bl * 16);
+      bsw = *reinterpret_cast<const uint16_t*>(btile + tile_scale_offset(K) + (size_t)(ck >> 2) * 512 + bl * 8 + (ck & 3) * 2);
+    }
+  };
+  auto stage = [&](auto bconst) {
+    constexpr int b = decltype(bconst)::value;
+    TileP As = b ? As1 : As0;
+    TileP Bs = b ? Bs1 : Bs0;
+    half2_t o[16];
+    dequant32_nvfp4(acw, asw, o);
+    store32(&As[sr][32 * sc], o);
+    if (MODE == 1) dequant32_cb(p0, p1, p2, bcw, o);
+    else dequant32_nvfp4(bcw, bsw, o);
+    store32(&Bs[sr][32 * sc], o);
+  };
+
+  float16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto mfma_step = [&](auto bconst) {
+    constexpr int b = decltype(bconst)::value;
+    TileP As = b ? As1 : As0;
+    TileP Bs = b ? Bs1 : Bs0;
+#pragma unroll
+    for (int kk = 0; kk < BBK; kk += 16) {
+      half8_t af[4], bf[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const half8_t*>(&As[wm * 128 + i * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *reinterpret_cast<const half8_t*>(&Bs[wn * 64 + j * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  load_step(0);
+  stage(std::integral_constant<int, 0>{});
+  __syncthreads();
+  load_step(1);
+  for (int st = 0; st + 2 < S; st += 2) {                 // steps st, st+1 also fetch st+2, st+3
+    mfma_step(std::integral_constant<int, 0>{});
+    stage(std::integral_constant<int, 1>{});
+    load_step(st + 2);
+    __syncthreads();
+    mfma_step(std::integral_constant<int, 1>{});
+    stage(std::integral_constant<int, 0>{});
+    load_step(st + 3);
+    __syncthreads();
+  }
+  mfma_step(std::integral_constant<int, 0>{});            // step S-2, stages the last one
+  stage(std::integral_constant<int, 1>{});
+  __syncthreads();
+  mfma_step(std::integral_constant<int, 1>{});
+
+  // ---- epilogue.  acc[i][j][r]: row wm*128 + i*32 + (r%4) + 8*(r/4) + 4*(lane/32),
+  // col wn*64 + j*32 + lane%32 of the 256x256 tile
+  if (!down) {
+    const float tsg = (MODE == 0) ? a.ts_gate[e] : 1.0f;
+    const float tsu = (MODE == 0) ? a.ts_up[e] : 1.0f;
+    // packed tile nt*4 + wn: gate cols = MFMA tile 0, up cols = tile 1
+    const int n = (nt * 4 + wn) * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = wm * 128 + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+        const int pos = row_pos[rl];
+        if (pos < 0) continue;
+        const float sx = row_scale[rl];
+        const float g = acc[i][0][r] * (sx * tsg);
+        const float u = acc[i][1][r] * (sx * tsu);
+        w.h[(size_t)pos * a.I + n] = silu_mul(g, u);
+      }
+  } else {
+    const float tsd = a.ts_down[e];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = nt * BB + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * 128 + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+          const int pos = row_pos[rl];
+          if (pos < 0) continue;
+          a.out[(size_t)row_pair[rl] * a.H + n] = acc[i][j][r] * (row_scale[rl] * tsd);
+        }
+    }
+  }
+}
+
 // NVFP4 of each h row (sorted order), one wave per row, one pass: lane l
 // holds the row's 16-element blocks l, l+64, ... (all loads first), the row
 // amax is a wave max of the block maxima; also the optional debug copies in
@@ -338,9 +529,30 @@ __global__ void zero_invalid_kernel(FfnArgs a, PrefillWs w, int N) {
   }
 }
 
+static bool big_tiles_fit(const FfnArgs& a) {
+  return a.H % BB == 0 && (2 * a.I) % BB == 0 && a.I % (2 * BBK) == 0 && a.I >= 4 * BBK &&
+         a.H % (2 * BBK) == 0 && a.H >= 4 * BBK;
+}
+
 hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
   const int N = a.T * a.k;
   PrefillWs w = carve(ws, a.E, a.I, a.k, a.T, nullptr);
+  if (big_tiles_fit(a)) {
+    hipError_t err = launch_permute(a.ids, a.T, a.k, a.E, w.counts, w.offsets, w.perm, w.inv,
+                                    w.perm_ws, w.tile_prefix, BB, s);
+    if (err != hipSuccess) return err;
+    const int max_mtiles = (N + BB - 1) / BB + a.E;
+    const int nt_gu = (2 * a.I) / BB;
+    if (a.fmt == FMT_CB3G128)
+      grouped_gemm_big_kernel<1><<<max_mtiles * nt_gu, BTHREADS, 0, s>>>(a, w, nt_gu);
+    else
+      grouped_gemm_big_kernel<0><<<max_mtiles * nt_gu, BTHREADS, 0, s>>>(a, w, nt_gu);
+    h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
+    const int nt_dn = a.H / BB;
+    grouped_gemm_big_kernel<2><<<max_mtiles * nt_dn, BTHREADS, 0, s>>>(a, w, nt_dn);
+    zero_invalid_kernel<<<N < 256 ? N : 256, 256, 0, s>>>(a, w, N);
+    return hipGetLastError();
+  }
   hipError_t err = launch_permute(a.ids, a.T, a.k, a.E, w.counts, w.offsets, w.perm, w.inv,
                                   w.perm_ws, w.tile_prefix, BM, s);
   if (err != hipSuccess) return err;
