@@ -284,8 +284,8 @@ __global__ __launch_bounds__(PF_THREADS) void grouped_gemm_kernel(FfnArgs a, Pre
 // runs while the other's MFMAs execute.  LDS holds two K-step buffers of A
 // (256 activation rows) and B (256 weight columns) as f16 (147,456 B of the
 // 160 KiB), as four distinct objects.  Step s: the MFMAs on buffer s%2, the
-// registers fetched for step s+1 dequantized into buffer (s+1)%2, step s+2's
-// global loads issued, one barrier.  A buffer is rewritten only after every
+// registers fetched for step s+1 dequantized into buffer (s+1)%2, step s+3's
+// global loads issued (two register sets), one barrier.  A buffer is rewritten only after every
 // wave has passed the barrier that ends the step reading it.  Loads are
 // straight-line: a padding row reads a valid row with scale 0.
 constexpr int BB = 256, BBK = 64, BLDK = BBK + 8, BTHREADS = 512;
@@ -350,34 +350,38 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
   const int bj = sr >> 6, bl = sr & 63;
   const uint8_t* btile = wbase + (size_t)bj * w_tile_bytes;
 
-  u32x4 acw, bcw;
-  uint32_t asw = 0, bsw = 0, p0 = 0, p1 = 0, p2 = 0;
-  auto load_step = [&](int st) {
+  // one K step's global data for this thread
+  struct Regs {
+    u32x4 acw, bcw;
+    uint32_t asw, bsw, p0, p1, p2;
+  };
+  auto load_step = [&](Regs& R, int st) {
     const int k0 = st * BBK + 32 * sc;
-    acw = *reinterpret_cast<const u32x4*>(acodes + k0 / 2);
-    const uint32_t s1 = *reinterpret_cast<const uint16_t*>(ascales + k0 / 16);
-    asw = avalid ? s1 : 0u;                              // padding rows: scale 0 stages zeros
+    R.acw = *reinterpret_cast<const u32x4*>(acodes + k0 / 2);
+    R.asw = *reinterpret_cast<const uint16_t*>(ascales + k0 / 16);
     const int ck = k0 / 32;
     if (MODE == 1) {
       const uint8_t* grp = btile + (size_t)(ck >> 2) * cb_group_bytes();
       const uint32_t* planes = reinterpret_cast<const uint32_t*>(grp + bl * 48);
       const int d = ck & 3;
-      p0 = planes[d]; p1 = planes[4 + d]; p2 = planes[8 + d];
-      bcw = *reinterpret_cast<const u32x4*>(grp + 64 * 48 + bl * 16);
+      R.p0 = planes[d]; R.p1 = planes[4 + d]; R.p2 = planes[8 + d];
+      R.bcw = *reinterpret_cast<const u32x4*>(grp + 64 * 48 + bl * 16);
     } else {
-      bcw = *reinterpret_cast<const u32x4*>(btile + (size_t)ck * 1024 + bl * 16);
-      bsw = *reinterpret_cast<const uint16_t*>(btile + tile_scale_offset(K) + (size_t)(ck >> 2) * 512 + bl * 8 + (ck & 3) * 2);
+      R.bcw = *reinterpret_cast<const u32x4*>(btile + (size_t)ck * 1024 + bl * 16);
+      R.bsw = *reinterpret_cast<const uint16_t*>(btile + tile_scale_offset(K) + (size_t)(ck >> 2) * 512 + bl * 8 + (ck & 3) * 2);
     }
   };
-  auto stage = [&](auto bconst) {
+  auto stage = [&](const Regs& R, auto bconst) {
     constexpr int b = decltype(bconst)::value;
     TileP As = b ? As1 : As0;
     TileP Bs = b ? Bs1 : Bs0;
     half2_t o[16];
-    dequant32_nvfp4(acw, asw, o);
+    // padding rows: scale 0 stages zeros (applied here, not at the load, so
+    // the load is not waited for until its step is staged)
+    dequant32_nvfp4(R.acw, avalid ? R.asw : 0u, o);
     store32(&As[sr][32 * sc], o);
-    if (MODE == 1) dequant32_cb(p0, p1, p2, bcw, o);
-    else dequant32_nvfp4(bcw, bsw, o);
+    if (MODE == 1) dequant32_cb(R.p0, R.p1, R.p2, R.bcw, o);
+    else dequant32_nvfp4(R.bcw, R.bsw, o);
     store32(&Bs[sr][32 * sc], o);
   };
 
@@ -410,24 +414,40 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
     }
   };
 
-  load_step(0);
-  stage(std::integral_constant<int, 0>{});
+  // Two register sets, so a step's loads are issued two steps before it is
+  // staged.  At the top of each loop pass (step st even): buffer 0 holds
+  // step st, R1 step st+1, R0 step st+2.
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  Regs R0, R1;
+  load_step(R0, 0);
+  load_step(R1, 1);
+  stage(R0, B0{});
   __syncthreads();
-  load_step(1);
-  for (int st = 0; st + 2 < S; st += 2) {                 // steps st, st+1 also fetch st+2, st+3
-    mfma_step(std::integral_constant<int, 0>{});
-    stage(std::integral_constant<int, 1>{});
-    load_step(st + 2);
+  load_step(R0, 2);
+  int st = 0;
+  for (; st + 4 < S; st += 2) {
+    mfma_step(B0{});
+    stage(R1, B1{});
+    load_step(R1, st + 3);
     __syncthreads();
-    mfma_step(std::integral_constant<int, 1>{});
-    stage(std::integral_constant<int, 0>{});
-    load_step(st + 3);
+    mfma_step(B1{});
+    stage(R0, B0{});
+    load_step(R0, st + 4);
     __syncthreads();
   }
-  mfma_step(std::integral_constant<int, 0>{});            // step S-2, stages the last one
-  stage(std::integral_constant<int, 1>{});
+  // the last four steps (st = S - 4): buffer 0 = st, R1 = st+1, R0 = st+2
+  mfma_step(B0{});
+  stage(R1, B1{});
+  load_step(R1, st + 3);
   __syncthreads();
-  mfma_step(std::integral_constant<int, 1>{});
+  mfma_step(B1{});
+  stage(R0, B0{});
+  __syncthreads();
+  mfma_step(B0{});
+  stage(R1, B1{});
+  __syncthreads();
+  mfma_step(B1{});
 
   // ---- epilogue.  acc[i][j][r]: row wm*128 + i*32 + (r%4) + 8*(r/4) + 4*(lane/32),
   // col wn*64 + j*32 + lane%32 of the 256x256 tile
