@@ -19,14 +19,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (idx >= (size_t)T * per_row) return;
   const int t = (int)(idx / per_row), c = (int)(idx % per_row);
   float acc[8] = {};
-  for (int i = 0; i < k; ++i) {
-    const float wi = w[(size_t)t * k + i];
-    const float4_t* o = reinterpret_cast<const float4_t*>(out + ((size_t)t * k + i) * H + c * 8);
-    float4_t a = o[0], b = o[1];
-    acc[0] = fmaf(wi, a.x, acc[0]); acc[1] = fmaf(wi, a.y, acc[1]);
-    acc[2] = fmaf(wi, a.z, acc[2]); acc[3] = fmaf(wi, a.w, acc[3]);
-    acc[4] = fmaf(wi, b.x, acc[4]); acc[5] = fmaf(wi, b.y, acc[5]);
-    acc[6] = fmaf(wi, b.z, acc[6]); acc[7] = fmaf(wi, b.w, acc[7]);
+  // slots in batches of CB: every load of a batch in flight before its FMAs
+  // (slots past k re-read slot k-1 and are not used); FMAs in slot order
+  constexpr int CB = 5;
+  for (int i0 = 0; i0 < k; i0 += CB) {
+    float4_t a[CB], b[CB];
+    float wi[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int i = min(i0 + u, k - 1);
+      wi[u] = w[(size_t)t * k + i];
+      const float4_t* o = reinterpret_cast<const float4_t*>(out + ((size_t)t * k + i) * H + c * 8);
+      a[u] = o[0];
+      b[u] = o[1];
+    }
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      if (i0 + u < k) {
+        acc[0] = fmaf(wi[u], a[u].x, acc[0]); acc[1] = fmaf(wi[u], a[u].y, acc[1]);
+        acc[2] = fmaf(wi[u], a[u].z, acc[2]); acc[3] = fmaf(wi[u], a[u].w, acc[3]);
+        acc[4] = fmaf(wi[u], b[u].x, acc[4]); acc[5] = fmaf(wi[u], b[u].y, acc[5]);
+        acc[6] = fmaf(wi[u], b[u].z, acc[6]); acc[7] = fmaf(wi[u], b[u].w, acc[7]);
+      }
+    }
   }
   if (residual) {
     u32x4 r = *reinterpret_cast<const u32x4*>(residual + (size_t)t * H + c * 8);
