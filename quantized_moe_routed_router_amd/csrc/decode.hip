@@ -304,9 +304,12 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
     ids = a.ids;
   }
   const PairIds P = load_pair_ids(ids, npairs, lane);
+  // one token: its x^ is loaded before the weights and staged while they
+  // are in flight; several tokens: only the tokens routed to this block's
+  // expert are staged, after the weight loads are issued
   const int xtot = a.T * (a.H / 16);
   ActRegs xr;
-  if (!TOPK) act_load(xr, a.x_codes, a.x_scales, xtot, tid, blockDim.x);
+  if (!TOPK && MAXP == 1) act_load(xr, a.x_codes, a.x_scales, xtot, tid, blockDim.x);
   const int e = pair_expert(P, p);
   uint64_t pm[PID_CH];
   pair_masks(P, npairs, e, lane, pm);
@@ -327,12 +330,21 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
   uint32_t sw[CPW];
   load_chunks<CPW>(tile, a.H, c0, nc, lane, cw, sw);          // all weight loads in flight
   if (by_token) {
-    if (!TOPK) {
+    if (!TOPK && MAXP == 1) {
       act_store(xr, a.x_codes, a.x_scales, xtot, xs, tid, blockDim.x);
-    } else if (min(a.T, nw) >= nw) {                            // every wave ranked: stage now
-      for (int t = 0; t < a.T; ++t)
-        stage_act_f16(a.x_codes + (size_t)t * (a.H / 2), a.x_scales + (size_t)t * (a.H / 16), a.H,
-                      xs + (size_t)t * (a.H / 2), tid, blockDim.x);
+    } else if (MAXP > 1 || min(a.T, nw) >= nw) {
+      // stage now, only the tokens routed to this expert (each token at
+      // most once: its k experts are distinct)
+#pragma unroll
+      for (int i = 0; i < PID_CH; ++i) {
+        uint64_t mm = pm[i];
+        while (mm) {
+          const int t = (64 * i + __ffsll((unsigned long long)mm) - 1) / a.k;
+          mm &= mm - 1;
+          stage_act_f16(a.x_codes + (size_t)t * (a.H / 2), a.x_scales + (size_t)t * (a.H / 16), a.H,
+                        xs + (size_t)t * (a.H / 2), tid, blockDim.x);
+        }
+      }
     }
   }
   int qstart = p;
@@ -690,7 +702,16 @@ static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logit
   const int KS = dec_ksplit(a.H);
   const int nw1 = dec_waves(a.H / 32 / KS);
   const size_t lds1 = (size_t)MAXP * a.H * 2 + (size_t)nw1 * MAXP * 64 * 4;
-  gate_up_decode_kernel<MAXP, DEC_CPW, FUSED><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out);
+  // The fused layer ranks the logits inside every gate/up block when there
+  // is one token (no extra launch on the critical path); with several
+  // tokens every block would rank all of them, so one wave per token ranks
+  // them once in the top-k kernel first.
+  if constexpr (FUSED && MAXP > 1) {
+    (void)launch_topk(logits, a.T, a.E, a.k, ids_out, w_out, s);
+    gate_up_decode_kernel<MAXP, DEC_CPW, false><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out);
+  } else {
+    gate_up_decode_kernel<MAXP, DEC_CPW, FUSED><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out);
+  }
   h_quant_decode_kernel<<<npairs, 64 * ((a.I / 16 + 63) / 64), 0, s>>>(a, ws);
   if (slice_fits(npairs, a.H, a.I)) {
     const size_t lds = slice_lds_bytes(npairs, a.I);

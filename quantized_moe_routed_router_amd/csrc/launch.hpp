@@ -20,6 +20,7 @@ hipError_t launch_pack_codebook(int H, int I, int e0, int n, const uint16_t* gcb
                                 const uint8_t* gidx, const uint16_t* ucb, const uint8_t* uidx,
                                 uint8_t* gate_up, hipStream_t s);
 
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
 hipError_t launch_router(const uint16_t* x, const float* W_r, const float* bias, int T, int E,
                          int H, int k, int32_t* ids, float* w, float* logits, hipStream_t s);
 

@@ -204,6 +204,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   }
 }
 
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, ids, w);
+  return hipGetLastError();
+}
+
 hipError_t launch_router(const uint16_t* x, const float* W_r, const float* bias, int T, int E,
                          int H, int k, int32_t* ids, float* w, float* logits, hipStream_t s) {
   if (T == 0) return hipSuccess;
