@@ -36,21 +36,36 @@ __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restri
   for (int e = threadIdx.x; e <= E; e += 256) chunk_counts[(size_t)blockIdx.x * (E + 1) + e] = hist[e];
 }
 
-// One thread per bin: running prefix over chunks.
+// One wave per bin: lane l owns a contiguous run of chunks; per-lane sums,
+// an exclusive scan of them across the wave, then each lane writes the
+// running prefix over its chunks (chunk order, so the sort stays stable).
 __global__ __launch_bounds__(256) void perm_chunk_scan_kernel(const int32_t* __restrict__ chunk_counts,
                                                               int nchunks, int E,
                                                               int32_t* __restrict__ chunk_base,
                                                               int32_t* __restrict__ totals) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e > E) return;
-  int run = 0;
-  for (int c = 0; c < nchunks; ++c) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e > E) return;                                    // wave-uniform; no block barrier below
+  const int per = (nchunks + 63) / 64;
+  const int c0 = min(lane * per, nchunks), c1 = min(c0 + per, nchunks);
+  int mine = 0;
+#pragma unroll 8
+  for (int c = c0; c < c1; ++c) mine += chunk_counts[(size_t)c * (E + 1) + e];
+  int incl = mine;                                      // inclusive scan over lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  int run = incl - mine;
+#pragma unroll 8
+  for (int c = c0; c < c1; ++c) {
     const size_t o = (size_t)c * (E + 1) + e;
     const int v = chunk_counts[o];
     chunk_base[o] = run;
     run += v;
   }
-  totals[e] = run;
+  if (lane == 63) totals[e] = incl;
 }
 
 // Single block: exclusive scan over bins (E+1 <= 1025 values).
@@ -143,9 +158,9 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* coun
   int32_t* bin_start = totals + (E + 1);
   if (nch > 0) {
     perm_count_kernel<<<nch, 256, (E + 1) * sizeof(int), s>>>(ids, N, E, cc);
-    perm_chunk_scan_kernel<<<(E + 1 + 255) / 256, 256, 0, s>>>(cc, nch, E, cb, totals);
+    perm_chunk_scan_kernel<<<(E + 1 + 3) / 4, 256, 0, s>>>(cc, nch, E, cb, totals);
   } else {
-    perm_chunk_scan_kernel<<<(E + 1 + 255) / 256, 256, 0, s>>>(cc, 0, E, cb, totals);
+    perm_chunk_scan_kernel<<<(E + 1 + 3) / 4, 256, 0, s>>>(cc, 0, E, cb, totals);
   }
   perm_offsets_kernel<<<1, 1024, 0, s>>>(totals, E, counts, offsets, bin_start, tile_prefix, BM);
   if (nch > 0)
