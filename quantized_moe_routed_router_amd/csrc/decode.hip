@@ -728,7 +728,7 @@ static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logit
 hipError_t launch_ffn_decode(const FfnArgs& a, void* ws, hipStream_t s) {
   DecodeWs w = carve_decode(ws, a.H, a.I, a.T * a.k, nullptr);
   if (a.T == 1) launch_decode_pair<1, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
-  else launch_decode_pair<8, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
+  else launch_decode_pair<4, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
   return hipGetLastError();
 }
 
@@ -779,7 +779,7 @@ hipError_t launch_layer_decode(const LayerArgs& L, void* ws, hipStream_t s) {
   if (L.T == 1)
     launch_decode_pair<1, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s);
   else
-    launch_decode_pair<8, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s);
+    launch_decode_pair<4, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s);
   return hipGetLastError();
 }
 
