@@ -113,6 +113,31 @@ __device__ __forceinline__ uint32_t quantize_block16(const float (&v)[16], float
   return sb;
 }
 
+// The same quantizer for a quarter of a 16-element block held by one lane
+// (four lanes per block): ab is the whole block's max |v|, so the block
+// scale is the one quantize_block16 computes; returns it and writes the
+// quarter's four codes (element 2j in the low nibble) to bits16.
+__device__ __forceinline__ uint32_t quantize_quarter4(const float (&v)[4], float ab, float ts,
+                                                      uint32_t& bits16) {
+#pragma clang fp contract(off)
+  uint32_t sb = 0;
+  if (ts != 0.0f) {
+    float six_ts = 6.0f * ts;
+    sb = e4m3_rne_satfinite(__fdiv_rn(ab, six_ts));
+  }
+  float d = e4m3_to_f32(sb) * ts;
+  bits16 = 0;
+  if (d != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float q = __fdiv_rn(v[i], d);
+      uint32_t c = e2m1_rne_sat(fabsf(q)) | ((__float_as_uint(v[i]) >> 31) << 3);
+      bits16 |= c << (4 * i);
+    }
+  }
+  return sb;
+}
+
 __device__ __forceinline__ float tensor_scale_from_amax(float amax) {
   return amax == 0.0f ? 0.0f : __fdiv_rn(amax, TS_DIVISOR);
 }

@@ -390,67 +390,65 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
 // ---------------------------------------------------------------- h^
 // h = SiLU(g) * u of every pair from the gate/up partials (summed over the
 // K-splits in split order), then NVFP4 with the row's own tensor scale.
-// Block = one pair, thread = one 16-element block of its row.  h^ is written
-// once here and read by every down block, so the down step does no
-// quantization arithmetic of its own.
-__global__ __launch_bounds__(256) void h_quant_decode_kernel(FfnArgs a, DecodeWs ws) {
-  __shared__ float wmax[4];
+// Block = one pair; four lanes per 16-element block (four elements each):
+// the block max is a quad reduction, the row amax a wave max plus a fixed
+// pass over the waves' maxima in LDS, and each lane quantizes its quarter
+// (the same steps as the whole-block quantizer).  h^ is written once here
+// and read by every down block.
+__global__ __launch_bounds__(1024) void h_quant_decode_kernel(FfnArgs a, DecodeWs ws) {
+  __shared__ float wmax[16];
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nw = blockDim.x >> 6;
-  const int nblk = a.I / 16;
+  const int nq = a.I / 4;                                  // quarters in the row
   const int KS = dec_ksplit(a.H);
   const size_t part_stride = (size_t)a.T * a.k * 2 * a.I;
-  const int b = tid < nblk ? tid : nblk - 1;               // extra threads redo the last block
-  float g[16], u[16];
-  for (int sp0 = 0; sp0 < KS; sp0 += 2) {                  // two splits' loads in flight at once
-    float4_t g4[2][4], u4[2][4];
+  const int qi = tid < nq ? tid : nq - 1;                   // extra lanes redo the last quarter
+  float g[4], u[4];
+  for (int sp0 = 0; sp0 < KS; sp0 += 2) {                   // two splits' loads in flight at once
+    float4_t g4[2], u4[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int spc = min(sp0 + s2, KS - 1);
-      const float4_t* gp = reinterpret_cast<const float4_t*>(ws.gu + (size_t)spc * part_stride + (size_t)q * 2 * a.I + b * 16);
-      const float4_t* upp = gp + a.I / 4;
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) { g4[s2][r4] = gp[r4]; u4[s2][r4] = upp[r4]; }
+      const float* gp = ws.gu + (size_t)spc * part_stride + (size_t)q * 2 * a.I + qi * 4;
+      g4[s2] = *reinterpret_cast<const float4_t*>(gp);
+      u4[s2] = *reinterpret_cast<const float4_t*>(gp + a.I);
     }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       if (sp0 + s2 < KS) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int i = 4 * r4 + c;
-            g[i] = (sp0 + s2 == 0) ? g4[s2][r4][c] : g[i] + g4[s2][r4][c];
-            u[i] = (sp0 + s2 == 0) ? u4[s2][r4][c] : u[i] + u4[s2][r4][c];
-          }
+        for (int c = 0; c < 4; ++c) {
+          g[c] = (sp0 + s2 == 0) ? g4[s2][c] : g[c] + g4[s2][c];
+          u[c] = (sp0 + s2 == 0) ? u4[s2][c] : u[c] + u4[s2][c];
         }
       }
     }
   }
-  float hv[16];
-  float bmax = 0.0f;
+  float hv[4];
+  float m4 = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    hv[i] = silu_mul(g[i], u[i]);
-    bmax = fmaxf(bmax, fabsf(hv[i]));
+  for (int c = 0; c < 4; ++c) {
+    hv[c] = silu_mul(g[c], u[c]);
+    m4 = fmaxf(m4, fabsf(hv[c]));
   }
-  const float m = dpp_wave_max(tid < nblk ? bmax : 0.0f);
+  // block max over the quad (lanes 4b .. 4b+3 hold block b)
+  float bmax = fmaxf(m4, __int_as_float(dpp_mov<0xB1>(0, __float_as_int(m4))));
+  bmax = fmaxf(bmax, __int_as_float(dpp_mov<0x4E>(0, __float_as_int(bmax))));
+  const float m = dpp_wave_max(tid < nq ? m4 : 0.0f);
   if (lane == 0) wmax[wv] = m;
   __syncthreads();
   float amax = wmax[0];
   for (int w = 1; w < nw; ++w) amax = fmaxf(amax, wmax[w]);
   const float ts = tensor_scale_from_amax(amax);
-  if (tid < nblk) {
-    uint32_t pk[2];
-    const uint32_t sb = quantize_block16(hv, ts, pk);
-    *reinterpret_cast<u32x2*>(ws.hc + (size_t)q * (a.I / 2) + b * 8) = u32x2{pk[0], pk[1]};
-    ws.hsc[(size_t)q * nblk + b] = (uint8_t)sb;
-    if (a.dbg_h) {
-#pragma unroll
-      for (int c = 0; c < 16; ++c) a.dbg_h[(size_t)q * a.I + b * 16 + c] = hv[c];
-    }
-    if (a.dbg_h_codes) *reinterpret_cast<u32x2*>(a.dbg_h_codes + (size_t)q * (a.I / 2) + b * 8) = u32x2{pk[0], pk[1]};
-    if (a.dbg_h_scales) a.dbg_h_scales[(size_t)q * nblk + b] = (uint8_t)sb;
+  if (tid < nq) {
+    uint32_t bits;
+    const uint32_t sb = quantize_quarter4(hv, bmax, ts, bits);
+    const int b = qi >> 2, part = qi & 3;
+    *reinterpret_cast<uint16_t*>(ws.hc + (size_t)q * (a.I / 2) + qi * 2) = (uint16_t)bits;
+    if (part == 0) ws.hsc[(size_t)q * (a.I / 16) + b] = (uint8_t)sb;
+    if (a.dbg_h) *reinterpret_cast<float4_t*>(a.dbg_h + (size_t)q * a.I + qi * 4) = float4_t{hv[0], hv[1], hv[2], hv[3]};
+    if (a.dbg_h_codes) *reinterpret_cast<uint16_t*>(a.dbg_h_codes + (size_t)q * (a.I / 2) + qi * 2) = (uint16_t)bits;
+    if (a.dbg_h_scales && part == 0) a.dbg_h_scales[(size_t)q * (a.I / 16) + b] = (uint8_t)sb;
   }
   if (tid == 0) {
     ws.hts[q] = ts;
@@ -712,7 +710,7 @@ static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logit
   } else {
     gate_up_decode_kernel<MAXP, DEC_CPW, FUSED><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out);
   }
-  h_quant_decode_kernel<<<npairs, 64 * ((a.I / 16 + 63) / 64), 0, s>>>(a, ws);
+  h_quant_decode_kernel<<<npairs, 64 * ((a.I / 4 + 63) / 64), 0, s>>>(a, ws);
   if (slice_fits(npairs, a.H, a.I)) {
     const size_t lds = slice_lds_bytes(npairs, a.I);
     if (FUSED) down_slice_kernel<true><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y);
