@@ -125,13 +125,17 @@ __device__ __forceinline__ float chunk_dot(const half2_t (&w0)[8], const half2_t
   *reinterpret_cast<u32x4*>(&x[4]) = a1;
   *reinterpret_cast<u32x4*>(&x[8]) = a2;
   *reinterpret_cast<u32x4*>(&x[12]) = a3;
-  float b0 = 0.0f, b1 = 0.0f;
+  // four independent dot2 chains per chunk (short dependency chains)
+  float b0 = 0.0f, b1 = 0.0f, b2 = 0.0f, b3 = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) b0 = dot2(w0[j], x[j], b0);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) b1 = dot2(w1[j], x[8 + j], b1);
-  acc = fmaf(s0, b0, acc);
-  return fmaf(s1, b1, acc);
+  for (int j = 0; j < 4; ++j) {
+    b0 = dot2(w0[j], x[j], b0);
+    b1 = dot2(w0[4 + j], x[4 + j], b1);
+    b2 = dot2(w1[j], x[8 + j], b2);
+    b3 = dot2(w1[4 + j], x[12 + j], b3);
+  }
+  acc = fmaf(s0, b0 + b1, acc);
+  return fmaf(s1, b2 + b3, acc);
 }
 
 // The CPW chunks c0 .. c0+nc-1 of a lane's row.  Straight-line: slots past
@@ -168,6 +172,26 @@ __device__ __forceinline__ void dot_chunks(const u32x4 (&cw)[CPW], const uint32_
         if (q < n) acc[q] = chunk_dot(w0, w1, s0, s1, act + (size_t)slot[q] * act_stride + (c0 + i) * 16, acc[q]);
     }
   }
+}
+
+// One activation row, no branches: chunks past nc take scale 0 (their loads
+// were clamped to valid chunks), so every wait on a chunk's load is the
+// in-order wait for that chunk alone.
+template <int CPW>
+__device__ __forceinline__ float dot_chunks_row(const u32x4 (&cw)[CPW], const uint32_t (&sw)[CPW], int c0,
+                                                int nc, int clast, const half2_t* __restrict__ act) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    half2_t w0[8], w1[8];
+    cvt16(cw[i].x, cw[i].y, w0);
+    cvt16(cw[i].z, cw[i].w, w1);
+    const bool ok = i < nc;
+    const float s0 = ok ? e4m3_to_f32(sw[i] & 0xFF) : 0.0f;
+    const float s1 = ok ? e4m3_to_f32(sw[i] >> 8) : 0.0f;
+    acc = chunk_dot(w0, w1, s0, s1, act + (size_t)min(c0 + i, clast) * 16, acc);
+  }
+  return acc;
 }
 
 // All pair ids of the call in registers (lane l holds pair l + 64 i), so the
@@ -245,13 +269,20 @@ __host__ __device__ inline int dec_ksplit(int H) {
   return 1;
 }
 
+// One token: a single split when the row fits one block's waves (then the
+// block holds whole gate and up rows and can form h itself).
+__host__ __device__ inline int dec_ks(int H, int T) {
+  return (T == 1 && H / 32 <= DEC_MAX_WAVES * DEC_CPW) ? 1 : dec_ksplit(H);
+}
+
 __host__ __device__ inline int dec_waves(int nchunk_block) {
   int nw = (nchunk_block + DEC_CPW - 1) / DEC_CPW;
   return nw < 1 ? 1 : (nw > DEC_MAX_WAVES ? DEC_MAX_WAVES : nw);
 }
 
 struct DecodeWs {
-  float* gu;          // [KS][T*k][2][I] gate/up partial dot sums, tensor scales applied
+  float* gu;          // [KS][T*k][2][I] gate/up partial dot sums, tensor scales applied;
+                      // h mode: h [T*k][I], then max |h| per 32-row tile [T*k][I/32]
   uint8_t* hc;        // [T*k][I/2]  h^ codes
   uint8_t* hsc;       // [T*k][I/16] h^ block scales (E4M3)
   float* hts;         // [T*k]       h^ tensor scales
@@ -263,7 +294,7 @@ struct DecodeWs {
 template <int MAXP, int CPW, bool TOPK>
 __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
     FfnArgs a, DecodeWs ws, const float* __restrict__ logits, int32_t* __restrict__ ids_out,
-    float* __restrict__ w_out) {
+    float* __restrict__ w_out, int hmode) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int nw = blockDim.x >> 6;
   half2_t* xs = reinterpret_cast<half2_t*>(smem);                         // [MAXP][H/2]
@@ -317,8 +348,18 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
   const size_t part_stride = (size_t)npairs * 2 * a.I;
   float* gu = ws.gu + (size_t)split * part_stride;
   if ((unsigned)e >= (unsigned)a.E) {                         // not an expert: partials 0
-    for (int q = p; q < npairs; ++q)
-      if (((pm[q >> 6] >> (q & 63)) & 1) && tid < 64) gu[(size_t)q * 2 * a.I + (tid >> 5) * a.I + 32 * j + (tid & 31)] = 0.0f;
+    for (int q = p; q < npairs; ++q) {
+      if (!((pm[q >> 6] >> (q & 63)) & 1) || tid >= 64) continue;
+      if (hmode) {                                            // h 0, tile max 0
+        if (tid < 32) {
+          ws.gu[(size_t)q * a.I + 32 * j + tid] = 0.0f;
+          if (a.dbg_h) a.dbg_h[(size_t)q * a.I + 32 * j + tid] = 0.0f;
+        }
+        if (tid == 0) ws.gu[(size_t)npairs * a.I + (size_t)q * (a.I / 32) + j] = 0.0f;
+      } else {
+        gu[(size_t)q * 2 * a.I + (tid >> 5) * a.I + 32 * j + (tid & 31)] = 0.0f;
+      }
+    }
     return;
   }
   const uint8_t* tile = a.gate_up + (size_t)e * gate_up_expert_bytes(a.H, a.I) + (size_t)j * tile_bytes(a.H);
@@ -347,43 +388,93 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
       }
     }
   }
-  int qstart = p;
-  while (true) {
-    int qnext;
-    const int n = masked_pairs<MAXP>(pm, npairs, qstart, list, &qnext, tid);
-    __syncthreads();
-    if (!by_token) {
-      for (int i = 0; i < n; ++i) {
-        const int t = list[i] / a.k;
-        stage_act_f16(a.x_codes + (size_t)t * (a.H / 2), a.x_scales + (size_t)t * (a.H / 16), a.H,
-                      xs + (size_t)i * (a.H / 2), tid, blockDim.x);
-      }
-      __syncthreads();
-    }
-    int slot[MAXP];
-#pragma unroll
-    for (int i = 0; i < MAXP; ++i) slot[i] = (i < n) ? (by_token ? list[i] / a.k : i) : 0;
-    float acc[MAXP];
-#pragma unroll
-    for (int i = 0; i < MAXP; ++i) acc[i] = 0.0f;
-    dot_chunks<CPW, MAXP>(cw, sw, c0, nc, n, xs, a.H / 2, slot, acc);
-#pragma unroll
-    for (int i = 0; i < MAXP; ++i) red[(wv * MAXP + i) * 64 + lane] = acc[i];
+  if constexpr (MAXP == 1) {
+    // one token (MAXP 1 is the one-token launch): every pair on this
+    // expert has the same x, so the dots run once, straight-line, and the
+    // partial goes to each such pair; tensor scales load per lane beside
+    // the weights
+    const float tsw = (lane < 32 ? a.ts_gate : a.ts_up)[e];
+    const float xts = a.x_ts[lane < a.T ? lane : a.T - 1];
+    __syncthreads();                                           // x^ staged
+    const float acc = dot_chunks_row<CPW>(cw, sw, c0, nc, a.H / 32 - 1, xs);
+    red[wv * 64 + lane] = acc;
     __syncthreads();
     if (wv == 0) {
-      for (int i = 0; i < n; ++i) {
-        float v = 0.0f;
-        for (int w = 0; w < nw; ++w) v += red[(w * MAXP + i) * 64 + lane];
-        // lane < 32: gate row 32j + lane; lane >= 32: up row 32j + lane - 32;
-        // the partial carries its tensor scales (x row, weight matrix)
-        const int q = list[i];
-        const float sc = a.x_ts[q / a.k] * (lane < 32 ? a.ts_gate[e] : a.ts_up[e]);
-        gu[(size_t)q * 2 * a.I + (lane >> 5) * a.I + 32 * j + (lane & 31)] = v * sc;
+      float v = 0.0f;
+      for (int w = 0; w < nw; ++w) v += red[w * 64 + lane];
+      v *= __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(xts))) * tsw;
+      if (hmode) {
+        // h mode (one split): this block holds whole gate rows (lanes 0-31)
+        // and up rows (lanes 32-63) 32j..32j+31, so it forms h = SiLU(g) u
+        // and the tile's max |h| for the down step's quantizer
+        const float u = __shfl_xor(v, 32, 64);
+        const float h = silu_mul(v, u);
+        const float hm = dpp_wave_max(lane < 32 ? fabsf(h) : 0.0f);
+        float* hmax = ws.gu + (size_t)npairs * a.I;
+#pragma unroll
+        for (int i = 0; i < PID_CH; ++i) {
+          uint64_t mm = pm[i];
+          while (mm) {
+            const int q = 64 * i + __ffsll((unsigned long long)mm) - 1;
+            mm &= mm - 1;
+            if (lane < 32) {
+              ws.gu[(size_t)q * a.I + 32 * j + lane] = h;
+              if (a.dbg_h) a.dbg_h[(size_t)q * a.I + 32 * j + lane] = h;
+            }
+            if (lane == 0) hmax[(size_t)q * (a.I / 32) + j] = hm;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < PID_CH; ++i) {
+          uint64_t mm = pm[i];
+          while (mm) {
+            const int q = 64 * i + __ffsll((unsigned long long)mm) - 1;
+            mm &= mm - 1;
+            gu[(size_t)q * 2 * a.I + (lane >> 5) * a.I + 32 * j + (lane & 31)] = v;
+          }
+        }
       }
     }
-    if (qnext >= npairs) break;
-    qstart = qnext;
-    __syncthreads();
+  } else {
+    int qstart = p;
+    while (true) {
+      int qnext;
+      const int n = masked_pairs<MAXP>(pm, npairs, qstart, list, &qnext, tid);
+      __syncthreads();
+      if (!by_token) {
+        for (int i = 0; i < n; ++i) {
+          const int t = list[i] / a.k;
+          stage_act_f16(a.x_codes + (size_t)t * (a.H / 2), a.x_scales + (size_t)t * (a.H / 16), a.H,
+                        xs + (size_t)i * (a.H / 2), tid, blockDim.x);
+        }
+        __syncthreads();
+      }
+      int slot[MAXP];
+  #pragma unroll
+      for (int i = 0; i < MAXP; ++i) slot[i] = (i < n) ? (by_token ? list[i] / a.k : i) : 0;
+      float acc[MAXP];
+  #pragma unroll
+      for (int i = 0; i < MAXP; ++i) acc[i] = 0.0f;
+      dot_chunks<CPW, MAXP>(cw, sw, c0, nc, n, xs, a.H / 2, slot, acc);
+  #pragma unroll
+      for (int i = 0; i < MAXP; ++i) red[(wv * MAXP + i) * 64 + lane] = acc[i];
+      __syncthreads();
+      if (wv == 0) {
+        for (int i = 0; i < n; ++i) {
+          float v = 0.0f;
+          for (int w = 0; w < nw; ++w) v += red[(w * MAXP + i) * 64 + lane];
+          // lane < 32: gate row 32j + lane; lane >= 32: up row 32j + lane - 32;
+          // the partial carries its tensor scales (x row, weight matrix)
+          const int q = list[i];
+          const float sc = a.x_ts[q / a.k] * (lane < 32 ? a.ts_gate[e] : a.ts_up[e]);
+          gu[(size_t)q * 2 * a.I + (lane >> 5) * a.I + 32 * j + (lane & 31)] = v * sc;
+        }
+      }
+      if (qnext >= npairs) break;
+      qstart = qnext;
+      __syncthreads();
+    }
   }
 }
 
@@ -400,7 +491,7 @@ __global__ __launch_bounds__(1024) void h_quant_decode_kernel(FfnArgs a, DecodeW
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nw = blockDim.x >> 6;
   const int nq = a.I / 4;                                  // quarters in the row
-  const int KS = dec_ksplit(a.H);
+  const int KS = dec_ks(a.H, a.T);
   const size_t part_stride = (size_t)a.T * a.k * 2 * a.I;
   const int qi = tid < nq ? tid : nq - 1;                   // extra lanes redo the last quarter
   float g[4], u[4];
@@ -537,7 +628,14 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(FfnArgs
 constexpr int SL_MAXP = 16;              // pairs (= waves) per block
 constexpr int SL_CPQ = 5;                // chunks per quarter held in registers (I <= 640)
 
-template <bool COMBINE>
+constexpr int SL_HQR = 3;                // h quarters per lane in h mode (I <= 768)
+
+// HQ (h mode, one token): wave q quantizes pair q's h row itself, from h
+// and the 32-row tile maxima the gate/up step wrote (the row amax is their
+// max), with the h^ quantizer's steps: four lanes per 16-element block
+// (quad max), each lane coding its quarter.  Every block repeats this for
+// all pairs; no separate h^ pass.
+template <bool COMBINE, bool HQ>
 __global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, DecodeWs ws,
                                                                   const float* __restrict__ w_comb,
                                                                   const uint16_t* __restrict__ residual,
@@ -557,7 +655,7 @@ __global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, Dec
   const int nitems = npairs * nblk;
   // ---- loads that do not depend on the routing, ids first
   const int qid = a.ids[lane < npairs ? lane : npairs - 1];
-  const float htl = ws.hts[lane < npairs ? lane : npairs - 1];
+  const float htl = HQ ? 0.0f : ws.hts[lane < npairs ? lane : npairs - 1];
   float wc = 0.0f;
   uint16_t res = 0;
   if (COMBINE) {
@@ -569,8 +667,22 @@ __global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, Dec
   }
   const int item = tid < nitems ? tid : nitems - 1;
   const int jq = item / nblk, jb = item % nblk;
-  const u32x2 hcw = *reinterpret_cast<const u32x2*>(ws.hc + (size_t)jq * (a.I / 2) + jb * 8);
-  const uint32_t hsw = ws.hsc[(size_t)jq * nblk + jb];
+  u32x2 hcw = {0u, 0u};
+  uint32_t hsw = 0;
+  float4_t hq[HQ ? SL_HQR : 1];
+  float hmx = 0.0f;
+  const int nqr = a.I / 4, ntile = a.I / 32;
+  if (!HQ) {
+    hcw = *reinterpret_cast<const u32x2*>(ws.hc + (size_t)jq * (a.I / 2) + jb * 8);
+    hsw = ws.hsc[(size_t)jq * nblk + jb];
+  } else {
+    const float* hrow = ws.gu + (size_t)q * a.I;
+#pragma unroll
+    for (int m = 0; m < SL_HQR; ++m)
+      hq[m] = *reinterpret_cast<const float4_t*>(hrow + (size_t)min(lane + 64 * m, nqr - 1) * 4);
+    hmx = ws.gu[(size_t)npairs * a.I + (size_t)q * ntile + min(lane, ntile - 1)];
+  }
+  __builtin_amdgcn_sched_barrier(0);        // these loads stay ahead of the weight loads
   // ---- this pair's expert and its weight loads
   const int e = __builtin_amdgcn_readlane(qid, q);
   const bool valid = (unsigned)e < (unsigned)a.E;
@@ -583,38 +695,68 @@ __global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, Dec
     cw[m] = *reinterpret_cast<const u32x4*>(tile + (size_t)c * 1024 + lit * 16);
     sw[m] = *reinterpret_cast<const uint16_t*>(tile + tile_scale_offset(a.I) + (size_t)(c >> 2) * 512 + lit * 8 + (c & 3) * 2);
   }
-  const float tsd = a.ts_down[valid ? e : 0];
+  // this pair's tensor scale as a per-lane load (lane l: pair l's expert)
+  const float tsd_l = a.ts_down[(unsigned)qid < (unsigned)a.E ? qid : 0];
   __builtin_amdgcn_sched_barrier(0);        // keep the weight loads ahead of the staging
 
   // ---- h^ into LDS as f16 A*s
-  if (tid < nitems) {
-    const _Float16 sc = (_Float16)e4m3_to_f32(hsw);
-    const half2_t s2 = {sc, sc};
-    half2_t wq[8];
-    cvt16(hcw.x, hcw.y, wq);
-    half2_t* d = hs + (size_t)jq * (a.I / 2) + jb * 8;
+  if (!HQ) {
+    if (tid < nitems) {
+      const _Float16 sc = (_Float16)e4m3_to_f32(hsw);
+      const half2_t s2 = {sc, sc};
+      half2_t wq[8];
+      cvt16(hcw.x, hcw.y, wq);
+      half2_t* d = hs + (size_t)jq * (a.I / 2) + jb * 8;
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) d[rr] = wq[rr] * s2;
+      for (int rr = 0; rr < 8; ++rr) d[rr] = wq[rr] * s2;
+    }
+    if (tid < npairs) hts[tid] = htl;
+  } else {
+    const float amax = dpp_wave_max(lane < ntile ? hmx : 0.0f);
+    const float ts = tensor_scale_from_amax(amax);
+    const bool dbg = blockIdx.x == 0;
+#pragma unroll
+    for (int m = 0; m < SL_HQR; ++m) {
+      const int qi = lane + 64 * m;
+      const float v[4] = {hq[m][0], hq[m][1], hq[m][2], hq[m][3]};
+      const float m4 = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+      float b4 = fmaxf(m4, __int_as_float(dpp_mov<0xB1>(0, __float_as_int(m4))));
+      b4 = fmaxf(b4, __int_as_float(dpp_mov<0x4E>(0, __float_as_int(b4))));
+      if (qi < nqr) {
+        uint32_t bits;
+        const uint32_t sb = quantize_quarter4(v, b4, ts, bits);
+        const _Float16 sc = (_Float16)e4m3_to_f32(sb);
+        const half2_t s2 = {sc, sc};
+        half2_t* d = hs + (size_t)q * (a.I / 2) + qi * 2;
+        d[0] = fp4x2_to_f16x2<0>(bits) * s2;
+        d[1] = fp4x2_to_f16x2<1>(bits) * s2;
+        if (dbg && a.dbg_h_codes)
+          *reinterpret_cast<uint16_t*>(a.dbg_h_codes + (size_t)q * (a.I / 2) + qi * 2) = (uint16_t)bits;
+        if (dbg && a.dbg_h_scales && (qi & 3) == 0) a.dbg_h_scales[(size_t)q * nblk + (qi >> 2)] = (uint8_t)sb;
+      }
+    }
+    if (lane == 0) {
+      hts[q] = ts;
+      if (dbg && a.dbg_h_ts) a.dbg_h_ts[q] = ts;
+    }
   }
-  if (tid < npairs) {
-    hts[tid] = htl;
-    if (COMBINE) wcs[tid] = wc;
-  }
+  if (COMBINE && tid < npairs) wcs[tid] = wc;
   __syncthreads();
 
   // ---- down dot of pair q over this block's 16 rows
+  // no branches: chunks past the row take scale 0 (their loads were clamped)
   float acc = 0.0f;
 #pragma unroll
   for (int m = 0; m < SL_CPQ; ++m) {
     const int c = qt + 4 * m;
-    if (c < nchunk) {
-      half2_t w0[8], w1[8];
-      cvt16(cw[m].x, cw[m].y, w0);
-      cvt16(cw[m].z, cw[m].w, w1);
-      acc = chunk_dot(w0, w1, e4m3_to_f32(sw[m] & 0xFF), e4m3_to_f32(sw[m] >> 8),
-                      hs + (size_t)q * (a.I / 2) + c * 16, acc);
-    }
+    const bool ok = c < nchunk;
+    half2_t w0[8], w1[8];
+    cvt16(cw[m].x, cw[m].y, w0);
+    cvt16(cw[m].z, cw[m].w, w1);
+    acc = chunk_dot(w0, w1, ok ? e4m3_to_f32(sw[m] & 0xFF) : 0.0f, ok ? e4m3_to_f32(sw[m] >> 8) : 0.0f,
+                    hs + (size_t)q * (a.I / 2) + min(c, nchunk - 1) * 16, acc);
   }
+  const float tsd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tsd_l), q));
   acc += __shfl_xor(acc, 16, 64);
   acc += __shfl_xor(acc, 32, 64);
   if (lane < 16) {
@@ -692,13 +834,19 @@ static bool slice_fits(int npairs, int H, int I) {
   return npairs <= SL_MAXP && I <= 32 * 4 * SL_CPQ && I / 16 <= 64 && H % 16 == 0 &&
          slice_lds_bytes(npairs, I) <= 56 * 1024;
 }
+// h mode: one token, one gate/up split, the slice kernel quantizing h itself
+static bool decode_h_mode(int T, int npairs, int H, int I) {
+  return T == 1 && dec_ks(H, T) == 1 && slice_fits(npairs, H, I) && I / 4 <= 64 * SL_HQR &&
+         I / 32 <= 64;
+}
 
 template <int MAXP, bool FUSED>
 static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logits, int32_t* ids_out,
                                float* w_out, const uint16_t* residual, uint16_t* y, hipStream_t s) {
   const int npairs = a.T * a.k;
-  const int KS = dec_ksplit(a.H);
+  const int KS = dec_ks(a.H, a.T);
   const int nw1 = dec_waves(a.H / 32 / KS);
+  const int hm = decode_h_mode(a.T, npairs, a.H, a.I) ? 1 : 0;
   const size_t lds1 = (size_t)MAXP * a.H * 2 + (size_t)nw1 * MAXP * 64 * 4;
   // The fused layer ranks the logits inside every gate/up block when there
   // is one token (no extra launch on the critical path); with several
@@ -706,15 +854,21 @@ static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logit
   // them once in the top-k kernel first.
   if constexpr (FUSED && MAXP > 1) {
     (void)launch_topk(logits, a.T, a.E, a.k, ids_out, w_out, s);
-    gate_up_decode_kernel<MAXP, DEC_CPW, false><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out);
+    gate_up_decode_kernel<MAXP, DEC_CPW, false><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out, hm);
   } else {
-    gate_up_decode_kernel<MAXP, DEC_CPW, FUSED><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out);
+    gate_up_decode_kernel<MAXP, DEC_CPW, FUSED><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out, hm);
+  }
+  if (hm) {
+    const size_t lds = slice_lds_bytes(npairs, a.I);
+    if (FUSED) down_slice_kernel<true, true><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y);
+    else down_slice_kernel<false, true><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
+    return;
   }
   h_quant_decode_kernel<<<npairs, 64 * ((a.I / 4 + 63) / 64), 0, s>>>(a, ws);
   if (slice_fits(npairs, a.H, a.I)) {
     const size_t lds = slice_lds_bytes(npairs, a.I);
-    if (FUSED) down_slice_kernel<true><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y);
-    else down_slice_kernel<false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
+    if (FUSED) down_slice_kernel<true, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y);
+    else down_slice_kernel<false, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
   } else {
     const int nw2 = dec_waves(a.I / 32);
     const size_t lds2 = (size_t)MAXP * a.I * 2 + (size_t)nw2 * MAXP * 64 * 4;
