@@ -59,24 +59,46 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return e ? nrm : sub;
 }
 
-// Round s >= 0 to the nearest E4M3 code (ties to even), saturating at 448.
+// Round s >= 0 to the nearest E4M3 code (ties to even), saturating at 448:
+// the hardware OCP FP8 (E4M3FN) conversion with scale 1 rounds exactly so
+// below 464 and returns NaN (0x7F) above, so s is clamped to 448 first (NaN
+// also becomes 448, as it did through the comparison form); the sign bit is
+// dropped so -0 gives code 0.  Checked against the bit-level rounding over
+// every fp32 s >= 0.
+typedef short fp8x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t e4m3_rne_satfinite(float s) {
-  if (!(s < 448.0f)) return 0x7E;                 // also catches +inf
-  if (s < 0x1p-6f) {                              // subnormal grid, quantum 2^-9
-    return (uint32_t)__builtin_rintf(s * 512.0f); // exact scaling; rint = RNE
-  }
-  uint32_t u = __float_as_uint(s);
-  uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);   // RNE at mantissa bit 20
-  uint32_t c = (r >> 20) - (120u << 3);
-  return c > 0x7Eu ? 0x7Eu : c;
+  const fp8x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((fp8x2_t){0, 0}, fminf(s, 448.0f), 0.0f,
+                                                              1.0f, false);
+  return (uint32_t)r[0] & 0x7Fu;
 }
 
-// 3-bit magnitude code of a >= 0 on {0,.5,1,1.5,2,3,4,6}: nearest, ties to
-// the even code, saturating (the interval boundaries are exact in fp32).
-__device__ __forceinline__ uint32_t e2m1_rne_sat(float a) {
-  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-         (uint32_t)(a > 5.0f);
+// Signed E2M1 codes of q0 (low nibble) and q1 into byte SEL of old: the
+// hardware FP4 conversion with scale 1 rounds |q| to nearest even on
+// {0,.5,1,1.5,2,3,4,6}, saturates at 6 and keeps the sign bit (checked over
+// every non-NaN fp32 of both signs).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_into(uint32_t old, float q0, float q1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, q0, q1, 1.0f, SEL);
+}
+
+// fp32 division v / d rounded to nearest even, in the hardware division's
+// own steps (reciprocal, one Newton step, two residual corrections) without
+// its operand scaling and fixup, which leave finite operands unchanged when
+// d lies in [2^-60, 2^60] (checked by div_fast_ok).  y = recip_refined(d)
+// is shared by every quotient with divisor d.  A numerator below 2^-100
+// (where the hardware would scale it) gives a quotient below 2^-40 either
+// way, which every caller rounds to code 0.
+__device__ __forceinline__ bool div_fast_ok(float d) {
+  return d >= 0x1p-60f && d <= 0x1p60f;
+}
+__device__ __forceinline__ float recip_refined(float d) {
+  const float y = __builtin_amdgcn_rcpf(d);
+  return fmaf(fmaf(-d, y, 1.0f), y, y);
+}
+__device__ __forceinline__ float div_refined(float v, float d, float y) {
+  float q = v * y;
+  q = fmaf(fmaf(-d, q, v), y, q);
+  return fmaf(fmaf(-d, q, v), y, q);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -97,17 +119,33 @@ __device__ __forceinline__ uint32_t quantize_block16(const float (&v)[16], float
   for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
   uint32_t sb = 0;
   if (ts != 0.0f) {
-    float six_ts = 6.0f * ts;
-    sb = e4m3_rne_satfinite(__fdiv_rn(ab, six_ts));
+    const float six_ts = 6.0f * ts;
+    float r;
+    if (div_fast_ok(six_ts)) r = div_refined(ab, six_ts, recip_refined(six_ts));
+    else r = __fdiv_rn(ab, six_ts);
+    sb = e4m3_rne_satfinite(r);
   }
   float d = e4m3_to_f32(sb) * ts;
   packed[0] = packed[1] = 0;
   if (d != 0.0f) {
+    float q[16];
+    if (div_fast_ok(d)) {
+      const float y = recip_refined(d);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float q = __fdiv_rn(v[i], d);
-      uint32_t c = e2m1_rne_sat(fabsf(q)) | ((__float_as_uint(v[i]) >> 31) << 3);
-      packed[i >> 3] |= c << (4 * (i & 7));
+      for (int i = 0; i < 16; ++i) q[i] = div_refined(v[i], d, y);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) q[i] = __fdiv_rn(v[i], d);
+    }
+    // the code's sign is v's (also for v = -0, whose quotient may be +0)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = __builtin_copysignf(q[i], v[i]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w = e2m1x2_into<0>(0u, q[8 * h + 0], q[8 * h + 1]);
+      w = e2m1x2_into<1>(w, q[8 * h + 2], q[8 * h + 3]);
+      w = e2m1x2_into<2>(w, q[8 * h + 4], q[8 * h + 5]);
+      packed[h] = e2m1x2_into<3>(w, q[8 * h + 6], q[8 * h + 7]);
     }
   }
   return sb;
@@ -122,18 +160,27 @@ __device__ __forceinline__ uint32_t quantize_quarter4(const float (&v)[4], float
 #pragma clang fp contract(off)
   uint32_t sb = 0;
   if (ts != 0.0f) {
-    float six_ts = 6.0f * ts;
-    sb = e4m3_rne_satfinite(__fdiv_rn(ab, six_ts));
+    const float six_ts = 6.0f * ts;
+    float r;
+    if (div_fast_ok(six_ts)) r = div_refined(ab, six_ts, recip_refined(six_ts));
+    else r = __fdiv_rn(ab, six_ts);
+    sb = e4m3_rne_satfinite(r);
   }
   float d = e4m3_to_f32(sb) * ts;
   bits16 = 0;
   if (d != 0.0f) {
+    float q[4];
+    if (div_fast_ok(d)) {
+      const float y = recip_refined(d);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float q = __fdiv_rn(v[i], d);
-      uint32_t c = e2m1_rne_sat(fabsf(q)) | ((__float_as_uint(v[i]) >> 31) << 3);
-      bits16 |= c << (4 * i);
+      for (int i = 0; i < 4; ++i) q[i] = div_refined(v[i], d, y);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = __fdiv_rn(v[i], d);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = __builtin_copysignf(q[i], v[i]);
+    bits16 = e2m1x2_into<1>(e2m1x2_into<0>(0u, q[0], q[1]), q[2], q[3]);
   }
   return sb;
 }
