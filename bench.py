@@ -405,7 +405,7 @@ def main():
                    "layer_bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "moe_expert_ffn_decode (gate_up_decode_kernel, h_quant_decode_kernel, down_slice_kernel)",
+                     "traffic": traffic, "kernel": "moe_expert_ffn_decode (gate_up_decode_kernel, down_slice_kernel)",
                      "bytes_per_launch": ffn_bytes, "us_per_launch": round(ffn_us, 3)},
         "cpu_baseline": cpu,
         "stack_decode": stack,
