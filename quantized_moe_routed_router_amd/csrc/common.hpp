@@ -333,6 +333,45 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, int E,
 // issued first) and the matching bf16 x; fp32 FMAs, a DPP sum per wave and a
 // fixed-order sum of the four waves through LDS (red: 4*T floats).
 constexpr int RROW_MAXF4 = 4;            // H <= 4096
+
+// TB tokens of one router row: every x load of the batch is issued before
+// the first sum (straight-line, clamped indices; a float4 past the row takes
+// x = 0, which adds exactly 0), then one DPP sum per token.
+template <int TB>
+__device__ __forceinline__ void router_row_tokens(const uint16_t* __restrict__ x,
+                                                  const float4_t (&wv)[RROW_MAXF4], int t0, int T,
+                                                  int H, int tid, float* red) {
+  const int nf4 = H / 4;
+  u32x2 xb[TB][RROW_MAXF4];
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt) {
+    const u32x2* xr = reinterpret_cast<const u32x2*>(x + (size_t)min(t0 + tt, T - 1) * H);
+#pragma unroll
+    for (int i = 0; i < RROW_MAXF4; ++i) xb[tt][i] = xr[min(tid + 256 * i, nf4 - 1)];
+  }
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt) {
+    if (t0 + tt >= T) break;
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RROW_MAXF4; ++i) {
+      const bool ok = tid + 256 * i < nf4;
+      const uint32_t lo = ok ? xb[tt][i].x : 0u, hi = ok ? xb[tt][i].y : 0u;
+      acc = fmaf(wv[i].x, bf16_to_f32(lo & 0xFFFF), acc);
+      acc = fmaf(wv[i].y, bf16_to_f32(lo >> 16), acc);
+      acc = fmaf(wv[i].z, bf16_to_f32(hi & 0xFFFF), acc);
+      acc = fmaf(wv[i].w, bf16_to_f32(hi >> 16), acc);
+    }
+    acc = dpp_wave_sum(acc);
+    if ((tid & 63) == 0) red[(tid >> 6) * 16 + t0 + tt] = acc;
+  }
+}
+
+// One router logit row (expert `row`) for T <= 16 tokens by a 256-thread
+// block: thread t holds float4s t, t+256, ... of the fp32 row (clamped
+// loads, all issued first) and reads the matching bf16 x of up to eight
+// tokens at once; fp32 FMAs, a DPP sum per wave and a fixed-order sum of the
+// four waves through LDS (red: 4*16 floats).
 __device__ __forceinline__ void router_row_block(const uint16_t* __restrict__ x,
                                                  const float* __restrict__ W,
                                                  const float* __restrict__ bias, int T, int E, int H,
@@ -342,23 +381,11 @@ __device__ __forceinline__ void router_row_block(const uint16_t* __restrict__ x,
   float4_t wv[RROW_MAXF4];
   const float4_t* wr = reinterpret_cast<const float4_t*>(W + (size_t)row * H);
 #pragma unroll
-  for (int i = 0; i < RROW_MAXF4; ++i)
-    if (tid + 256 * i < nf4) wv[i] = wr[tid + 256 * i];
-  for (int t = 0; t < T; ++t) {
-    const u32x2* xr = reinterpret_cast<const u32x2*>(x + (size_t)t * H);
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < RROW_MAXF4; ++i) {
-      if (tid + 256 * i < nf4) {
-        const u32x2 xb = xr[tid + 256 * i];
-        acc = fmaf(wv[i].x, bf16_to_f32(xb.x & 0xFFFF), acc);
-        acc = fmaf(wv[i].y, bf16_to_f32(xb.x >> 16), acc);
-        acc = fmaf(wv[i].z, bf16_to_f32(xb.y & 0xFFFF), acc);
-        acc = fmaf(wv[i].w, bf16_to_f32(xb.y >> 16), acc);
-      }
-    }
-    acc = dpp_wave_sum(acc);
-    if ((tid & 63) == 0) red[(tid >> 6) * 16 + t] = acc;
+  for (int i = 0; i < RROW_MAXF4; ++i) wv[i] = wr[min(tid + 256 * i, nf4 - 1)];
+  if (T == 1) {
+    router_row_tokens<1>(x, wv, 0, T, H, tid, red);
+  } else {
+    for (int t0 = 0; t0 < T; t0 += 8) router_row_tokens<8>(x, wv, t0, T, H, tid, red);
   }
   __syncthreads();
   if (tid < T) {
