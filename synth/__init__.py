@@ -75,6 +75,10 @@ WORKLOADS = {
     "stack48": Workload("stack48", H=2560, I=640, E=512, k=10, T=1, layers=48,
                         router_std=_STACK_ROUTER_STD, outlier_rate=0.01,
                         outlier_mult=20.0, seed=2, residual=True),
+    # Wide single layers (few experts): one token with H above 2560 takes the
+    # decode path with a K-split gate/up and a separate h^ step.
+    "wide4k": Workload("wide4k", H=4096, I=256, E=16, k=4, T=1, seed=5),
+    "wide10k": Workload("wide10k", H=10240, I=128, E=8, k=2, T=1, seed=6),
     # 8192-token prefill with a Zipf(1.1) router bias.
     "prefill8k": Workload("prefill8k", H=2560, I=640, E=512, k=10, T=8192,
                           zipf_s=1.1, seed=3),

@@ -55,6 +55,17 @@ def test_decode_tiny_batch_sizes(T):
     check_stages(c, x, run_layer(c, x))
 
 
+@pytest.mark.parametrize("name", ["wide4k", "wide10k"])
+def test_decode_one_token_split_k(name):
+    """One token with H above 2560 (H/32 over one block's 80 chunks): gate/up
+    split over K, the separate h^ kernel summing the split partials, and the
+    slice down kernel reading h^ (the path the one-split h mode bypasses)."""
+    c = case(name, "host")
+    for stream, residual in ((5, False), (6, True)):
+        x = synth.activations(c.wl, T=1, stream=stream)
+        say(name, "split-K decode stages", check_stages(c, x, run_layer(c, x, residual=residual), residual=residual))
+
+
 def test_decode_shared_experts_and_batching():
     """Several tokens on the same experts (one weight read serves them all),
     including more than 8 pairs on one expert (second pass of a block)."""

@@ -25,9 +25,9 @@ def fused(c, xbits, residual):
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny", 4), ("tiny", 16), ("decode", 1),
-                                    ("decode_b8", 8)])
+                                    ("decode_b8", 8), ("wide4k", 1)])
 def test_fused_equals_separate_path(name, T):
-    src = "host" if name == "tiny" else "device"
+    src = "host" if name in ("tiny", "wide4k") else "device"
     c = case("decode" if name == "decode_b8" else name, src)
     x = synth.activations(synth.WORKLOADS[name], T=T, stream=500 + T)
     for residual in (False, True):
