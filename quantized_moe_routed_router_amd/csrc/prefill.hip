@@ -414,6 +414,59 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
     }
   };
 
+  // MFMAs on buffer b with the staging of the next step into buffer 1-b
+  // spread over its four K slices (NVFP4 operands): slice kk dequantizes and
+  // writes elements 8kk..8kk+7 of this thread's A and B chunks, and the
+  // scheduling groups interleave that VALU work with the slice's MFMAs, so the
+  // matrix cores are not idle while the block stages.
+  auto mfma_stage_step = [&](auto bconst, const Regs& R) {
+    constexpr int b = decltype(bconst)::value;
+    TileP As = b ? As1 : As0;
+    TileP Bs = b ? Bs1 : Bs0;
+    TileP Ad = b ? As0 : As1;
+    TileP Bd = b ? Bs0 : Bs1;
+    const uint32_t asw = avalid ? R.asw : 0u;
+    const _Float16 as0 = (_Float16)e4m3_to_f32(asw & 0xFF), as1 = (_Float16)e4m3_to_f32((asw >> 8) & 0xFF);
+    const _Float16 bs0 = (_Float16)e4m3_to_f32(R.bsw & 0xFF), bs1 = (_Float16)e4m3_to_f32((R.bsw >> 8) & 0xFF);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      half8_t af[4], bf[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const half8_t*>(&As[wm * 128 + i * 32 + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *reinterpret_cast<const half8_t*>(&Bs[wn * 64 + j * 32 + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+      // staging part kk: dword kk of each chunk (elements 8kk..8kk+7)
+      {
+        const uint32_t aw = kk == 0 ? R.acw.x : kk == 1 ? R.acw.y : kk == 2 ? R.acw.z : R.acw.w;
+        const uint32_t bw = kk == 0 ? R.bcw.x : kk == 1 ? R.bcw.y : kk == 2 ? R.bcw.z : R.bcw.w;
+        const _Float16 sa = kk < 2 ? as0 : as1, sb = kk < 2 ? bs0 : bs1;
+        const half2_t a2 = {sa, sa}, b2 = {sb, sb};
+        half2_t oa[4], ob[4];
+        oa[0] = fp4x2_to_f16x2<0>(aw) * a2; oa[1] = fp4x2_to_f16x2<1>(aw) * a2;
+        oa[2] = fp4x2_to_f16x2<2>(aw) * a2; oa[3] = fp4x2_to_f16x2<3>(aw) * a2;
+        ob[0] = fp4x2_to_f16x2<0>(bw) * b2; ob[1] = fp4x2_to_f16x2<1>(bw) * b2;
+        ob[2] = fp4x2_to_f16x2<2>(bw) * b2; ob[3] = fp4x2_to_f16x2<3>(bw) * b2;
+        *reinterpret_cast<u32x4*>(&Ad[sr][32 * sc + 8 * kk]) = *reinterpret_cast<const u32x4*>(oa);
+        *reinterpret_cast<u32x4*>(&Bd[sr][32 * sc + 8 * kk]) = *reinterpret_cast<const u32x4*>(ob);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      // this slice: fragment reads, then MFMA / VALU alternating, then the two writes
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+    }
+  };
+
   // Two register sets, so a step's loads are issued two steps before it is
   // staged.  At the top of each loop pass (step st even): buffer 0 holds
   // step st, R1 step st+1, R0 step st+2.
@@ -427,12 +480,20 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
   load_step(R0, 2);
   int st = 0;
   for (; st + 4 < S; st += 2) {
-    mfma_step(B0{});
-    stage(R1, B1{});
+    if constexpr (MODE == 1) {
+      mfma_step(B0{});
+      stage(R1, B1{});
+    } else {
+      mfma_stage_step(B0{}, R1);
+    }
     load_step(R1, st + 3);
     __syncthreads();
-    mfma_step(B1{});
-    stage(R0, B0{});
+    if constexpr (MODE == 1) {
+      mfma_step(B1{});
+      stage(R0, B0{});
+    } else {
+      mfma_stage_step(B1{}, R0);
+    }
     load_step(R0, st + 4);
     __syncthreads();
   }
