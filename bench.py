@@ -200,6 +200,66 @@ def stack_decode(layers, dev, reps: int):
     return res
 
 
+def crossover(layers, dev, reps: int = 20):
+    """Small-batch decode: one layer step (router, x quant, expert FFN, combine
+    with residual) at T tokens through (a) the fused decode layer (GEMV
+    kernels, T <= 16), (b) the separate entry points with the decode FFN
+    (T <= 64) and (c) the separate entry points with the prefill FFN (permute
+    + grouped MFMA GEMMs).  Each path's steps over the resident layers (fresh tokens
+    each step) are captured as one HIP graph and replayed."""
+    import torch
+    import synth
+    wl = synth.WORKLOADS["decode"]
+    NL = len(layers)
+    out = []
+    for T in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        xs = [synth.activations_torch(wl, T, 1200 + 7 * T + li, dev).view(torch.int16) for li in range(NL)]
+        row = {"T": T}
+        paths = []
+        if T <= 16:
+            paths += [("fused_decode_us", "fused")]
+        if T <= 64:
+            paths += [("separate_decode_us", False)]
+        paths += [("prefill_us", True)]
+        for key, mode in paths:
+            stream = torch.cuda.Stream()
+            if mode == "fused":
+                bufs = [L.alloc_fused(T) for L in layers]
+                def step_all():
+                    for L, b, x in zip(layers, bufs, xs):
+                        L.forward_fused(x, b, residual=True, stream=stream)
+            else:
+                bufs = [L.alloc(T, prefill=mode) for L in layers]
+                def step_all():
+                    for L, b, x in zip(layers, bufs, xs):
+                        L.forward(x, b, residual=True, stream=stream)
+            with torch.cuda.stream(stream):
+                step_all()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step_all()
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                g.replay()
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            with torch.cuda.stream(stream):
+                for _ in range(reps):
+                    g.replay()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            row[key] = round(ev0.elapsed_time(ev1) * 1e3 / (reps * NL), 2)
+            del g, bufs
+            torch.cuda.empty_cache()
+        best = min(v for k, v in row.items() if k != "T")
+        row["best_tok_s"] = round(T / (best * 1e-6), 1)
+        log("crossover", row)
+        out.append(row)
+    return out
+
+
 def cpu_baseline(wl, n_tokens: int, dev):
     """The oracle on the host: n_tokens single-token steps through layer 0
     (router, quantizer, expert FFN with on-the-fly dequantization, combine).
@@ -291,6 +351,8 @@ def main():
                     help="also run a 1 GiB device copy (for counter calibration)")
     ap.add_argument("--ffn-only", action="store_true",
                     help="only the eager expert-FFN launches (for counter runs): no graph, no prefill")
+    ap.add_argument("--crossover", action="store_true",
+                    help="only the small-batch table: decode GEMV path vs grouped-MFMA path, T = 1..256")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -316,6 +378,9 @@ def main():
 
     stream = torch.cuda.Stream()
     cycle = NL * max(1, (NX // NL))            # steps per captured graph
+    if args.crossover:
+        print(json.dumps({"crossover": crossover(layers, dev), "layers": NL}), flush=True)
+        return
     if args.ffn_only:
         ffn_us, ffn_bytes = time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream)
         if args.copy_calibration:

@@ -44,8 +44,9 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
-#define MOE_DECODE_MAX_T 16   /* largest token count moe_expert_ffn_decode takes */
+#define MOE_ABI_VERSION 2
+#define MOE_DECODE_MAX_T 64   /* largest token count moe_expert_ffn_decode takes */
+#define MOE_LAYER_MAX_T 16    /* largest token count moe_layer_decode takes */
 #define MOE_MAX_E 1024
 #define MOE_MAX_K 32
 
@@ -127,7 +128,10 @@ int moe_router_topk(const uint16_t* x, const float* W_r, const float* bias, int 
 int moe_quantize_act(const uint16_t* x, int T, int H, uint8_t* codes,
                      uint8_t* scales, float* ts, void* stream);
 
-/* Expert FFN for a small batch (decode), 1 <= T <= MOE_DECODE_MAX_T.
+/* Expert FFN for a small batch (decode), 1 <= T <= MOE_DECODE_MAX_T: weight
+ * GEMVs that read each distinct expert once (below about 64 tokens per call
+ * the expert tiles of the grouped GEMM are mostly padding, so this path is
+ * the faster one there).
  * For each (t, slot), e = ids[t, slot]:
  *   g = W^_gate[e] x^_t,  u = W^_up[e] x^_t,  h = SiLU(g) * u  (fp32)
  *   h^ = NVFP4(h) per (t, slot) row,  out[t, slot, :] = W^_down[e] h^
@@ -151,7 +155,7 @@ int moe_expert_ffn_prefill(const moe_dims* dims, const moe_experts* experts,
                            void* ws, size_t ws_bytes, const moe_ffn_debug* dbg,
                            void* stream);
 
-/* The whole decode layer for 1 <= T <= MOE_DECODE_MAX_T tokens in three
+/* The whole decode layer for 1 <= T <= MOE_LAYER_MAX_T tokens in three
  * kernels: router logits + NVFP4 of x; top-k (ranked in every gate/up block)
  * + gate/up; down + weighted combine.  Same arithmetic as moe_router_topk,
  * moe_quantize_act, moe_expert_ffn_decode and moe_combine in sequence:

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED = 0, -1, -2, -3
 MOE_ERR_CAPACITY, MOE_ERR_HIP, MOE_ERR_WORKSPACE = -4, -5, -6
 MOE_FMT_NVFP4, MOE_FMT_CB3G128 = 0, 1
-MOE_DECODE_MAX_T = 16
+MOE_DECODE_MAX_T = 64      # moe_expert_ffn_decode
+MOE_LAYER_MAX_T = 16       # moe_layer_decode
 
 
 class MoeError(RuntimeError):

@@ -275,7 +275,7 @@ int moe_expert_ffn_decode(const moe_dims* d, const moe_experts* ex, const moe_ac
 
 size_t moe_layer_decode_workspace_bytes(const moe_dims* d, int T) {
   if (check_dims("moe_layer_decode_workspace_bytes", d) != MOE_OK) return 0;
-  if (T < 1 || T > MOE_DECODE_MAX_T) return 0;
+  if (T < 1 || T > MOE_LAYER_MAX_T) return 0;
   return moe::layer_decode_workspace_bytes(d->E, d->H, d->I, d->k, T);
 }
 
@@ -285,8 +285,8 @@ int moe_layer_decode(const moe_dims* d, const moe_experts* ex, const uint16_t* x
   const char* fn = "moe_layer_decode";
   int st = check_dims(fn, d);
   if (st) return st;
-  if (T < 1 || T > MOE_DECODE_MAX_T)
-    return fail(MOE_ERR_SHAPE, "%s: T = %d outside [1, %d]", fn, T, MOE_DECODE_MAX_T);
+  if (T < 1 || T > MOE_LAYER_MAX_T)
+    return fail(MOE_ERR_SHAPE, "%s: T = %d outside [1, %d]", fn, T, MOE_LAYER_MAX_T);
   if (d->fmt_gate_up != MOE_FMT_NVFP4)
     return fail(MOE_ERR_UNSUPPORTED, "%s: gate/up format %d is prefill-only", fn, d->fmt_gate_up);
   if (d->H % 256 || d->H > 4096)

@@ -194,18 +194,19 @@ __device__ __forceinline__ float dot_chunks_row(const u32x4 (&cw)[CPW], const ui
   return acc;
 }
 
-// All pair ids of the call in registers (lane l holds pair l + 64 i), so the
-// owner test and the pair lists come from ballots, not from dependent loads.
-constexpr int PID_CH = (MOE_DECODE_MAX_T * MOE_MAX_K + 63) / 64;    // 8 chunks of 64 pairs
-
+// All pair ids of the call in registers (lane l holds pair l + 64 i, PC
+// chunks of 64 pairs: 1 for one token, 8 up to 16 tokens, 32 up to 64), so
+// the owner test and the pair lists come from ballots, not dependent loads.
+template <int PC>
 struct PairIds {
-  int v[PID_CH];
+  int v[PC];
 };
 
-__device__ __forceinline__ PairIds load_pair_ids(const int32_t* ids, int npairs, int lane) {
-  PairIds p;
+template <int PC>
+__device__ __forceinline__ PairIds<PC> load_pair_ids(const int32_t* ids, int npairs, int lane) {
+  PairIds<PC> p;
 #pragma unroll
-  for (int i = 0; i < PID_CH; ++i) {             // every load issued before the first use
+  for (int i = 0; i < PC; ++i) {                 // every load issued before the first use
     const int q = lane + 64 * i;
     const int v = ids[q < npairs ? q : npairs - 1];
     p.v[i] = q < npairs ? v : 0;
@@ -214,37 +215,40 @@ __device__ __forceinline__ PairIds load_pair_ids(const int32_t* ids, int npairs,
 }
 
 // Expert of pair p (wave-uniform).
-__device__ __forceinline__ int pair_expert(const PairIds& P, int p) {
+template <int PC>
+__device__ __forceinline__ int pair_expert(const PairIds<PC>& P, int p) {
   int sel = 0;
 #pragma unroll
-  for (int i = 0; i < PID_CH; ++i)
+  for (int i = 0; i < PC; ++i)
     if (i == (p >> 6)) sel = P.v[i];
   return __builtin_amdgcn_readlane(sel, p & 63);
 }
 
 // Ballot masks of the pairs routed to expert e (wave-uniform).
-__device__ __forceinline__ void pair_masks(const PairIds& P, int npairs, int e, int lane,
-                                           uint64_t (&m)[PID_CH]) {
+template <int PC>
+__device__ __forceinline__ void pair_masks(const PairIds<PC>& P, int npairs, int e, int lane,
+                                           uint64_t (&m)[PC]) {
 #pragma unroll
-  for (int i = 0; i < PID_CH; ++i) m[i] = __ballot(lane + 64 * i < npairs && P.v[i] == e);
+  for (int i = 0; i < PC; ++i) m[i] = __ballot(lane + 64 * i < npairs && P.v[i] == e);
 }
 
-__device__ __forceinline__ int first_pair(const uint64_t (&m)[PID_CH]) {
+template <int PC>
+__device__ __forceinline__ int first_pair(const uint64_t (&m)[PC]) {
 #pragma unroll
-  for (int i = 0; i < PID_CH; ++i)
+  for (int i = 0; i < PC; ++i)
     if (m[i]) return 64 * i + __ffsll((unsigned long long)m[i]) - 1;
   return -1;
 }
 
 // Up to MAXP pairs from the masks at or after qstart, written to list by
 // thread 0; returns the count and the next unserved pair (or npairs).
-template <int MAXP>
-__device__ __forceinline__ int masked_pairs(const uint64_t (&m)[PID_CH], int npairs, int qstart,
+template <int MAXP, int PC>
+__device__ __forceinline__ int masked_pairs(const uint64_t (&m)[PC], int npairs, int qstart,
                                             int* list, int* qnext, int tid) {
   int n = 0;
   *qnext = npairs;
 #pragma unroll
-  for (int i = 0; i < PID_CH; ++i) {
+  for (int i = 0; i < PC; ++i) {
     uint64_t mm = m[i];
     const int lo = qstart - 64 * i;
     if (lo >= 64) mm = 0;
@@ -291,7 +295,7 @@ struct DecodeWs {
 // ---------------------------------------------------------------- gate/up
 // TOPK: rank the router logits in-block first (fused layer), writing ids and
 // w once (block 0,0,0); otherwise read ids.
-template <int MAXP, int CPW, bool TOPK>
+template <int MAXP, int CPW, bool TOPK, int PC>
 __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
     FfnArgs a, DecodeWs ws, const float* __restrict__ logits, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out, int hmode) {
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
   half2_t* xs = reinterpret_cast<half2_t*>(smem);                         // [MAXP][H/2]
   float* red = reinterpret_cast<float*>(smem + (size_t)MAXP * a.H * 2);   // [nw][MAXP][64]
   __shared__ int list[MAXP];
-  __shared__ int sids[MOE_DECODE_MAX_T * MOE_MAX_K];
+  __shared__ int sids[TOPK ? MOE_MAX_K : 1];             // ranked ids (one token)
   __shared__ int tscr[TOPK ? DEC_MAX_WAVES : 1][64 + MOE_MAX_K];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int npairs = a.T * a.k, p = blockIdx.x, j = blockIdx.y, split = blockIdx.z;
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
   } else {
     ids = a.ids;
   }
-  const PairIds P = load_pair_ids(ids, npairs, lane);
+  const PairIds<PC> P = load_pair_ids<PC>(ids, npairs, lane);
   // one token: its x^ is loaded before the weights and staged while they
   // are in flight; several tokens: only the tokens routed to this block's
   // expert are staged, after the weight loads are issued
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
   ActRegs xr;
   if (!TOPK && MAXP == 1) act_load(xr, a.x_codes, a.x_scales, xtot, tid, blockDim.x);
   const int e = pair_expert(P, p);
-  uint64_t pm[PID_CH];
+  uint64_t pm[PC];
   pair_masks(P, npairs, e, lane, pm);
   if (first_pair(pm) != p) return;                            // another block owns e
   const size_t part_stride = (size_t)npairs * 2 * a.I;
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
       // stage now, only the tokens routed to this expert (each token at
       // most once: its k experts are distinct)
 #pragma unroll
-      for (int i = 0; i < PID_CH; ++i) {
+      for (int i = 0; i < PC; ++i) {
         uint64_t mm = pm[i];
         while (mm) {
           const int t = (64 * i + __ffsll((unsigned long long)mm) - 1) / a.k;
@@ -412,7 +416,7 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
         const float hm = dpp_wave_max(lane < 32 ? fabsf(h) : 0.0f);
         float* hmax = ws.gu + (size_t)npairs * a.I;
 #pragma unroll
-        for (int i = 0; i < PID_CH; ++i) {
+        for (int i = 0; i < PC; ++i) {
           uint64_t mm = pm[i];
           while (mm) {
             const int q = 64 * i + __ffsll((unsigned long long)mm) - 1;
@@ -426,7 +430,7 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < PID_CH; ++i) {
+        for (int i = 0; i < PC; ++i) {
           uint64_t mm = pm[i];
           while (mm) {
             const int q = 64 * i + __ffsll((unsigned long long)mm) - 1;
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
     int qstart = p;
     while (true) {
       int qnext;
-      const int n = masked_pairs<MAXP>(pm, npairs, qstart, list, &qnext, tid);
+      const int n = masked_pairs<MAXP, PC>(pm, npairs, qstart, list, &qnext, tid);
       __syncthreads();
       if (!by_token) {
         for (int i = 0; i < n; ++i) {
@@ -548,7 +552,7 @@ __global__ __launch_bounds__(1024) void h_quant_decode_kernel(FfnArgs a, DecodeW
 }
 
 // ---------------------------------------------------------------- down
-template <int MAXP, int CPW>
+template <int MAXP, int CPW, int PC>
 __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(FfnArgs a, DecodeWs ws) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int nw = blockDim.x >> 6;
@@ -558,9 +562,9 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(FfnArgs
   __shared__ float hts[MAXP];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int npairs = a.T * a.k, p = blockIdx.x, j = blockIdx.y;
-  const PairIds P = load_pair_ids(a.ids, npairs, lane);
+  const PairIds<PC> P = load_pair_ids<PC>(a.ids, npairs, lane);
   const int e = pair_expert(P, p);
-  uint64_t pm[PID_CH];
+  uint64_t pm[PC];
   pair_masks(P, npairs, e, lane, pm);
   if (first_pair(pm) != p) return;                            // another block owns e
   if ((unsigned)e >= (unsigned)a.E) {                         // not an expert: o = 0
@@ -579,7 +583,7 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(FfnArgs
     int qstart = p;
     while (true) {
       int qnext;
-      const int n = masked_pairs<MAXP>(pm, npairs, qstart, list, &qnext, tid);
+      const int n = masked_pairs<MAXP, PC>(pm, npairs, qstart, list, &qnext, tid);
       __syncthreads();
       // h^ of the batch's pairs (quantized once by the h^ kernel) as f16 A*s
       for (int i = 0; i < n; ++i) {
@@ -840,7 +844,7 @@ static bool decode_h_mode(int T, int npairs, int H, int I) {
          I / 32 <= 64;
 }
 
-template <int MAXP, bool FUSED>
+template <int MAXP, int PC, bool FUSED>
 static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logits, int32_t* ids_out,
                                float* w_out, const uint16_t* residual, uint16_t* y, hipStream_t s) {
   const int npairs = a.T * a.k;
@@ -854,9 +858,9 @@ static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logit
   // them once in the top-k kernel first.
   if constexpr (FUSED && MAXP > 1) {
     (void)launch_topk(logits, a.T, a.E, a.k, ids_out, w_out, s);
-    gate_up_decode_kernel<MAXP, DEC_CPW, false><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out, hm);
+    gate_up_decode_kernel<MAXP, DEC_CPW, false, PC><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out, hm);
   } else {
-    gate_up_decode_kernel<MAXP, DEC_CPW, FUSED><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out, hm);
+    gate_up_decode_kernel<MAXP, DEC_CPW, FUSED, PC><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out, hm);
   }
   if (hm) {
     const size_t lds = slice_lds_bytes(npairs, a.I);
@@ -872,15 +876,16 @@ static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logit
   } else {
     const int nw2 = dec_waves(a.I / 32);
     const size_t lds2 = (size_t)MAXP * a.I * 2 + (size_t)nw2 * MAXP * 64 * 4;
-    down_decode_kernel<MAXP, DEC_CPW><<<dim3(npairs, a.H / 64), 64 * nw2, lds2, s>>>(a, ws);
+    down_decode_kernel<MAXP, DEC_CPW, PC><<<dim3(npairs, a.H / 64), 64 * nw2, lds2, s>>>(a, ws);
     if (FUSED) (void)launch_combine(a.out, w_out, residual, a.T, a.k, a.H, y, s);
   }
 }
 
 hipError_t launch_ffn_decode(const FfnArgs& a, void* ws, hipStream_t s) {
   DecodeWs w = carve_decode(ws, a.H, a.I, a.T * a.k, nullptr);
-  if (a.T == 1) launch_decode_pair<1, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
-  else launch_decode_pair<4, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
+  if (a.T == 1) launch_decode_pair<1, 1, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
+  else if (a.T * a.k <= 512) launch_decode_pair<4, 8, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
+  else launch_decode_pair<4, 32, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
   return hipGetLastError();
 }
 
@@ -929,9 +934,9 @@ hipError_t launch_layer_decode(const LayerArgs& L, void* ws, hipStream_t s) {
   DecodeWs dw = carve_decode(w.gu, L.H, L.I, L.T * L.k, nullptr);
   const uint16_t* res = L.residual ? L.x : nullptr;
   if (L.T == 1)
-    launch_decode_pair<1, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s);
+    launch_decode_pair<1, 1, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s);
   else
-    launch_decode_pair<4, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s);
+    launch_decode_pair<4, 8, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ def test_library_exports_every_header_function():
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == m.exported_symbols()
-    assert m.moe_abi_version() == 1
+    assert m.moe_abi_version() == 2
 
 
 def test_sizes():
@@ -61,7 +61,9 @@ def test_validation_null_and_shape():
     code, msg = _err(m.moe_router_topk, 1024, 1024, None, 4, m.dims(2000, 256, 128, 2), 1024, 1024, 1024, 0)
     assert code == m.MOE_ERR_SHAPE and "E = 2000" in msg
     ex = dict(gate_up=1024, down=1024, ts_gate=1024, ts_up=1024, ts_down=1024)
-    code, msg = _err(m.moe_expert_ffn_decode, d, ex, (1024, 1024, 1024), 1024, 17, 1024, 1024, 1 << 20, None, 0)
+    code, msg = _err(m.moe_expert_ffn_decode, d, ex, (1024, 1024, 1024), 1024, 65, 1024, 1024, 1 << 20, None, 0)
+    assert code == m.MOE_ERR_SHAPE and "T = 65" in msg
+    code, msg = _err(m.moe_layer_decode, d, ex, 1024, 1024, None, 17, False, 1024, None, None, 1024, 1 << 20, 0)
     assert code == m.MOE_ERR_SHAPE and "T = 17" in msg
     code, msg = _err(m.moe_expert_ffn_decode, d, ex, (1024, 1024, 1024), 1024, 4, 1024, 1024, 16, None, 0)
     assert code == m.MOE_ERR_WORKSPACE and "16 bytes" in msg

@@ -48,7 +48,7 @@ def test_decode_tiny_residual_and_pure_oracle():
     assert_bf16_rounding_of(g["y"][ok], pure["y"][ok], slack_rel=2e-3)
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("T", [1, 2, 3, 8, 16, 17, 33, 64])
 def test_decode_tiny_batch_sizes(T):
     c = case("tiny", "host")
     x = synth.activations(c.wl, T=T, stream=10 + T)
@@ -114,6 +114,21 @@ def test_decode_flash_next_b8_sampled():
     x = synth.activations(synth.WORKLOADS["decode_b8"], T=8, stream=200)
     g = run_layer(c, x, residual=True)
     say("decode b8 stages", check_stages(c, x, g, residual=True, check_tokens=[0, 5]))
+
+
+@pytest.mark.parametrize("T", [32, 64])
+def test_decode_flash_next_many_tokens_sampled(T):
+    """Decode GEMVs at 32 and 64 tokens (320 and 640 (t, slot) pairs; above 512
+    pairs the kernels hold 32 chunks of pair ids per lane): sampled tokens
+    through every stage, and the whole output against the grouped-GEMM
+    (prefill) entry on the same ids."""
+    c = case("decode", "device")
+    x = synth.activations(synth.WORKLOADS["decode_b8"], T=T, stream=300 + T)
+    g = run_layer(c, x, residual=True)
+    say(f"decode T={T} stages", check_stages(c, x, g, residual=True, check_tokens=[0, T // 2, T - 1]))
+    gp = run_layer(c, x, residual=True, prefill=True)
+    assert np.array_equal(g["ids"], gp["ids"])
+    assert rowwise_rel(g["out"], gp["out"]).max() <= 2e-3
 
 
 def test_combine_parity():
