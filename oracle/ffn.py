@@ -96,10 +96,12 @@ def gate_up(deq: Dict[int, tuple], xq, ids) -> np.ndarray:
     return h.astype(np.float32).reshape(T, k, I)
 
 
-def quantize_h(h):
-    """h^ = Q(h), one tensor scale per (t, slot) row: codes [T*k, I], ..."""
+def quantize_h(h, ts_rows=None):
+    """h^ = Q(h), one tensor scale per (t, slot) row: codes [T*k, I], ...
+    ts_rows: static tensor scales per row (the row's expert's calibrated h
+    scale), or None for the row's own amax / 2688."""
     h = np.asarray(h, dtype=np.float32)
-    return nvfp4.quantize(h.reshape(-1, h.shape[-1]), per_row=True)
+    return nvfp4.quantize(h.reshape(-1, h.shape[-1]), per_row=True, ts_given=ts_rows)
 
 
 def down(deq: Dict[int, tuple], hq, ids) -> np.ndarray:
@@ -130,16 +132,17 @@ def to_bf16(y) -> np.ndarray:
 
 
 def layer(x_bf16_bits, W_r, bias, experts: Dict[int, QExpert], k: int,
-          residual: bool = False):
+          residual: bool = False, h_ts=None):
     """The whole layer with the oracle's own ids and h (no teacher forcing).
     `experts` must hold every expert the router can pick for these tokens.
+    h_ts: static h tensor scale per expert ([E]) or None (per-row amax).
     Returns a dict of every stage."""
     from . import router
     ids, w, near, tau, l = router.route(x_bf16_bits, W_r, k, bias)
     xq = quantize_act(x_bf16_bits)
     deq = {e: dequant_expert(experts[e]) for e in np.unique(ids)}
     h = gate_up(deq, xq, ids)
-    hq = quantize_h(h)
+    hq = quantize_h(h, None if h_ts is None else np.asarray(h_ts, np.float32)[ids].reshape(-1))
     o = down(deq, hq, ids)
     y = combine(o, w, x_bf16_bits if residual else None)
     return dict(ids=ids, w=w, near=near, tau=tau, logits=l, xq=xq, h=h, hq=hq,

@@ -16,6 +16,10 @@ even, in this order (reading):
      with 6 * ts rounded first; sb = 0 when ts = 0;
   4. d = E4M3value(sb) * ts; if d = 0 the block's codes are all 0, otherwise
      code = sign(v) << 3 | E2M1(|v / d|).
+With a static (calibrated) tensor scale, as NVIDIA's NVFP4 checkpoints carry
+for activations (the engine was built for that quantisation: blog post,
+"What it's for"), ts is given per row and steps 1-2 are skipped; values
+beyond 6 * 448 * ts saturate to the largest code and block scale.
 The sign bit is kept even when the magnitude rounds to 0 (so a small negative
 value encodes as 0x8).
 """
@@ -29,11 +33,13 @@ BLOCK = 16
 TS_DIVISOR = np.float32(2688.0)   # 6 * 448
 
 
-def quantize(v, per_row: bool):
+def quantize(v, per_row: bool, ts_given=None):
     """Quantize a 2-D fp32 array v [R, K] (K a multiple of 16).
 
     per_row=True : one tensor scale per row (activation rows).
     per_row=False: one tensor scale for the whole array (a weight matrix).
+    ts_given     : per-row static tensor scales [R] (per_row only): used
+                   as ts instead of amax / 2688.
 
     Returns (codes uint8 [R, K] unpacked 0..15, scales uint8 [R, K/16],
     ts float32 [R] (per_row) or float32 scalar).
@@ -48,7 +54,11 @@ def quantize(v, per_row: bool):
         amax = np.float32(a.max()) if a.size else np.float32(0)
     amax = np.asarray(amax, dtype=np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
-        ts = np.where(amax == 0, np.float32(0), amax / TS_DIVISOR).astype(np.float32)
+        if ts_given is not None:
+            assert per_row
+            ts = np.ascontiguousarray(ts_given, dtype=np.float32).reshape(R)
+        else:
+            ts = np.where(amax == 0, np.float32(0), amax / TS_DIVISOR).astype(np.float32)
         ts_rows = np.broadcast_to(ts, (R,)) if not per_row else ts
         six_ts = (np.float32(6.0) * ts_rows).astype(np.float32)
         blocks = v.reshape(R, K // BLOCK, BLOCK)

@@ -105,9 +105,11 @@ def e4m3_encode(a: Fraction) -> int:
 
 # ---------------------------------------------------------------- quantizer
 
-def quantize_rows(v: np.ndarray, per_row: bool):
+def quantize_rows(v: np.ndarray, per_row: bool, ts_given=None):
     """NVFP4 quantization of fp32 rows in exact rationals, each operation
-    rounded to fp32 as it happens.  Returns (codes, scales, ts-list)."""
+    rounded to fp32 as it happens.  ts_given: static per-row tensor scales
+    (fp32 values) used instead of amax / 2688.  Returns (codes, scales,
+    ts-list)."""
     v = np.asarray(v, dtype=np.float32)
     R, K = v.shape
     F = [[Fraction(float(x)) for x in row] for row in v]
@@ -121,7 +123,10 @@ def quantize_rows(v: np.ndarray, per_row: bool):
     scales = np.zeros((R, K // 16), np.uint8)
     tss = []
     for r in range(R):
-        ts = round_f32(amaxes[r] / 2688) if amaxes[r] != 0 else Fraction(0)
+        if ts_given is not None:
+            ts = Fraction(float(np.float32(ts_given[r])))
+        else:
+            ts = round_f32(amaxes[r] / 2688) if amaxes[r] != 0 else Fraction(0)
         tss.append(ts)
         six = round_f32(6 * ts)
         for b in range(K // 16):

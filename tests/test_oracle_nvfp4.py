@@ -236,3 +236,38 @@ def torch_e4m3(x):
 def e4m3_val(c):
     import torch
     return float(torch.tensor([c], dtype=torch.uint8).view(torch.float8_e4m3fn).float()[0])
+
+
+def test_static_tensor_scale_brute_force():
+    """Static (calibrated) per-row tensor scales: equal to the brute force for
+    scales below (saturating blocks), at and above each row's own amax/2688."""
+    v = _rows(12, 6, 64)
+    own = nvfp4.quantize(v, per_row=True)[2]
+    for f in (0.05, 1.0, 3.7):
+        ts = (own * np.float32(f)).astype(np.float32)
+        ts[0] = np.float32(0.01)                      # a row whose own ts is small
+        codes, scales, ts_out = nvfp4.quantize(v, per_row=True, ts_given=ts)
+        bc, bs, _ = brute.quantize_rows(v, per_row=True, ts_given=ts)
+        assert np.array_equal(codes, bc) and np.array_equal(scales, bs)
+        assert np.array_equal(ts_out.view(np.uint32), ts.view(np.uint32))
+
+
+def test_static_tensor_scale_equals_dynamic_at_own_scale():
+    v = _rows(13, 5, 128)
+    c0, s0, t0 = nvfp4.quantize(v, per_row=True)
+    c1, s1, t1 = nvfp4.quantize(v, per_row=True, ts_given=t0)
+    assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+
+
+def test_static_tensor_scale_worked_block():
+    """One block [1, 0, ..., 0] with ts = 1/448 (fp32): 1 / (6 ts) = 74.67 rounds
+    to the E4M3 value 72 (exponent 6, mantissa 1/8: code 0x69), d = 72 ts =
+    0.1607..., 1 / d = 6.22 rounds to the E2M1 value 6 (code 7).  Saturation:
+    a value 1e6 with the same ts takes block scale 448 (0x7E) and code 7."""
+    v = np.zeros((2, 16), np.float32)
+    v[0, 0] = 1.0
+    v[1, 3] = -1e6
+    ts = np.full(2, np.float32(1.0) / np.float32(448.0), np.float32)
+    codes, scales, _ = nvfp4.quantize(v, per_row=True, ts_given=ts)
+    assert scales[0, 0] == 0x69 and codes[0, 0] == 7 and not codes[0, 1:].any()
+    assert scales[1, 0] == 0x7E and codes[1, 3] == 0x8 | 7
