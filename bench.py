@@ -429,6 +429,38 @@ def main():
     ffn_us, ffn_bytes = time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream)
     achieved = ffn_bytes / (ffn_us * 1e-6) / 1e9
 
+    # the same layer cycle with static (calibrated) h tensor scales: h^ is
+    # quantized in the gate/up kernel, the down kernel reads it
+    static_h = None
+    if args.path == "fused":
+        for li, L in enumerate(layers):
+            L.set_static_h_scales(torch.from_numpy(synth.static_h_scales(wl, li)).to(dev))
+        gs = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for i in range(cycle):
+                step(i)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gs, stream=stream):
+            for i in range(cycle):
+                step(i)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            gs.replay()
+        torch.cuda.synchronize()
+        ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev2.record(stream)
+        with torch.cuda.stream(stream):
+            for _ in range(reps):
+                gs.replay()
+        ev3.record(stream)
+        torch.cuda.synchronize()
+        us_s = ev2.elapsed_time(ev3) * 1e3 / steps
+        static_h = {"us_per_step": round(us_s, 3), "tok_s": round(1e6 / us_s, 1)}
+        log(f"static h scales: {us_s:.2f} us/step")
+        for L in layers:
+            L.set_static_h_scales(None)
+        del gs
+
     # whole step's algorithmic HBM bytes: router weights + k experts + activations
     step_bytes = wl.E * wl.H * 4 + ffn_bytes + wl.H * 2 * 2 + wl.k * wl.H * 4
     layer_gbps = step_bytes / (ms_step * 1e-3) / 1e9
@@ -473,6 +505,7 @@ def main():
                      "traffic": traffic, "kernel": "moe_expert_ffn_decode (gate_up_decode_kernel, down_slice_kernel)",
                      "bytes_per_launch": ffn_bytes, "us_per_launch": round(ffn_us, 3)},
         "cpu_baseline": cpu,
+        "decode_static_h_scale": static_h,
         "stack_decode": stack,
         "prefill_64k": prefill,
     }

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_DECODE_MAX_T 64   /* largest token count moe_expert_ffn_decode takes */
 #define MOE_LAYER_MAX_T 16    /* largest token count moe_layer_decode takes */
 #define MOE_MAX_E 1024
@@ -74,13 +74,20 @@ typedef struct moe_dims {
 /* One layer's resident expert weights, in the packed layouts written by
  * moe_pack_nvfp4 / moe_pack_codebook (sizes from moe_packed_bytes).
  * ts_* are the per-(expert, projection) fp32 tensor scales, [E] each;
- * ts_gate / ts_up are ignored (may be NULL) for MOE_FMT_CB3G128. */
+ * ts_gate / ts_up are ignored (may be NULL) for MOE_FMT_CB3G128.
+ * h_ts [E] or NULL: a static (calibrated) NVFP4 tensor scale for h, the down
+ * projection's input, per expert, as NVIDIA's NVFP4 checkpoints carry for
+ * activations (the engine was built for that quantisation: blog post, "What
+ * it's for").  NULL: each (t, slot) row of h takes amax / 2688 (dynamic).
+ * With a static scale the quantizer skips the amax step; values beyond
+ * 6 * 448 * h_ts[e] saturate.  Must be >= 0 and finite. */
 typedef struct moe_experts {
   const void* gate_up;
   const void* down;
   const float* ts_gate;
   const float* ts_up;
   const float* ts_down;
+  const float* h_ts;
 } moe_experts;
 
 /* NVFP4 activations, one tensor scale per token row:

@@ -38,7 +38,7 @@ class moe_dims(ctypes.Structure):
 class moe_experts(ctypes.Structure):
     _fields_ = [("gate_up", ctypes.c_void_p), ("down", ctypes.c_void_p),
                 ("ts_gate", ctypes.c_void_p), ("ts_up", ctypes.c_void_p),
-                ("ts_down", ctypes.c_void_p)]
+                ("ts_down", ctypes.c_void_p), ("h_ts", ctypes.c_void_p)]
 
 
 class moe_actq(ctypes.Structure):
@@ -174,7 +174,7 @@ def moe_quantize_act(x, T: int, H: int, codes, scales, ts, stream=None):
 
 def _experts(ex) -> moe_experts:
     return moe_experts(_ptr(ex["gate_up"]), _ptr(ex["down"]), _ptr(ex.get("ts_gate")),
-                       _ptr(ex.get("ts_up")), _ptr(ex["ts_down"]))
+                       _ptr(ex.get("ts_up")), _ptr(ex["ts_down"]), _ptr(ex.get("h_ts")))
 
 
 def _actq(xq) -> moe_actq:

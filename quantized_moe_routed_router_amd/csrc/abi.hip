@@ -238,6 +238,7 @@ static int check_ffn(const char* fn, const moe_dims* d, const moe_experts* ex, c
   NEED_PTR(xq->codes); NEED_PTR(xq->scales); NEED_PTR(xq->ts);
   NEED_PTR(ids); NEED_PTR(out); NEED_PTR(ws);
   if (dbg) { OPT_PTR(dbg->h); OPT_PTR(dbg->h_codes); OPT_PTR(dbg->h_scales); OPT_PTR(dbg->h_ts); }
+  OPT_PTR(ex->h_ts);
   const size_t need = moe_ffn_workspace_bytes(d, T, prefill ? 1 : 0);
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace is %zu bytes, %zu needed for T = %d", fn, ws_bytes, need, T);
@@ -250,6 +251,7 @@ static moe::FfnArgs make_args(const moe_dims* d, const moe_experts* ex, const mo
   a.E = d->E; a.H = d->H; a.I = d->I; a.k = d->k; a.T = T; a.fmt = d->fmt_gate_up;
   a.gate_up = (const uint8_t*)ex->gate_up; a.down = (const uint8_t*)ex->down;
   a.ts_gate = ex->ts_gate; a.ts_up = ex->ts_up; a.ts_down = ex->ts_down;
+  a.h_ts = ex->h_ts;
   a.x_codes = xq->codes; a.x_scales = xq->scales; a.x_ts = xq->ts;
   a.ids = ids; a.out = out;
   if (dbg) { a.dbg_h = dbg->h; a.dbg_h_codes = dbg->h_codes; a.dbg_h_scales = dbg->h_scales; a.dbg_h_ts = dbg->h_ts; }
@@ -296,6 +298,7 @@ int moe_layer_decode(const moe_dims* d, const moe_experts* ex, const uint16_t* x
     return fail(MOE_ERR_SHAPE, "%s: H = %d above 3072 needs T = 1", fn, d->H);
   if (!ex) return fail(MOE_ERR_INVALID, "%s: experts is NULL", fn);
   NEED_PTR(ex->gate_up); NEED_PTR(ex->down); NEED_PTR(ex->ts_gate); NEED_PTR(ex->ts_up); NEED_PTR(ex->ts_down);
+  OPT_PTR(ex->h_ts);
   NEED_PTR(x); NEED_PTR(W_r); OPT_PTR(bias); NEED_PTR(y); OPT_PTR(ids); OPT_PTR(w); NEED_PTR(ws);
   const size_t need = moe::layer_decode_workspace_bytes(d->E, d->H, d->I, d->k, T);
   if (ws_bytes < need)
@@ -305,6 +308,7 @@ int moe_layer_decode(const moe_dims* d, const moe_experts* ex, const uint16_t* x
   L.x = x; L.W_r = W_r; L.bias = bias; L.residual = add_residual != 0;
   L.gate_up = (const uint8_t*)ex->gate_up; L.down = (const uint8_t*)ex->down;
   L.ts_gate = ex->ts_gate; L.ts_up = ex->ts_up; L.ts_down = ex->ts_down;
+  L.h_ts = ex->h_ts;
   L.y = y; L.ids_out = ids; L.w_out = w;
   return hip_status(moe::launch_layer_decode(L, ws, as_stream(stream)), fn);
 }

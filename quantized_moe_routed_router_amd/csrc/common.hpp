@@ -185,6 +185,30 @@ __device__ __forceinline__ uint32_t quantize_quarter4(const float (&v)[4], float
   return sb;
 }
 
+// The same quantizer for one element held by one lane (sixteen lanes per
+// block): ab is the block's max |v|; returns the block scale code and writes
+// the element's signed E2M1 code to code4.
+__device__ __forceinline__ uint32_t quantize_one(float v, float ab, float ts, uint32_t& code4) {
+#pragma clang fp contract(off)
+  uint32_t sb = 0;
+  if (ts != 0.0f) {
+    const float six_ts = 6.0f * ts;
+    float r;
+    if (div_fast_ok(six_ts)) r = div_refined(ab, six_ts, recip_refined(six_ts));
+    else r = __fdiv_rn(ab, six_ts);
+    sb = e4m3_rne_satfinite(r);
+  }
+  const float d = e4m3_to_f32(sb) * ts;
+  code4 = 0;
+  if (d != 0.0f) {
+    float q;
+    if (div_fast_ok(d)) q = div_refined(v, d, recip_refined(d));
+    else q = __fdiv_rn(v, d);
+    code4 = e2m1x2_into<0>(0u, __builtin_copysignf(q, v), 0.0f) & 0xFu;
+  }
+  return sb;
+}
+
 __device__ __forceinline__ float tensor_scale_from_amax(float amax) {
   return amax == 0.0f ? 0.0f : __fdiv_rn(amax, TS_DIVISOR);
 }

@@ -360,6 +360,20 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
           if (a.dbg_h) a.dbg_h[(size_t)q * a.I + 32 * j + tid] = 0.0f;
         }
         if (tid == 0) ws.gu[(size_t)npairs * a.I + (size_t)q * (a.I / 32) + j] = 0.0f;
+        if (a.h_ts) {                                         // static mode: h^ = 0
+          if (tid < 16) {
+            ws.hc[(size_t)q * (a.I / 2) + 16 * j + tid] = 0;
+            if (a.dbg_h_codes) a.dbg_h_codes[(size_t)q * (a.I / 2) + 16 * j + tid] = 0;
+          }
+          if (tid < 2) {
+            ws.hsc[(size_t)q * (a.I / 16) + 2 * j + tid] = 0;
+            if (a.dbg_h_scales) a.dbg_h_scales[(size_t)q * (a.I / 16) + 2 * j + tid] = 0;
+          }
+          if (tid == 0 && j == 0) {
+            ws.hts[q] = 0.0f;
+            if (a.dbg_h_ts) a.dbg_h_ts[q] = 0.0f;
+          }
+        }
       } else {
         gu[(size_t)q * 2 * a.I + (tid >> 5) * a.I + 32 * j + (tid & 31)] = 0.0f;
       }
@@ -415,6 +429,22 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
         const float h = silu_mul(v, u);
         const float hm = dpp_wave_max(lane < 32 ? fabsf(h) : 0.0f);
         float* hmax = ws.gu + (size_t)npairs * a.I;
+        // static h scale: this tile's two 16-row blocks are quantized here
+        // (block max over each 16-lane row, one element per lane, the odd
+        // lane's code folded into the even lane's byte), so the down kernel
+        // reads h^ instead of quantizing h itself
+        uint32_t c4 = 0, sb = 0, cpair = 0;
+        float hts_s = 0.0f;
+        if (a.h_ts) {
+          hts_s = a.h_ts[e];
+          float ab = fabsf(h);
+          ab = fmaxf(ab, __int_as_float(dpp_mov<0xB1>(0, __float_as_int(ab))));
+          ab = fmaxf(ab, __int_as_float(dpp_mov<0x4E>(0, __float_as_int(ab))));
+          ab = fmaxf(ab, __int_as_float(dpp_mov<0x141>(0, __float_as_int(ab))));   // row_half_mirror
+          ab = fmaxf(ab, __int_as_float(dpp_mov<0x140>(0, __float_as_int(ab))));   // row_mirror
+          sb = quantize_one(h, ab, hts_s, c4);
+          cpair = c4 | (__shfl_xor(c4, 1, 64) << 4);
+        }
 #pragma unroll
         for (int i = 0; i < PC; ++i) {
           uint64_t mm = pm[i];
@@ -426,6 +456,20 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
               if (a.dbg_h) a.dbg_h[(size_t)q * a.I + 32 * j + lane] = h;
             }
             if (lane == 0) hmax[(size_t)q * (a.I / 32) + j] = hm;
+            if (a.h_ts) {
+              if (lane < 32 && (lane & 1) == 0) {
+                ws.hc[(size_t)q * (a.I / 2) + 16 * j + lane / 2] = (uint8_t)cpair;
+                if (a.dbg_h_codes) a.dbg_h_codes[(size_t)q * (a.I / 2) + 16 * j + lane / 2] = (uint8_t)cpair;
+              }
+              if (lane == 0 || lane == 16) {
+                ws.hsc[(size_t)q * (a.I / 16) + 2 * j + lane / 16] = (uint8_t)sb;
+                if (a.dbg_h_scales) a.dbg_h_scales[(size_t)q * (a.I / 16) + 2 * j + lane / 16] = (uint8_t)sb;
+              }
+              if (lane == 0 && j == 0) {
+                ws.hts[q] = hts_s;
+                if (a.dbg_h_ts) a.dbg_h_ts[q] = hts_s;
+              }
+            }
           }
         }
       } else {
@@ -534,7 +578,11 @@ __global__ __launch_bounds__(1024) void h_quant_decode_kernel(FfnArgs a, DecodeW
   __syncthreads();
   float amax = wmax[0];
   for (int w = 1; w < nw; ++w) amax = fmaxf(amax, wmax[w]);
-  const float ts = tensor_scale_from_amax(amax);
+  // static mode: the pair's expert's calibrated scale (0 for an invalid id,
+  // whose h is 0)
+  int eq = 0;
+  if (a.h_ts) eq = a.ids[q];
+  const float ts = a.h_ts ? ((unsigned)eq < (unsigned)a.E ? a.h_ts[eq] : 0.0f) : tensor_scale_from_amax(amax);
   if (tid < nq) {
     uint32_t bits;
     const uint32_t sb = quantize_quarter4(hv, bmax, ts, bits);
@@ -864,8 +912,13 @@ static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logit
   }
   if (hm) {
     const size_t lds = slice_lds_bytes(npairs, a.I);
-    if (FUSED) down_slice_kernel<true, true><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y);
-    else down_slice_kernel<false, true><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
+    if (a.h_ts) {                              // static h scale: h^ written by gate/up
+      if (FUSED) down_slice_kernel<true, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y);
+      else down_slice_kernel<false, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
+    } else {
+      if (FUSED) down_slice_kernel<true, true><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y);
+      else down_slice_kernel<false, true><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
+    }
     return;
   }
   h_quant_decode_kernel<<<npairs, 64 * ((a.I / 4 + 63) / 64), 0, s>>>(a, ws);
@@ -925,7 +978,7 @@ hipError_t launch_layer_decode(const LayerArgs& L, void* ws, hipStream_t s) {
   FfnArgs a{};
   a.E = L.E; a.H = L.H; a.I = L.I; a.k = L.k; a.T = L.T; a.fmt = FMT_NVFP4;
   a.gate_up = L.gate_up; a.down = L.down;
-  a.ts_gate = L.ts_gate; a.ts_up = L.ts_up; a.ts_down = L.ts_down;
+  a.ts_gate = L.ts_gate; a.ts_up = L.ts_up; a.ts_down = L.ts_down; a.h_ts = L.h_ts;
   a.x_codes = w.xc; a.x_scales = w.xs; a.x_ts = w.xts;
   int32_t* ids_out = L.ids_out ? L.ids_out : w.ids;
   float* w_out = L.w_out ? L.w_out : w.w;

@@ -40,6 +40,7 @@ struct FfnArgs {
   uint8_t* dbg_h_codes;
   uint8_t* dbg_h_scales;
   float* dbg_h_ts;
+  const float* h_ts;   // static h tensor scale per expert, or null (per-row amax)
 };
 
 size_t decode_workspace_bytes(int E, int H, int I, int k, int T);
@@ -55,6 +56,7 @@ struct LayerArgs {
   const float* ts_gate;
   const float* ts_up;
   const float* ts_down;
+  const float* h_ts;
   uint16_t* y;
   int32_t* ids_out;
   float* w_out;

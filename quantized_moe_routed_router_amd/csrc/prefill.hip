@@ -579,7 +579,8 @@ __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, in
       for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(v[j][c]));
     }
   amax = dpp_wave_max(amax);
-  const float ts = tensor_scale_from_amax(amax);
+  // static mode: the row's expert's calibrated scale
+  const float ts = a.h_ts ? a.h_ts[a.ids[pair]] : tensor_scale_from_amax(amax);
 #pragma unroll
   for (int j = 0; j < HQ_MAXB; ++j) {
     const int b = lane + 64 * j;

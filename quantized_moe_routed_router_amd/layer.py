@@ -37,13 +37,23 @@ class Layer:
         self.ts_down = torch.zeros(E, dtype=torch.float32, device=self.device)
         self.W_r: Optional[torch.Tensor] = None
         self.bias: Optional[torch.Tensor] = None
+        # static (calibrated) NVFP4 tensor scale of h per expert, or None
+        self.h_ts: Optional[torch.Tensor] = None
 
     # -------------------------------------------------------------- weights
     def experts(self) -> dict:
         return dict(gate_up=self.gate_up, down=self.down,
                     ts_gate=self.ts_gate if self.fmt == MOE_FMT_NVFP4 else None,
                     ts_up=self.ts_up if self.fmt == MOE_FMT_NVFP4 else None,
-                    ts_down=self.ts_down)
+                    ts_down=self.ts_down, h_ts=self.h_ts)
+
+    def set_static_h_scales(self, h_ts: Optional[torch.Tensor]):
+        """Static NVFP4 tensor scales of h ([E] fp32, >= 0), or None for the
+        per-row dynamic scale."""
+        if h_ts is not None:
+            assert h_ts.shape == (self.E,) and h_ts.dtype == torch.float32
+            h_ts = h_ts.contiguous()
+        self.h_ts = h_ts
 
     def set_router(self, W_r: torch.Tensor, bias: Optional[torch.Tensor] = None):
         assert W_r.shape == (self.E, self.H) and W_r.dtype == torch.float32

@@ -156,6 +156,19 @@ def expert_weights(wl: Workload, layer: int, expert: int):
     return tuple(out)
 
 
+def static_h_scales(wl: Workload, layer: int = 0) -> np.ndarray:
+    """Calibrated-style static h tensor scales, one per expert (fp32 [E]):
+    a base of the order of a row's amax / 2688 at this workload's weight and
+    activation spread (g and u ~ expert_std * sqrt(H * E[x^2]), a row amax of
+    about 6 of their product) times a seeded factor in [0.5, 2], so some
+    rows saturate and some quantize coarsely."""
+    x2 = (1.0 - wl.outlier_rate) + wl.outlier_rate * wl.outlier_mult ** 2
+    s = wl.expert_std * math.sqrt(wl.H * x2)
+    base = 6.0 * s * s / 2688.0
+    g = _rng(wl.seed, 0x5C, layer)
+    return (base * g.uniform(0.5, 2.0, wl.E)).astype(np.float32)
+
+
 def codebook_weights(wl: Workload, layer: int, expert: int, proj: int):
     """3-bit group-128 codebook weights for one gate or up matrix [I, H].
 

@@ -171,8 +171,9 @@ def run_layer(c: LayerCase, xbits: np.ndarray, residual=False, prefill=False, id
     return out
 
 
-def check_stages(c: LayerCase, xbits, g, residual=False, check_tokens=None):
-    """Stage-wise comparison of device outputs g (from run_layer)."""
+def check_stages(c: LayerCase, xbits, g, residual=False, check_tokens=None, h_ts=None):
+    """Stage-wise comparison of device outputs g (from run_layer).  h_ts:
+    the static h tensor scales per expert the layer ran with, or None."""
     T, k, I = xbits.shape[0], c.L.k, c.L.I
     toks = range(T) if check_tokens is None else check_tokens
     ids = g["ids"]
@@ -185,7 +186,8 @@ def check_stages(c: LayerCase, xbits, g, residual=False, check_tokens=None):
     rel_h = rowwise_rel(h_dev, h_ref)
     assert rel_h.max() <= 1e-5, rel_h.max()
     # h^ bit-exact from the device's h
-    hc, hs, hts = offn.quantize_h(h_dev)
+    ts_rows = None if h_ts is None else np.asarray(h_ts, np.float32)[ids[sel]].reshape(-1)
+    hc, hs, hts = offn.quantize_h(h_dev, ts_rows)
     dc = g["dbg_h_codes"].reshape(T, k, I // 2)[sel].reshape(-1, I // 2)
     ds = g["dbg_h_scales"].reshape(T, k, I // 16)[sel].reshape(-1, I // 16)
     dts = g["dbg_h_ts"].reshape(T, k)[sel].reshape(-1)
@@ -198,7 +200,7 @@ def check_stages(c: LayerCase, xbits, g, residual=False, check_tokens=None):
     rel_o = rowwise_rel(o_dev, o_ref)
     assert rel_o.max() <= 2e-3, rel_o.max()
     # pure oracle o (its own h^): rows whose h^ agrees must match
-    hq_pure = offn.quantize_h(h_ref)
+    hq_pure = offn.quantize_h(h_ref, ts_rows)
     o_pure = offn.down(deq, hq_pure, ids[sel])
     same = np.all(nvfp4.pack_nibbles(hq_pure[0]) == dc, axis=1) & np.all(hq_pure[1] == hs, axis=1)
     rel_p = rowwise_rel(o_dev, o_pure)

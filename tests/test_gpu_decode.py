@@ -131,6 +131,30 @@ def test_decode_flash_next_many_tokens_sampled(T):
     assert rowwise_rel(g["out"], gp["out"]).max() <= 2e-3
 
 
+@pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny", 5), ("wide4k", 1), ("decode", 1), ("decode", 8)])
+def test_decode_static_h_scale(name, T):
+    """Static (calibrated) h tensor scales per expert: h^ bit-exact with the
+    oracle quantizer at those scales (one token: quantized in the gate/up
+    kernel; otherwise in the h^ kernel), every other stage as usual; the fused
+    layer equal to the separate entry points."""
+    c = case(name, "host" if name in ("tiny", "wide4k") else "device")
+    h_ts = synth.static_h_scales(c.wl)
+    c.L.set_static_h_scales(torch.from_numpy(h_ts).to(DEV))
+    try:
+        x = synth.activations(synth.WORKLOADS["decode_b8"] if name == "decode" else c.wl, T=T, stream=700 + T)
+        g = run_layer(c, x, residual=True)
+        say(name, T, "static h stages",
+            check_stages(c, x, g, residual=True, h_ts=h_ts, check_tokens=None if T <= 5 else [0, T - 1]))
+        if c.wl.H <= 4096:
+            fb = c.L.alloc_fused(T)
+            c.L.forward_fused(bf16_tensor(x, DEV), fb, residual=True)
+            torch.cuda.synchronize()
+            assert np.array_equal(t2n(fb["ids"]), g["ids"])
+            assert np.array_equal(t2n(fb["y"]), g["y"])
+    finally:
+        c.L.set_static_h_scales(None)
+
+
 def test_combine_parity():
     say("combine")
     r = np.random.default_rng(8)

@@ -21,6 +21,21 @@ def test_prefill_tiny(T):
     say("prefill tiny", T, check_stages(c, x, g, residual=True))
 
 
+@pytest.mark.parametrize("T", [4, 300])
+def test_prefill_static_h_scale(T):
+    """Static h tensor scales per expert in the grouped-GEMM path: h^
+    bit-exact with the oracle quantizer at those scales, other stages as usual."""
+    c = case("tiny", "host")
+    h_ts = synth.static_h_scales(c.wl)
+    c.L.set_static_h_scales(torch.from_numpy(h_ts).to(DEV))
+    try:
+        x = synth.activations(c.wl, T=T, stream=800 + T)
+        g = run_layer(c, x, prefill=True, residual=True)
+        say("prefill static h", T, check_stages(c, x, g, residual=True, h_ts=h_ts))
+    finally:
+        c.L.set_static_h_scales(None)
+
+
 def test_prefill_matches_decode_path():
     """Same tokens through both paths: identical ids and h^ codes (modulo
     accumulation-order flips), outputs within fp32 accumulation noise."""
