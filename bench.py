@@ -288,38 +288,70 @@ def cpu_baseline(wl, n_tokens: int, dev):
                        f"(numpy oracle, fp64 matmuls on dequantized weights, {dt:.1f} s)")
 
 
-def time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream):
-    """The expert FFN call (gate/up, h^, down kernels) timed eagerly with
-    events on its own stream around each launch, cycling layers and tokens.
-    Returns (us per launch, algorithmic HBM bytes per launch)."""
+def time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream, graph=True):
+    """The expert FFN call (its gate/up and down kernels), cycling layers and
+    tokens so the experts come from HBM.  Eager: HIP events on its stream
+    around each launch (host launch gaps between the two kernels included).
+    Graph: the same sequence of calls captured once and replayed, events
+    around the replays (the kernels' own time, as rocprofv3 reports it).
+    Returns (graph us per call or None, eager us per call, algorithmic HBM
+    bytes per call)."""
     import numpy as np
     import torch
     import quantized_moe_routed_router_amd as moe
-    with torch.cuda.stream(stream):            # inputs of the standalone FFN calls
-        for li in range(NL):
-            layers[li].forward(xs[li % NX:li % NX + 1], bufs[li], residual=True, stream=stream)
-    torch.cuda.synchronize()
+    # every (layer, token) of the cycle gets its own routed ids and x^
     n_ffn = min(400, 4 * cycle)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ffn)]
+    seq = [(i % NL, (i // NL) % NX) for i in range(n_ffn)]
+    inputs = {}
     with torch.cuda.stream(stream):
-        for i in range(n_ffn):
-            li = i % NL
-            L, b = layers[li], bufs[li]
-            xq = (b["x_codes"], b["x_scales"], b["x_ts"])
+        for li, t in sorted(set(seq)):
+            b = layers[li].alloc(1, prefill=False)
+            layers[li].forward(xs[t:t + 1], b, residual=True, stream=stream)
+            inputs[(li, t)] = b
+    torch.cuda.synchronize()
+
+    def call(li, t):
+        L, b = layers[li], inputs[(li, t)]
+        moe.moe_expert_ffn_decode(L.d, L.experts(), (b["x_codes"], b["x_scales"], b["x_ts"]), b["ids"], 1,
+                                  b["out"], b["ws"], b["ws_bytes"], None, stream)
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in seq]
+    with torch.cuda.stream(stream):
+        for i, (li, t) in enumerate(seq):
             evs[i][0].record(stream)
-            moe.moe_expert_ffn_decode(L.d, L.experts(), xq, b["ids"], 1, b["out"], b["ws"],
-                                      b["ws_bytes"], None, stream)
+            call(li, t)
             evs[i][1].record(stream)
     torch.cuda.synchronize()
-    ffn_us = float(np.mean([a.elapsed_time(c) for a, c in evs[4:]])) * 1e3
+    eager_us = float(np.mean([a.elapsed_time(c) for a, c in evs[4:]])) * 1e3
+    graph_us = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for li, t in seq:
+                call(li, t)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record(stream)
+        with torch.cuda.stream(stream):
+            for _ in range(reps):
+                g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) * 1e3 / (reps * len(seq))
+        del g
     # algorithmic bytes: the k distinct experts' packed gate/up/down (one
     # token), x^ in and the k fp32 output rows out; the call's own
-    # intermediates (gate/up partials, h^) are not counted
+    # intermediates (h and its tile maxima) are not counted
     exp_bytes = moe.moe_packed_bytes(layers[0].d, 0) // wl.E + moe.moe_packed_bytes(layers[0].d, 1) // wl.E
     act_bytes = wl.H // 2 + wl.H // 16 + 4 + wl.k * wl.H * 4
     ffn_bytes = wl.k * exp_bytes + act_bytes
-    log(f"expert FFN: {ffn_us:.2f} us/launch, {ffn_bytes} B -> {ffn_bytes / ffn_us / 1e3:.0f} GB/s")
-    return ffn_us, ffn_bytes
+    log(f"expert FFN: {eager_us:.2f} us/call eager"
+        + (f", {graph_us:.2f} us/call graph-replayed -> {ffn_bytes / graph_us / 1e3:.0f} GB/s" if graph_us else ""))
+    return graph_us, eager_us, ffn_bytes
 
 
 def copy_calibration(dev):
@@ -382,10 +414,10 @@ def main():
         print(json.dumps({"crossover": crossover(layers, dev), "layers": NL}), flush=True)
         return
     if args.ffn_only:
-        ffn_us, ffn_bytes = time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream)
+        _, ffn_us, ffn_bytes = time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream, graph=False)
         if args.copy_calibration:
             copy_calibration(dev)
-        print(json.dumps({"ffn_us": round(ffn_us, 3), "ffn_bytes": ffn_bytes}), flush=True)
+        print(json.dumps({"ffn_us_eager": round(ffn_us, 3), "ffn_bytes": ffn_bytes}), flush=True)
         return
     def step(i):
         li = i % NL
@@ -426,7 +458,7 @@ def main():
     ms_step = ms_total / steps
     log(f"graph: {steps} steps in {ms_total:.3f} ms (host {t_host * 1e3:.1f} ms): {ms_step * 1e3:.2f} us/step")
 
-    ffn_us, ffn_bytes = time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream)
+    ffn_us, ffn_eager_us, ffn_bytes = time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream)
     achieved = ffn_bytes / (ffn_us * 1e-6) / 1e9
 
     # the same layer cycle with static (calibrated) h tensor scales: h^ is
@@ -503,7 +535,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "moe_expert_ffn_decode (gate_up_decode_kernel, down_slice_kernel)",
-                     "bytes_per_launch": ffn_bytes, "us_per_launch": round(ffn_us, 3)},
+                     "bytes_per_launch": ffn_bytes, "us_per_launch": round(ffn_us, 3),
+                     "timing": "HIP events around graph replays of the calls (layers and tokens cycling)",
+                     "us_per_launch_eager": round(ffn_eager_us, 3)},
         "cpu_baseline": cpu,
         "decode_static_h_scale": static_h,
         "stack_decode": stack,
