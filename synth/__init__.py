@@ -75,6 +75,12 @@ WORKLOADS = {
     "stack48": Workload("stack48", H=2560, I=640, E=512, k=10, T=1, layers=48,
                         router_std=_STACK_ROUTER_STD, outlier_rate=0.01,
                         outlier_mult=20.0, seed=2, residual=True),
+    # Degenerate routing on the tiny shapes: one expert per token, and every
+    # expert for every token (k = E = 16: the most pairs one token can have).
+    "tiny_k1": Workload("tiny_k1", H=256, I=128, E=16, k=1, T=4,
+                        router_std=0.05, expert_std=0.02, seed=7),
+    "tiny_all": Workload("tiny_all", H=256, I=128, E=16, k=16, T=4,
+                         router_std=0.05, expert_std=0.02, seed=8),
     # Wide single layers (few experts): one token with H above 2560 takes the
     # decode path with a K-split gate/up and a separate h^ step.
     "wide4k": Workload("wide4k", H=4096, I=256, E=16, k=4, T=1, seed=5),
