@@ -512,38 +512,68 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 
   // ---- epilogue.  acc[i][j][r]: row wm*128 + i*32 + (r%4) + 8*(r/4) + 4*(lane/32),
   // col wn*64 + j*32 + lane%32 of the 256x256 tile
+  // Both epilogues turn each wave's results around in LDS, a 64 x 32 quarter
+  // at a time, and write 16 B per lane (eight lanes per 32-column row, eight
+  // rows per store instruction).  Buffer 0 (A and B) is free: its last reader
+  // passed the barrier before the last MFMA step.  Each wave uses only its
+  // own 9 KB region, so a wave-level LDS sync suffices.
+  constexpr int QS = 36;                                   // row stride (floats) of a quarter
+  float* q = reinterpret_cast<float*>(wv < 4 ? &As0[0][0] : &Bs0[0][0]) + (wv & 3) * (64 * QS);
+  const int c4 = (lane & 7) * 4, rq = lane >> 3;
   if (!down) {
     const float tsg = (MODE == 0) ? a.ts_gate[e] : 1.0f;
     const float tsu = (MODE == 0) ? a.ts_up[e] : 1.0f;
-    // packed tile nt*4 + wn: gate cols = MFMA tile 0, up cols = tile 1
-    const int n = (nt * 4 + wn) * 32 + (lane & 31);
+    // packed tile nt*4 + wn: gate cols = MFMA tile 0, up cols = tile 1; the
+    // wave's h columns are that tile's 32
+    const int n = (nt * 4 + wn) * 32 + c4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ih = 0; ih < 2; ++ih) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = wm * 128 + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
-        const int pos = row_pos[rl];
-        if (pos < 0) continue;
-        const float sx = row_scale[rl];
-        const float g = acc[i][0][r] * (sx * tsg);
-        const float u = acc[i][1][r] * (sx * tsu);
-        w.h[(size_t)pos * a.I + n] = silu_mul(g, u);
-      }
-  } else {
-    const float tsd = a.ts_down[e];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = nt * BB + wn * 64 + j * 32 + (lane & 31);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int rl = wm * 128 + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
-          const int pos = row_pos[rl];
-          if (pos < 0) continue;
-          a.out[(size_t)row_pair[rl] * a.H + n] = acc[i][j][r] * (row_scale[rl] * tsd);
+          const int lr = i2 * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+          const float sx = row_scale[wm * 128 + ih * 64 + lr];
+          const float g = acc[2 * ih + i2][0][r] * (sx * tsg);
+          const float u = acc[2 * ih + i2][1][r] * (sx * tsu);
+          q[lr * QS + (lane & 31)] = silu_mul(g, u);
         }
+      wave_lds_sync();
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int row = rq + 8 * m;
+        const float4_t v = *reinterpret_cast<const float4_t*>(q + row * QS + c4);
+        const int pos = row_pos[wm * 128 + ih * 64 + row];
+        if (pos >= 0) *reinterpret_cast<float4_t*>(w.h + (size_t)pos * a.I + n) = v;
+      }
+      wave_lds_sync();                                     // reads done before the next quarter's writes
     }
+  } else {
+    // rows of o are scattered: one (t, slot) pair each
+    const float tsd = a.ts_down[e];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int ih = 0; ih < 2; ++ih) {
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            q[(i2 * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5)) * QS + (lane & 31)] = acc[2 * ih + i2][j][r];
+        wave_lds_sync();
+        const int n = nt * BB + wn * 64 + j * 32 + c4;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int row = rq + 8 * m;
+          const int rl = wm * 128 + ih * 64 + row;
+          const float4_t v = *reinterpret_cast<const float4_t*>(q + row * QS + c4);
+          if (row_pos[rl] >= 0) {
+            const float sc = row_scale[rl] * tsd;
+            *reinterpret_cast<float4_t*>(a.out + (size_t)row_pair[rl] * a.H + n) = v * sc;
+          }
+        }
+        wave_lds_sync();                                   // reads done before the next quarter's writes
+      }
   }
 }
 
