@@ -300,9 +300,20 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 2, wn = wv & 3;                    // wave patch: rows wm*128, cols wn*64
-  const int gm = blockIdx.x / n_ntiles, nt = blockIdx.x % n_ntiles;
   const int total_tiles = w.tile_prefix[a.E];
-  if (gm >= total_tiles) return;
+  const int active = total_tiles * n_ntiles;
+  if ((int)blockIdx.x >= active) return;
+  // XCD-aware order: blocks are dealt to the 8 XCDs round-robin, so block b
+  // runs on XCD b % 8; mapping each XCD's blocks to one contiguous range of
+  // tiles keeps the column tiles of a row tile (same gathered activation
+  // rows) and the row tiles of an expert (same weights) in one L2.  A
+  // bijection on [0, active).
+  int lb;
+  {
+    const int q = active >> 3, r = active & 7, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    lb = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
+  }
+  const int gm = lb / n_ntiles, nt = lb % n_ntiles;
   const int e = find_expert(w.tile_prefix, a.E, gm);
   const int mt = gm - w.tile_prefix[e];
   const int row0 = w.offsets[e] + mt * BB, row_end = w.offsets[e + 1];
