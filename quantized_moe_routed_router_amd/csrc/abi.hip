@@ -359,7 +359,7 @@ int moe_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_
   const size_t need = moe::permute_workspace_bytes(T, k, E);
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace is %zu bytes, %zu needed", fn, ws_bytes, need);
-  return hip_status(moe::launch_permute(ids, T, k, E, counts, offsets, perm, inv, ws, nullptr, 0,
+  return hip_status(moe::launch_permute(ids, T, k, E, counts, offsets, perm, inv, ws, nullptr, nullptr, 0,
                                         as_stream(stream)),
                     fn);
 }

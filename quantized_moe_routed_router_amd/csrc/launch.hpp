@@ -74,9 +74,11 @@ hipError_t launch_rms_norm(const uint16_t* x, int T, int H, float target, uint16
 
 size_t permute_workspace_bytes(int T, int k, int E);
 // Counting sort of ids; also writes the per-expert tile prefix for grouped
-// GEMMs with BM-row tiles when tile_prefix != nullptr ([E+1] entries).
+// GEMMs with BM-row tiles when tile_prefix != nullptr ([E+1] entries), and
+// when tile_map != nullptr one record per tile {expert, first row, end row of
+// the expert, 0} (4 ints each, tile_prefix[E] records).
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
-                          int32_t* tile_prefix, int BM, hipStream_t s);
+                          int32_t* tile_prefix, int32_t* tile_map, int BM, hipStream_t s);
 
 }  // namespace moe

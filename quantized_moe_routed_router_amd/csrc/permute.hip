@@ -74,7 +74,7 @@ __global__ __launch_bounds__(1024) void perm_offsets_kernel(const int32_t* __res
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ bin_start,
                                                             int32_t* __restrict__ tile_prefix,
-                                                            int BM) {
+                                                            int32_t* __restrict__ tile_map, int BM) {
   __shared__ int sc[2][1056];
   __shared__ int st[2][1056];
   const int tid = threadIdx.x;
@@ -102,6 +102,12 @@ __global__ __launch_bounds__(1024) void perm_offsets_kernel(const int32_t* __res
     if (e < E) counts[e] = totals[e];
     offsets[e] = excl;                               // offsets[E] = entries with valid ids
     if (tile_prefix) tile_prefix[e] = e ? st[cur][e - 1] : 0;
+    // the expert's tiles: {e, first row of the tile, end of the expert's rows}
+    if (tile_map && e < E) {
+      const int t0 = e ? st[cur][e - 1] : 0, nt = st[cur][e] - t0, end = sc[cur][e];
+      for (int i = 0; i < nt; ++i)
+        *reinterpret_cast<int4*>(tile_map + (size_t)(t0 + i) * 4) = int4{e, excl + i * BM, end, 0};
+    }
   }
 }
 
@@ -149,7 +155,7 @@ size_t permute_workspace_bytes(int T, int k, int E) {
 
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
-                          int32_t* tile_prefix, int BM, hipStream_t s) {
+                          int32_t* tile_prefix, int32_t* tile_map, int BM, hipStream_t s) {
   const int N = T * k;
   const int nch = (N + PCH - 1) / PCH;
   int32_t* cc = reinterpret_cast<int32_t*>(ws);
@@ -162,7 +168,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* coun
   } else {
     perm_chunk_scan_kernel<<<(E + 1 + 3) / 4, 256, 0, s>>>(cc, 0, E, cb, totals);
   }
-  perm_offsets_kernel<<<1, 1024, 0, s>>>(totals, E, counts, offsets, bin_start, tile_prefix, BM);
+  perm_offsets_kernel<<<1, 1024, 0, s>>>(totals, E, counts, offsets, bin_start, tile_prefix, tile_map, BM);
   if (nch > 0)
     perm_scatter_kernel<<<nch, 64, (E + 1) * sizeof(int), s>>>(ids, N, E, cb, bin_start, perm, inv);
   return hipGetLastError();

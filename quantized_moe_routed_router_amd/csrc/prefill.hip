@@ -35,6 +35,7 @@ struct PrefillWs {
   int32_t* perm;
   int32_t* inv;
   int32_t* tile_prefix;
+  int32_t* tile_map;     // per tile {expert, first row, end row of the expert, 0}
   float* h;
   uint8_t* hq_codes;
   uint8_t* hq_scales;
@@ -55,6 +56,7 @@ static PrefillWs carve(void* ws, int E, int I, int k, int T, size_t* total) {
   w.perm = (int32_t*)take(N * 4);
   w.inv = (int32_t*)take(N * 4);
   w.tile_prefix = (int32_t*)take((size_t)(E + 1) * 4);
+  w.tile_map = (int32_t*)take(((N + 127) / 128 + (size_t)E) * 16);   // enough for 128- and 256-row tiles
   w.h = (float*)take(N * I * 4);
   w.hq_codes = take(N * I / 2);
   w.hq_scales = take(N * I / 16);
@@ -70,15 +72,6 @@ size_t prefill_workspace_bytes(int E, int H, int I, int k, int T) {
   return total;
 }
 
-// expert e and its local m-tile for global m-tile gm (binary search)
-__device__ __forceinline__ int find_expert(const int32_t* __restrict__ tile_prefix, int E, int gm) {
-  int lo = 0, hi = E;                       // tile_prefix[lo] <= gm < tile_prefix[hi]
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (tile_prefix[mid] <= gm) lo = mid; else hi = mid;
-  }
-  return lo;
-}
 
 // 32 NVFP4 elements (16 code bytes, 2 E4M3 scales) -> 32 f16 values e2m1*s
 __device__ __forceinline__ void dequant32_nvfp4(u32x4 cw, uint32_t sw, half2_t (&o)[16]) {
@@ -139,9 +132,8 @@ __global__ __launch_bounds__(PF_THREADS) void grouped_gemm_kernel(FfnArgs a, Pre
   const int gm = blockIdx.x / n_ntiles, nt = blockIdx.x % n_ntiles;
   const int total_tiles = w.tile_prefix[a.E];
   if (gm >= total_tiles) return;
-  const int e = find_expert(w.tile_prefix, a.E, gm);
-  const int mt = gm - w.tile_prefix[e];
-  const int row0 = w.offsets[e] + mt * BM, row_end = w.offsets[e + 1];
+  const int4 tr = reinterpret_cast<const int4*>(w.tile_map)[gm];   // {expert, first row, end row}
+  const int e = tr.x, row0 = tr.y, row_end = tr.z;
 
   const bool down = MODE == 2;
   const int K = down ? a.I : a.H;               // contraction length
@@ -314,9 +306,8 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
     lb = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
   }
   const int gm = lb / n_ntiles, nt = lb % n_ntiles;
-  const int e = find_expert(w.tile_prefix, a.E, gm);
-  const int mt = gm - w.tile_prefix[e];
-  const int row0 = w.offsets[e] + mt * BB, row_end = w.offsets[e + 1];
+  const int4 tr = reinterpret_cast<const int4*>(w.tile_map)[gm];   // {expert, first row, end row}
+  const int e = tr.x, row0 = tr.y, row_end = tr.z;
 
   const bool down = MODE == 2;
   const int K = down ? a.I : a.H;
@@ -662,7 +653,7 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
   PrefillWs w = carve(ws, a.E, a.I, a.k, a.T, nullptr);
   if (big_tiles_fit(a)) {
     hipError_t err = launch_permute(a.ids, a.T, a.k, a.E, w.counts, w.offsets, w.perm, w.inv,
-                                    w.perm_ws, w.tile_prefix, BB, s);
+                                    w.perm_ws, w.tile_prefix, w.tile_map, BB, s);
     if (err != hipSuccess) return err;
     const int max_mtiles = (N + BB - 1) / BB + a.E;
     const int nt_gu = (2 * a.I) / BB;
@@ -677,7 +668,7 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
     return hipGetLastError();
   }
   hipError_t err = launch_permute(a.ids, a.T, a.k, a.E, w.counts, w.offsets, w.perm, w.inv,
-                                  w.perm_ws, w.tile_prefix, BM, s);
+                                  w.perm_ws, w.tile_prefix, w.tile_map, BM, s);
   if (err != hipSuccess) return err;
   const int max_mtiles = (N + BM - 1) / BM + a.E;
   const int nt_gu = (2 * a.I) / BN;                  // 64-row packed tiles, two per block
