@@ -317,38 +317,9 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
                                      : (MODE == 1 ? cb_gate_up_expert_bytes(a.H, a.I) : gate_up_expert_bytes(a.H, a.I));
   const uint8_t* wbase = (down ? a.down : a.gate_up) + (size_t)e * w_expert_bytes + (size_t)(nt * 4) * w_tile_bytes;
 
-  if (tid < BB) {
-    const int pos = row0 + tid;
-    int rp = -1, pr = 0;
-    float sc = 0.0f;
-    if (pos < row_end) {
-      rp = pos;
-      pr = w.perm[pos];
-      sc = down ? w.hq_ts[pos] : a.x_ts[pr / a.k];
-    }
-    row_pos[tid] = rp;
-    row_pair[tid] = pr;
-    row_scale[tid] = sc;
-  }
-  __syncthreads();
-
   // staging roles: A row sr, chunk sc (32 K-elements); B packed tile bj,
   // lane bl, chunk sc
   const int sr = tid >> 1, sc = tid & 1;
-  const bool avalid = row_pos[sr] >= 0;
-  const uint8_t* acodes;
-  const uint8_t* ascales;
-  {
-    const int rp = avalid ? row_pos[sr] : row0;         // row0 < row_end: a valid row
-    if (down) {
-      acodes = w.hq_codes + (size_t)rp * (a.I / 2);
-      ascales = w.hq_scales + (size_t)rp * (a.I / 16);
-    } else {
-      const int t = w.perm[rp] / a.k;
-      acodes = a.x_codes + (size_t)t * (a.H / 2);
-      ascales = a.x_scales + (size_t)t * (a.H / 16);
-    }
-  }
   const int bj = sr >> 6, bl = sr & 63;
   const uint8_t* btile = wbase + (size_t)bj * w_tile_bytes;
 
@@ -357,11 +328,8 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
     u32x4 acw, bcw;
     uint32_t asw, bsw, p0, p1, p2;
   };
-  auto load_step = [&](Regs& R, int st) {
-    const int k0 = st * BBK + 32 * sc;
-    R.acw = *reinterpret_cast<const u32x4*>(acodes + k0 / 2);
-    R.asw = *reinterpret_cast<const uint16_t*>(ascales + k0 / 16);
-    const int ck = k0 / 32;
+  auto load_B = [&](Regs& R, int st) {
+    const int ck = (st * BBK + 32 * sc) / 32;
     if (MODE == 1) {
       const uint8_t* grp = btile + (size_t)(ck >> 2) * cb_group_bytes();
       const uint32_t* planes = reinterpret_cast<const uint32_t*>(grp + bl * 48);
@@ -372,6 +340,51 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
       R.bcw = *reinterpret_cast<const u32x4*>(btile + (size_t)ck * 1024 + bl * 16);
       R.bsw = *reinterpret_cast<const uint16_t*>(btile + tile_scale_offset(K) + (size_t)(ck >> 2) * 512 + bl * 8 + (ck & 3) * 2);
     }
+  };
+  // the first two steps' weights depend only on the tile: in flight before
+  // the row metadata and its barrier
+  Regs R0, R1;
+  load_B(R0, 0);
+  load_B(R1, 1);
+
+  if (tid < BB) {
+    const int pos = row0 + tid;
+    int rp = -1, pr = 0;
+    float rs = 0.0f;
+    if (pos < row_end) {
+      rp = pos;
+      pr = w.perm[pos];
+      rs = down ? w.hq_ts[pos] : a.x_ts[pr / a.k];
+    }
+    row_pos[tid] = rp;
+    row_pair[tid] = pr;
+    row_scale[tid] = rs;
+  }
+  __syncthreads();
+
+  const bool avalid = row_pos[sr] >= 0;
+  const uint8_t* acodes;
+  const uint8_t* ascales;
+  {
+    const int rp = avalid ? row_pos[sr] : row0;         // row0 < row_end: a valid row
+    if (down) {
+      acodes = w.hq_codes + (size_t)rp * (a.I / 2);
+      ascales = w.hq_scales + (size_t)rp * (a.I / 16);
+    } else {
+      const int t = row_pair[sr] / a.k;                 // padding rows: pair 0, a valid token
+      acodes = a.x_codes + (size_t)t * (a.H / 2);
+      ascales = a.x_scales + (size_t)t * (a.H / 16);
+    }
+  }
+
+  auto load_A = [&](Regs& R, int st) {
+    const int k0 = st * BBK + 32 * sc;
+    R.acw = *reinterpret_cast<const u32x4*>(acodes + k0 / 2);
+    R.asw = *reinterpret_cast<const uint16_t*>(ascales + k0 / 16);
+  };
+  auto load_step = [&](Regs& R, int st) {
+    load_A(R, st);
+    load_B(R, st);
   };
   auto stage = [&](const Regs& R, auto bconst) {
     constexpr int b = decltype(bconst)::value;
@@ -474,9 +487,8 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
   // step st, R1 step st+1, R0 step st+2.
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  Regs R0, R1;
-  load_step(R0, 0);
-  load_step(R1, 1);
+  load_A(R0, 0);
+  load_A(R1, 1);
   stage(R0, B0{});
   __syncthreads();
   load_step(R0, 2);
