@@ -8,8 +8,10 @@
 //
 // Pipeline (one call, no host round trip):
 //   permute   stable counting sort of the (t, slot) pairs by expert, plus the
-//             per-expert count of BM-row tiles (prefix in tile_prefix)
-//   gate/up   per (expert, 128-row tile, 128-col tile): rows are the expert's
+//             per-expert count of BM-row tiles (prefix in tile_prefix) and one
+//             record per tile {expert, first row, end row} (tile_map)
+//   gate/up   per (expert, row tile, column tile; 256 x 256 when the shapes
+//             allow, else 128 x 128): rows are the expert's
 //             pairs (x^ rows gathered through perm), cols 64-row packed weight
 //             tiles (32 gate rows + the same 32 up rows).  Operands are
 //             dequantized into LDS as f16 (E2M1 x E4M3 is exact in f16, so is a
