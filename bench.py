@@ -354,6 +354,60 @@ def time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream, graph=True):
     return graph_us, eager_us, ffn_bytes
 
 
+def read_stream(dev, nbytes: int, n_bufs: int = 48, reps: int = 5):
+    """A plain streaming read of nbytes (torch's fp32 sum), over n_bufs
+    distinct buffers in turn so every read comes from HBM, captured in one
+    HIP graph and replayed: the practical rate of a single cold pass of that
+    size on this GPU, the yardstick for a call that must read those bytes
+    once.  Also the rate of one 1 GiB read.  Only times are used."""
+    import torch
+    n = nbytes // 4
+    bufs = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(n_bufs)]
+    outs = [torch.empty((), dtype=torch.float32, device=dev) for _ in range(n_bufs)]
+    stream = torch.cuda.Stream()
+
+    def run():
+        for b, o in zip(bufs, outs):
+            torch.sum(b, dim=0, out=o)
+
+    with torch.cuda.stream(stream):
+        run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        run()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * n_bufs)
+    del g, bufs, outs
+    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    o = torch.empty((), dtype=torch.float32, device=dev)
+    torch.sum(big, dim=0, out=o)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.sum(big, dim=0, out=o)
+    e1.record()
+    torch.cuda.synchronize()
+    big_us = e0.elapsed_time(e1) * 1e3 / reps
+    del big
+    torch.cuda.empty_cache()
+    res = {"kernel": "torch fp32 sum (a generic reduction, not a tuned stream kernel)",
+           "bytes": n * 4, "us": round(us, 3), "gbps": round(n * 4 / us / 1e3, 1),
+           "gib_read_gbps": round((1 << 30) / big_us / 1e3, 1)}
+    log(f"read stream: {n * 4} B in {us:.2f} us ({res['gbps']:.0f} GB/s); 1 GiB at {res['gib_read_gbps']:.0f} GB/s")
+    return res
+
+
 def copy_calibration(dev):
     """Three 1 GiB device-to-device copies: a kernel of known traffic for
     scaling the FETCH_SIZE / WRITE_SIZE counters."""
@@ -500,6 +554,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(dev)
 
+    stream_ref = read_stream(dev, ffn_bytes)
+    stream_ref["ffn_call_frac_of_stream"] = round(achieved / stream_ref["gbps"], 3)
+
     stack = None
     if not args.no_stack:
         stack = stack_decode(layers, dev, reps=20)
@@ -538,6 +595,7 @@ def main():
                      "bytes_per_launch": ffn_bytes, "us_per_launch": round(ffn_us, 3),
                      "timing": "HIP events around graph replays of the calls (layers and tokens cycling)",
                      "us_per_launch_eager": round(ffn_eager_us, 3)},
+        "read_stream": stream_ref,
         "cpu_baseline": cpu,
         "decode_static_h_scale": static_h,
         "stack_decode": stack,
