@@ -355,20 +355,22 @@ def time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream, graph=True):
 
 
 def read_stream(dev, nbytes: int, n_bufs: int = 48, reps: int = 5):
-    """A plain streaming read of nbytes (torch's fp32 sum), over n_bufs
-    distinct buffers in turn so every read comes from HBM, captured in one
-    HIP graph and replayed: the practical rate of a single cold pass of that
+    """A plain streaming read of nbytes (the library's moe_stream_read: every
+    thread's 16-byte loads of a pass in flight together, all CUs), over
+    n_bufs distinct buffers in turn so every read comes from HBM, captured in
+    one HIP graph and replayed: the practical rate of one cold pass of that
     size on this GPU, the yardstick for a call that must read those bytes
-    once.  Also the rate of one 1 GiB read.  Only times are used."""
+    once.  Also the rate of one 1 GiB read."""
     import torch
-    n = nbytes // 4
-    bufs = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(n_bufs)]
-    outs = [torch.empty((), dtype=torch.float32, device=dev) for _ in range(n_bufs)]
+    import quantized_moe_routed_router_amd as moe
+    n = nbytes // 16 * 16
+    bufs = [torch.ones(n, dtype=torch.uint8, device=dev) for _ in range(n_bufs)]
+    sink = torch.zeros(moe.MOE_STREAM_READ_MAX_BLOCKS, dtype=torch.int32, device=dev)
     stream = torch.cuda.Stream()
 
     def run():
-        for b, o in zip(bufs, outs):
-            torch.sum(b, dim=0, out=o)
+        for b in bufs:
+            moe.moe_stream_read(b, n, sink, stream)
 
     with torch.cuda.stream(stream):
         run()
@@ -388,23 +390,24 @@ def read_stream(dev, nbytes: int, n_bufs: int = 48, reps: int = 5):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (reps * n_bufs)
-    del g, bufs, outs
-    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    o = torch.empty((), dtype=torch.float32, device=dev)
-    torch.sum(big, dim=0, out=o)
+    del g, bufs
+    big = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        moe.moe_stream_read(big, 1 << 30, sink, stream)
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        torch.sum(big, dim=0, out=o)
-    e1.record()
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            moe.moe_stream_read(big, 1 << 30, sink, stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     big_us = e0.elapsed_time(e1) * 1e3 / reps
     del big
     torch.cuda.empty_cache()
-    res = {"kernel": "torch fp32 sum (a generic reduction, not a tuned stream kernel)",
-           "bytes": n * 4, "us": round(us, 3), "gbps": round(n * 4 / us / 1e3, 1),
+    res = {"kernel": "moe_stream_read (16-byte loads, all in flight per pass)",
+           "bytes": n, "us": round(us, 3), "gbps": round(n / us / 1e3, 1),
            "gib_read_gbps": round((1 << 30) / big_us / 1e3, 1)}
-    log(f"read stream: {n * 4} B in {us:.2f} us ({res['gbps']:.0f} GB/s); 1 GiB at {res['gib_read_gbps']:.0f} GB/s")
+    log(f"read stream: {n} B in {us:.2f} us ({res['gbps']:.0f} GB/s); 1 GiB at {res['gib_read_gbps']:.0f} GB/s")
     return res
 
 

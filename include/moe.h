@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 #define MOE_DECODE_MAX_T 64   /* largest token count moe_expert_ffn_decode takes */
 #define MOE_LAYER_MAX_T 16    /* largest token count moe_layer_decode takes */
 #define MOE_MAX_E 1024
@@ -264,6 +264,17 @@ int moe_check_capacity(int device, size_t bytes_needed);
  * MOE_OK when bytes_needed <= bytes_free, else MOE_ERR_CAPACITY with a
  * message naming both. */
 int moe_capacity_verdict(size_t bytes_free, size_t bytes_needed);
+
+/* Measurement helper (not a step of the layer): one streaming read of
+ * `bytes` bytes at `src` (device, 16-byte aligned, bytes % 16 == 0) with
+ * 16-byte loads spread over the whole GPU, each thread's loads of a pass in
+ * flight together: the yardstick for a call that must read that many bytes
+ * once.  sink: device buffer of MOE_STREAM_READ_MAX_BLOCKS uint32; its words
+ * are written only when a block's XOR of the data equals 0x9E3779B9 (so the
+ * loads cannot be dropped); the contents are not a result.  bytes = 0
+ * enqueues nothing. */
+#define MOE_STREAM_READ_MAX_BLOCKS 2048
+int moe_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 /* Message of the last failure on this host thread ("" if none). */
 const char* moe_last_error(void);

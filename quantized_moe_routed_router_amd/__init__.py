@@ -79,6 +79,7 @@ _SIGS = {
     "moe_layer_decode": (_I, [ctypes.POINTER(moe_dims), ctypes.POINTER(moe_experts), _P, _P, _P, _I,
                               _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_stream_read": (_I, [_P, _SZ, _P, _P]),
 }
 
 _lib = None
@@ -211,6 +212,17 @@ def moe_combine(out, w, residual, T: int, k: int, H: int, y, stream=None):
 
 def moe_rms_norm(x, T: int, H: int, target_rms: float, y, stream=None):
     _check(lib().moe_rms_norm(_ptr(x), T, H, float(target_rms), _ptr(y), _stream(stream)))
+
+
+MOE_STREAM_READ_MAX_BLOCKS = 2048
+
+
+def moe_stream_read(src, nbytes: int, sink, stream=None):
+    """Measurement helper: one streaming read of nbytes at src (the
+    yardstick for a call that reads that many bytes once); sink is a device
+    buffer of MOE_STREAM_READ_MAX_BLOCKS uint32 whose contents are not a
+    result."""
+    _check(lib().moe_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
 
 
 def moe_layer_decode_workspace_bytes(d: moe_dims, T: int) -> int:

@@ -347,6 +347,14 @@ int moe_rms_norm(const uint16_t* x, int T, int H, float target_rms, uint16_t* y,
   return hip_status(moe::launch_rms_norm(x, T, H, target_rms, y, as_stream(stream)), fn);
 }
 
+int moe_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  const char* fn = "moe_stream_read";
+  if (bytes % 16) return fail(MOE_ERR_SHAPE, "%s: bytes = %zu is not a multiple of 16", fn, bytes);
+  if (bytes == 0) return ok();
+  NEED_PTR(src); NEED_PTR(sink);
+  return hip_status(moe::launch_stream_read(src, bytes, sink, as_stream(stream)), fn);
+}
+
 int moe_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
                 int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "moe_permute";

@@ -2,6 +2,7 @@
 // residual: y = bf16_rne(r + sum_i w_i o_i), fp32 accumulation in slot order,
 // one rounding.  The pages keep expert partial sums in FP32 (release post
 // "capy-flash v0.7.1", section "Why it matters").
+#include "../../include/moe.h"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -108,6 +109,40 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const uint16_t* __restric
 hipError_t launch_rms_norm(const uint16_t* x, int T, int H, float target, uint16_t* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
   rms_norm_kernel<<<T, 256, 0, s>>>(x, H, target, y);
+  return hipGetLastError();
+}
+
+// Measurement helper: one streaming read of a buffer, the yardstick for a
+// call that must read a given number of bytes once.  Each thread issues all
+// its 16-byte loads of a pass (four, a grid-stride apart) before using any;
+// the grid fills every CU.  The data only feed an XOR that is written out in
+// the single case that it equals a fixed constant, so the loads stay.
+constexpr int SR_THREADS = 256, SR_UNROLL = 4;
+__global__ __launch_bounds__(SR_THREADS) void stream_read_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                                 uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * SR_THREADS;
+  size_t i = (size_t)blockIdx.x * SR_THREADS + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (SR_UNROLL - 1) * stride < n16; i += SR_UNROLL * stride) {
+    u32x4 v[SR_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SR_UNROLL; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < SR_UNROLL; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  size_t blocks = (n16 + (size_t)SR_THREADS * SR_UNROLL - 1) / ((size_t)SR_THREADS * SR_UNROLL);
+  if (blocks > MOE_STREAM_READ_MAX_BLOCKS) blocks = MOE_STREAM_READ_MAX_BLOCKS;
+  if (blocks == 0) return hipSuccess;
+  stream_read_kernel<<<(unsigned)blocks, SR_THREADS, 0, s>>>(reinterpret_cast<const u32x4*>(src), n16, sink);
   return hipGetLastError();
 }
 

@@ -71,6 +71,7 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s);
 hipError_t launch_combine(const float* out, const float* w, const uint16_t* residual, int T, int k,
                           int H, uint16_t* y, hipStream_t s);
 hipError_t launch_rms_norm(const uint16_t* x, int T, int H, float target, uint16_t* y, hipStream_t s);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 
 size_t permute_workspace_bytes(int T, int k, int E);
 // Counting sort of ids; also writes the per-expert tile prefix for grouped

@@ -26,7 +26,7 @@ def test_library_exports_every_header_function():
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == m.exported_symbols()
-    assert m.moe_abi_version() == 3
+    assert m.moe_abi_version() == 4
 
 
 def test_sizes():
@@ -56,6 +56,10 @@ def test_validation_null_and_shape():
     assert code == m.MOE_ERR_SHAPE and "250" in msg
     code, msg = _err(m.moe_quantize_act, 1028, 4, 256, 1024, 1024, 1024, 0)
     assert code == m.MOE_ERR_INVALID and "aligned" in msg
+    code, msg = _err(m.moe_stream_read, 1024, 100, 1024, 0)
+    assert code == m.MOE_ERR_SHAPE and "bytes = 100" in msg
+    code, msg = _err(m.moe_stream_read, None, 4096, 1024, 0)
+    assert code == m.MOE_ERR_INVALID and "src is NULL" in msg
     code, msg = _err(m.moe_router_topk, 1024, 1024, None, 4, m.dims(16, 256, 128, 17), 1024, 1024, 1024, 0)
     assert code == m.MOE_ERR_SHAPE and "k = 17" in msg
     code, msg = _err(m.moe_router_topk, 1024, 1024, None, 4, m.dims(2000, 256, 128, 2), 1024, 1024, 1024, 0)
@@ -108,3 +112,4 @@ def test_zero_sized_calls_enqueue_nothing():
     m.moe_combine(None, None, None, 0, 2, 256, None, 0)
     m.moe_rms_norm(None, 0, 256, 1.0, None, 0)
     m.moe_quantize_weights(None, 0, 4, 16, None, None, None, 0)
+    m.moe_stream_read(None, 0, None, 0)
