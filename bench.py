@@ -200,7 +200,7 @@ def stack_decode(layers, dev, reps: int):
     return res
 
 
-def crossover(layers, dev, reps: int = 20):
+def crossover(layers, dev, reps: int = 20, Ts=(1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024)):
     """Small-batch decode: one layer step (router, x quant, expert FFN, combine
     with residual) at T tokens through (a) the fused decode layer (GEMV
     kernels, T <= 16), (b) the separate entry points with the decode FFN
@@ -212,7 +212,8 @@ def crossover(layers, dev, reps: int = 20):
     wl = synth.WORKLOADS["decode"]
     NL = len(layers)
     out = []
-    for T in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+    import quantized_moe_routed_router_amd as moe
+    for T in Ts:
         xs = [synth.activations_torch(wl, T, 1200 + 7 * T + li, dev).view(torch.int16) for li in range(NL)]
         row = {"T": T}
         paths = []
@@ -255,6 +256,7 @@ def crossover(layers, dev, reps: int = 20):
             torch.cuda.empty_cache()
         best = min(v for k, v in row.items() if k != "T")
         row["best_tok_s"] = round(T / (best * 1e-6), 1)
+        row["prefill_tile_rows"] = moe.moe_ffn_prefill_tile_rows(layers[0].d, T)
         log("crossover", row)
         out.append(row)
     return out
@@ -440,6 +442,8 @@ def main():
                     help="also run a 1 GiB device copy (for counter calibration)")
     ap.add_argument("--ffn-only", action="store_true",
                     help="only the eager expert-FFN launches (for counter runs): no graph, no prefill")
+    ap.add_argument("--crossover-t", type=str, default=None,
+                    help="comma-separated token counts for --crossover")
     ap.add_argument("--crossover", action="store_true",
                     help="only the small-batch table: decode GEMV path vs grouped-MFMA path, T = 1..256")
     args = ap.parse_args()
@@ -468,7 +472,8 @@ def main():
     stream = torch.cuda.Stream()
     cycle = NL * max(1, (NX // NL))            # steps per captured graph
     if args.crossover:
-        print(json.dumps({"crossover": crossover(layers, dev), "layers": NL}), flush=True)
+        kw = {} if args.crossover_t is None else {"Ts": tuple(int(v) for v in args.crossover_t.split(","))}
+        print(json.dumps({"crossover": crossover(layers, dev, **kw), "layers": NL}), flush=True)
         return
     if args.ffn_only:
         _, ffn_us, ffn_bytes = time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream, graph=False)

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 #define MOE_DECODE_MAX_T 64   /* largest token count moe_expert_ffn_decode takes */
 #define MOE_LAYER_MAX_T 16    /* largest token count moe_layer_decode takes */
 #define MOE_MAX_E 1024
@@ -161,6 +161,16 @@ int moe_expert_ffn_prefill(const moe_dims* dims, const moe_experts* experts,
                            const moe_actq* xq, const int32_t* ids, int T, float* out,
                            void* ws, size_t ws_bytes, const moe_ffn_debug* dbg,
                            void* stream);
+
+/* Row-tile height of the grouped GEMMs moe_expert_ffn_prefill runs for these
+ * dims at T tokens (a host-side query, no device work): 32 while the experts
+ * hold few rows on average (NVFP4 gate/up and T*k <= 16*E: one wave per
+ * 32-row expert tile and 64-row weight tile, operands straight to the matrix
+ * cores, each expert tile's weights read once), else 256 where the shapes
+ * allow 256 x 256 tiles (H % 256 == 0, I >= 256), else 128.  All three give
+ * the same result up to fp32 accumulation order.  Returns a negative
+ * MOE_ERR_* code on invalid dims or T < 1. */
+int moe_ffn_prefill_tile_rows(const moe_dims* dims, int T);
 
 /* The whole decode layer for 1 <= T <= MOE_LAYER_MAX_T tokens in three
  * kernels: router logits + NVFP4 of x; top-k (ranked in every gate/up block)

@@ -61,6 +61,7 @@ _SIGS = {
     "moe_packed_bytes": (_SZ, [ctypes.POINTER(moe_dims), _I]),
     "moe_ffn_workspace_bytes": (_SZ, [ctypes.POINTER(moe_dims), _I, _I]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "moe_ffn_prefill_tile_rows": (_I, [ctypes.POINTER(moe_dims), _I]),
     "moe_quantize_act": (_I, [_P, _I, _I, _P, _P, _P, _P]),
     "moe_quantize_weights": (_I, [_P, _I, _I, _I, _P, _P, _P, _P]),
     "moe_pack_nvfp4": (_I, [ctypes.POINTER(moe_dims), _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -143,6 +144,14 @@ def moe_packed_bytes(d: moe_dims, which: int) -> int:
 
 def moe_ffn_workspace_bytes(d: moe_dims, T: int, prefill: bool) -> int:
     return lib().moe_ffn_workspace_bytes(ctypes.byref(d), T, 1 if prefill else 0)
+
+
+def moe_ffn_prefill_tile_rows(d: moe_dims, T: int) -> int:
+    """Row-tile height (32, 128 or 256) the prefill entry uses at T tokens."""
+    rc = lib().moe_ffn_prefill_tile_rows(ctypes.byref(d), T)
+    if rc < 0:
+        _check(rc)
+    return rc
 
 
 def moe_permute_workspace_bytes(T: int, k: int, E: int) -> int:

@@ -313,6 +313,15 @@ int moe_layer_decode(const moe_dims* d, const moe_experts* ex, const uint16_t* x
   return hip_status(moe::launch_layer_decode(L, ws, as_stream(stream)), fn);
 }
 
+int moe_ffn_prefill_tile_rows(const moe_dims* d, int T) {
+  const char* fn = "moe_ffn_prefill_tile_rows";
+  int st = check_dims(fn, d);
+  if (st) return st;
+  if (T < 1) return fail(MOE_ERR_SHAPE, "%s: T = %d must be >= 1", fn, T);
+  ok();
+  return moe::prefill_tile_rows(d->E, d->H, d->I, d->k, T, d->fmt_gate_up);
+}
+
 int moe_expert_ffn_prefill(const moe_dims* d, const moe_experts* ex, const moe_actq* xq,
                            const int32_t* ids, int T, float* out, void* ws, size_t ws_bytes,
                            const moe_ffn_debug* dbg, void* stream) {

@@ -67,6 +67,8 @@ hipError_t launch_ffn_decode(const FfnArgs& a, void* ws, hipStream_t s);
 
 size_t prefill_workspace_bytes(int E, int H, int I, int k, int T);
 hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s);
+// Row-tile height (32, 128 or 256) launch_ffn_prefill uses for these shapes.
+int prefill_tile_rows(int E, int H, int I, int k, int T, int fmt);
 
 hipError_t launch_combine(const float* out, const float* w, const uint16_t* residual, int T, int k,
                           int H, uint16_t* y, hipStream_t s);

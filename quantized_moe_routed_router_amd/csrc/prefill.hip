@@ -58,7 +58,7 @@ static PrefillWs carve(void* ws, int E, int I, int k, int T, size_t* total) {
   w.perm = (int32_t*)take(N * 4);
   w.inv = (int32_t*)take(N * 4);
   w.tile_prefix = (int32_t*)take((size_t)(E + 1) * 4);
-  w.tile_map = (int32_t*)take(((N + 127) / 128 + (size_t)E) * 16);   // enough for 128- and 256-row tiles
+  w.tile_map = (int32_t*)take(((N + 31) / 32 + (size_t)E) * 16);   // enough for 32-, 128- and 256-row tiles
   w.h = (float*)take(N * I * 4);
   w.hq_codes = take(N * I / 2);
   w.hq_scales = take(N * I / 16);
@@ -593,6 +593,133 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
   }
 }
 
+// ---------------------------------------------------------------- 32-row tiles
+// Mid batches, where an expert holds a few rows: one wave per (32-row expert
+// tile, 64-row packed weight tile), operands loaded straight into MFMA
+// registers, no LDS and no barrier, so the weight stream (read once per
+// expert tile) is the whole cost.  v_mfma_f32_32x32x16_f16 takes from lane l
+// row l%32 of A and of B and eight k values.  In K step s (64 values), lanes
+// 0-31 hold chunk 2s and lanes 32-63 chunk 2s+1, 16 code bytes each,
+// dequantized to 32 f16 per lane, and MFMA m of the step takes values
+// 8m..8m+7 of each lane's chunk: A and B share this k order, so the four
+// MFMAs cover the step's 64 products exactly once.  Two register sets
+// alternate, one step's loads in flight while the other's are consumed.
+// NVFP4 weights only; K % 128 == 0 (even step count).
+constexpr int MB = 32, MWAVES = 4;
+constexpr int MID_MAX_AVG_ROWS = 16;   // 32-row tiles while T*k <= this * E
+
+struct MidRegs {
+  u32x4 ac;          // A codes, this lane's chunk of its row
+  uint32_t as;       // A block scales (two E4M3 bytes)
+  u32x4 bc[2];       // B codes: packed rows r and 32 + r
+  uint32_t bs[2];
+};
+
+__device__ __forceinline__ half8_t cat8(half2_t a, half2_t b, half2_t c, half2_t d) {
+  const half4_t lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const half4_t hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// MODE 0: gate/up NVFP4, 2: down
+template <int MODE>
+__global__ __launch_bounds__(64 * MWAVES) void grouped_gemm_mid_kernel(FfnArgs a, PrefillWs w, int n_ptiles) {
+  static_assert(MODE == 0 || MODE == 2, "NVFP4 weights only");
+  constexpr bool down = MODE == 2;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * MWAVES + (threadIdx.x >> 6);
+  if (item >= w.tile_prefix[a.E] * n_ptiles) return;
+  const int gm = item / n_ptiles, p = item % n_ptiles;
+  const int4 tr = reinterpret_cast<const int4*>(w.tile_map)[gm];   // {expert, first row, end row}
+  const int e = tr.x, row0 = tr.y, row_end = tr.z;
+  const int K = down ? a.I : a.H;
+  const int r = lane & 31, hf = lane >> 5;
+
+  // this lane's A row; a padding lane reads the tile's first row (its
+  // output rows are never stored)
+  const int pos = row0 + r < row_end ? row0 + r : row0;
+  const int pair = w.perm[pos];
+  const uint8_t* acodes;
+  const uint8_t* ascales;
+  float own_scale;
+  if (down) {
+    acodes = w.hq_codes + (size_t)pos * (a.I / 2);
+    ascales = w.hq_scales + (size_t)pos * (a.I / 16);
+    own_scale = w.hq_ts[pos];
+  } else {
+    const int t = pair / a.k;
+    acodes = a.x_codes + (size_t)t * (a.H / 2);
+    ascales = a.x_scales + (size_t)t * (a.H / 16);
+    own_scale = a.x_ts[t];
+  }
+  const uint8_t* tile = (down ? a.down + (size_t)e * down_expert_bytes(a.H, a.I)
+                              : a.gate_up + (size_t)e * gate_up_expert_bytes(a.H, a.I)) +
+                        (size_t)p * tile_bytes(K);
+  const uint8_t* bcodes = tile + r * 16;
+  const uint8_t* bscales = tile + tile_scale_offset(K) + r * 8;
+
+  auto load = [&](MidRegs& o, int s) {
+    const int ck = 2 * s + hf;
+    o.ac = *reinterpret_cast<const u32x4*>(acodes + ck * 16);
+    o.as = *reinterpret_cast<const uint16_t*>(ascales + ck * 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      o.bc[j] = *reinterpret_cast<const u32x4*>(bcodes + (size_t)ck * 1024 + j * 512);
+      o.bs[j] = *reinterpret_cast<const uint16_t*>(bscales + (size_t)(ck >> 2) * 512 + j * 256 + (ck & 3) * 2);
+    }
+  };
+  float16_t acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[j][q] = 0.0f;
+  auto step = [&](const MidRegs& o) {
+    half2_t av[16], bv[2][16];
+    dequant32_nvfp4(o.ac, o.as, av);
+    dequant32_nvfp4(o.bc[0], o.bs[0], bv[0]);
+    dequant32_nvfp4(o.bc[1], o.bs[1], bv[1]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const half8_t af = cat8(av[4 * m], av[4 * m + 1], av[4 * m + 2], av[4 * m + 3]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            af, cat8(bv[j][4 * m], bv[j][4 * m + 1], bv[j][4 * m + 2], bv[j][4 * m + 3]), acc[j], 0, 0, 0);
+    }
+  };
+
+  const int S = K / 64;
+  MidRegs o0, o1;
+  load(o0, 0);
+  load(o1, 1);
+  for (int s = 0; s < S - 2; s += 2) {
+    step(o0);
+    load(o0, s + 2);
+    step(o1);
+    load(o1, s + 3);
+  }
+  step(o0);
+  step(o1);
+
+  // acc[j][q]: tile row (q%4) + 8*(q/4) + 4*hf, column r of sub-tile j
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int rl = (q & 3) + 8 * (q >> 2) + 4 * hf;
+    const float sc = __shfl(own_scale, rl);
+    const int pr = __shfl(pair, rl);
+    if (row0 + rl >= row_end) continue;
+    if (!down) {
+      const float g = acc[0][q] * (sc * a.ts_gate[e]);
+      const float u = acc[1][q] * (sc * a.ts_up[e]);
+      w.h[(size_t)(row0 + rl) * a.I + p * 32 + r] = silu_mul(g, u);
+    } else {
+      const float tsd = a.ts_down[e];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) a.out[(size_t)pr * a.H + p * 64 + j * 32 + r] = acc[j][q] * (sc * tsd);
+    }
+  }
+}
+
 // NVFP4 of each h row (sorted order), one wave per row, one pass: lane l
 // holds the row's 16-element blocks l, l+64, ... (all loads first), the row
 // amax is a wave max of the block maxima; also the optional debug copies in
@@ -662,10 +789,34 @@ static bool big_tiles_fit(const FfnArgs& a) {
          a.H % (2 * BBK) == 0 && a.H >= 4 * BBK;
 }
 
+// Row-tile height the grouped GEMMs use for these shapes: 32 while the
+// experts hold few rows on average (the weight stream is the cost and the
+// 32-row wave kernel reads it once per expert tile), 256 when the shapes
+// allow the big tiles, else 128.
+int prefill_tile_rows(int E, int H, int I, int k, int T, int fmt) {
+  FfnArgs a{};
+  a.E = E; a.H = H; a.I = I; a.k = k; a.T = T; a.fmt = fmt;
+  if (fmt == FMT_NVFP4 && (long long)T * k <= (long long)MID_MAX_AVG_ROWS * E) return MB;
+  return big_tiles_fit(a) ? BB : BM;
+}
+
 hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
   const int N = a.T * a.k;
   PrefillWs w = carve(ws, a.E, a.I, a.k, a.T, nullptr);
-  if (big_tiles_fit(a)) {
+  const int rows = prefill_tile_rows(a.E, a.H, a.I, a.k, a.T, a.fmt);
+  if (rows == MB) {
+    hipError_t err = launch_permute(a.ids, a.T, a.k, a.E, w.counts, w.offsets, w.perm, w.inv,
+                                    w.perm_ws, w.tile_prefix, w.tile_map, MB, s);
+    if (err != hipSuccess) return err;
+    const long long max_mtiles = (N + MB - 1) / MB + a.E;
+    const int np_gu = a.I / 32, np_dn = a.H / 64;   // 64-row packed tiles per projection
+    grouped_gemm_mid_kernel<0><<<(max_mtiles * np_gu + MWAVES - 1) / MWAVES, 64 * MWAVES, 0, s>>>(a, w, np_gu);
+    h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
+    grouped_gemm_mid_kernel<2><<<(max_mtiles * np_dn + MWAVES - 1) / MWAVES, 64 * MWAVES, 0, s>>>(a, w, np_dn);
+    zero_invalid_kernel<<<N < 256 ? N : 256, 256, 0, s>>>(a, w, N);
+    return hipGetLastError();
+  }
+  if (rows == BB) {
     hipError_t err = launch_permute(a.ids, a.T, a.k, a.E, w.counts, w.offsets, w.perm, w.inv,
                                     w.perm_ws, w.tile_prefix, w.tile_map, BB, s);
     if (err != hipSuccess) return err;

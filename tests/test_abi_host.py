@@ -26,7 +26,7 @@ def test_library_exports_every_header_function():
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == m.exported_symbols()
-    assert m.moe_abi_version() == 4
+    assert m.moe_abi_version() == 5
 
 
 def test_sizes():
@@ -40,6 +40,24 @@ def test_sizes():
     assert m.moe_ffn_workspace_bytes(d, 1, False) >= 10 * 640 * 4
     assert m.moe_packed_bytes(m.dims(512, 2500, 640, 10), 0) == 0       # H not a multiple of 128
     assert m.moe_permute_workspace_bytes(4, 2, 16) > 0
+
+
+def test_prefill_tile_rows_rule():
+    fn = m.dims(512, 2560, 640, 10)
+    assert m.moe_ffn_prefill_tile_rows(fn, 1) == 32
+    assert m.moe_ffn_prefill_tile_rows(fn, 819) == 32          # 8190 pairs <= 16 * 512
+    assert m.moe_ffn_prefill_tile_rows(fn, 820) == 256
+    assert m.moe_ffn_prefill_tile_rows(fn, 65536) == 256
+    cb = m.dims(512, 2560, 640, 10, m.MOE_FMT_CB3G128)
+    assert m.moe_ffn_prefill_tile_rows(cb, 1) == 256           # codebook gate/up: no 32-row path
+    tiny = m.dims(16, 256, 128, 2)
+    assert m.moe_ffn_prefill_tile_rows(tiny, 128) == 32
+    assert m.moe_ffn_prefill_tile_rows(tiny, 129) == 128       # I = 128 < 256: 128-row tiles
+    assert m.moe_ffn_prefill_tile_rows(m.dims(16, 256, 128, 2, m.MOE_FMT_CB3G128), 4) == 128
+    with pytest.raises(m.MoeError):
+        m.moe_ffn_prefill_tile_rows(tiny, 0)
+    with pytest.raises(m.MoeError):
+        m.moe_ffn_prefill_tile_rows(m.dims(16, 200, 128, 2), 4)
 
 
 def _err(fn, *args):

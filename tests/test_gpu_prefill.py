@@ -72,6 +72,47 @@ def test_prefill_skewed_ids_many_tiles():
     assert np.array_equal(g2["out"][ok], g["out"][ok])
 
 
+@pytest.mark.parametrize("T,rows", [(37, 32), (300, 128)])
+def test_prefill_tiling_covered(T, rows):
+    """The tiny prefill cases above run the 32-row and the 128-row tilings."""
+    c = case("tiny", "host")
+    assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == rows
+
+
+def test_prefill_mid_tiles_skewed():
+    """32-row expert tiles: one expert holds every token's first slot (120
+    rows: three full tiles and a ragged one), the others a few rows each;
+    then ids outside [0, E), which give zero rows."""
+    c = case("tiny", "host")
+    T = 120
+    assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 32
+    x = synth.activations(c.wl, T=T, stream=79)
+    r = np.random.default_rng(2)
+    ids = np.stack([np.array([5, r.integers(0, 16)]) for _ in range(T)]).astype(np.int32)
+    ids[ids[:, 1] == 5, 1] = 6
+    g = run_layer(c, x, prefill=True, ids_override=ids)
+    say("mid tiles skewed", check_stages(c, x, g, check_tokens=range(0, T, 3)))
+    ids2 = ids.copy()
+    ids2[3, 1] = -4
+    ids2[9, 0] = 16
+    g2 = run_layer(c, x, prefill=True, ids_override=ids2)
+    assert np.all(g2["out"][3, 1] == 0) and np.all(g2["out"][9, 0] == 0)
+    ok = np.ones(ids.shape, bool)
+    ok[3, 1] = ok[9, 0] = False
+    assert np.array_equal(g2["out"][ok], g["out"][ok])
+
+
+@pytest.mark.parametrize("T", [128, 819])
+def test_prefill_flash_next_mid_sampled(T):
+    """Flash-Next shapes on the 32-row tiling (819 tokens: the largest T it
+    takes at k = 10, E = 512): sampled tokens through every stage."""
+    c = case("decode", "device")
+    assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 32
+    x = synth.activations(synth.WORKLOADS["decode_b8"], T=T, stream=900 + T)
+    g = run_layer(c, x, residual=True, prefill=True)
+    say(f"prefill mid T={T}", check_stages(c, x, g, residual=True, check_tokens=[0, T // 2, T - 1]))
+
+
 def test_prefill_codebook_tiny():
     c = case("tiny", "host", moe.MOE_FMT_CB3G128)
     x = synth.activations(c.wl, T=40, stream=79)
