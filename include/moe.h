@@ -136,9 +136,9 @@ int moe_quantize_act(const uint16_t* x, int T, int H, uint8_t* codes,
                      uint8_t* scales, float* ts, void* stream);
 
 /* Expert FFN for a small batch (decode), 1 <= T <= MOE_DECODE_MAX_T: weight
- * GEMVs that read each distinct expert once (below about 64 tokens per call
- * the expert tiles of the grouped GEMM are mostly padding, so this path is
- * the faster one there).
+ * GEMVs that read each distinct expert once (the faster expert FFN up to
+ * about 16 tokens per call; from about 32 tokens the prefill entry's 32-row
+ * expert tiles are).
  * For each (t, slot), e = ids[t, slot]:
  *   g = W^_gate[e] x^_t,  u = W^_up[e] x^_t,  h = SiLU(g) * u  (fp32)
  *   h^ = NVFP4(h) per (t, slot) row,  out[t, slot, :] = W^_down[e] h^
@@ -164,7 +164,7 @@ int moe_expert_ffn_prefill(const moe_dims* dims, const moe_experts* experts,
 
 /* Row-tile height of the grouped GEMMs moe_expert_ffn_prefill runs for these
  * dims at T tokens (a host-side query, no device work): 32 while the experts
- * hold few rows on average (NVFP4 gate/up and T*k <= 16*E: one wave per
+ * hold few rows on average (NVFP4 gate/up and T*k <= 96*E: one wave per
  * 32-row expert tile and 64-row weight tile, operands straight to the matrix
  * cores, each expert tile's weights read once), else 256 where the shapes
  * allow 256 x 256 tiles (H % 256 == 0, I >= 256), else 128.  All three give

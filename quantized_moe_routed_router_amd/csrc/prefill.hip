@@ -606,7 +606,7 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 // alternate, one step's loads in flight while the other's are consumed.
 // NVFP4 weights only; K % 128 == 0 (even step count).
 constexpr int MB = 32, MWAVES = 4;
-constexpr int MID_MAX_AVG_ROWS = 16;   // 32-row tiles while T*k <= this * E
+constexpr int MID_MAX_AVG_ROWS = 96;   // 32-row tiles while T*k <= this * E
 
 struct MidRegs {
   u32x4 ac;          // A codes, this lane's chunk of its row

@@ -45,14 +45,14 @@ def test_sizes():
 def test_prefill_tile_rows_rule():
     fn = m.dims(512, 2560, 640, 10)
     assert m.moe_ffn_prefill_tile_rows(fn, 1) == 32
-    assert m.moe_ffn_prefill_tile_rows(fn, 819) == 32          # 8190 pairs <= 16 * 512
-    assert m.moe_ffn_prefill_tile_rows(fn, 820) == 256
+    assert m.moe_ffn_prefill_tile_rows(fn, 4915) == 32         # 49150 pairs <= 96 * 512
+    assert m.moe_ffn_prefill_tile_rows(fn, 4916) == 256
     assert m.moe_ffn_prefill_tile_rows(fn, 65536) == 256
     cb = m.dims(512, 2560, 640, 10, m.MOE_FMT_CB3G128)
     assert m.moe_ffn_prefill_tile_rows(cb, 1) == 256           # codebook gate/up: no 32-row path
     tiny = m.dims(16, 256, 128, 2)
-    assert m.moe_ffn_prefill_tile_rows(tiny, 128) == 32
-    assert m.moe_ffn_prefill_tile_rows(tiny, 129) == 128       # I = 128 < 256: 128-row tiles
+    assert m.moe_ffn_prefill_tile_rows(tiny, 768) == 32
+    assert m.moe_ffn_prefill_tile_rows(tiny, 769) == 128       # I = 128 < 256: 128-row tiles
     assert m.moe_ffn_prefill_tile_rows(m.dims(16, 256, 128, 2, m.MOE_FMT_CB3G128), 4) == 128
     with pytest.raises(m.MoeError):
         m.moe_ffn_prefill_tile_rows(tiny, 0)

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.mark.parametrize("T", [1, 4, 37, 300])
+@pytest.mark.parametrize("T", [1, 4, 37, 300, 800])
 def test_prefill_tiny(T):
     c = case("tiny", "host")
     x = synth.activations(c.wl, T=T, stream=300 + T)
@@ -72,7 +72,7 @@ def test_prefill_skewed_ids_many_tiles():
     assert np.array_equal(g2["out"][ok], g["out"][ok])
 
 
-@pytest.mark.parametrize("T,rows", [(37, 32), (300, 128)])
+@pytest.mark.parametrize("T,rows", [(37, 32), (300, 32), (800, 128)])
 def test_prefill_tiling_covered(T, rows):
     """The tiny prefill cases above run the 32-row and the 128-row tilings."""
     c = case("tiny", "host")
@@ -102,9 +102,9 @@ def test_prefill_mid_tiles_skewed():
     assert np.array_equal(g2["out"][ok], g["out"][ok])
 
 
-@pytest.mark.parametrize("T", [128, 819])
+@pytest.mark.parametrize("T", [128, 4915])
 def test_prefill_flash_next_mid_sampled(T):
-    """Flash-Next shapes on the 32-row tiling (819 tokens: the largest T it
+    """Flash-Next shapes on the 32-row tiling (4915 tokens: the largest T it
     takes at k = 10, E = 512): sampled tokens through every stage."""
     c = case("decode", "device")
     assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 32
