@@ -604,15 +604,19 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 // 8m..8m+7 of each lane's chunk: A and B share this k order, so the four
 // MFMAs cover the step's 64 products exactly once.  Two register sets
 // alternate, one step's loads in flight while the other's are consumed.
-// NVFP4 weights only; K % 128 == 0 (even step count).
+// Codebook gate/up (MODE 1): the lane reads its chunk's three bit-plane words
+// and its row's eight fp16 entries instead.  K % 128 == 0 (even step count).
 constexpr int MB = 32, MWAVES = 4;
 constexpr int MID_MAX_AVG_ROWS = 96;   // 32-row tiles while T*k <= this * E
+constexpr int MID_MAX_AVG_ROWS_CB = 32;   // the same for codebook gate/up (VALU-heavier decode:
+                                          // it repays the big tiles' reuse sooner)
 
 struct MidRegs {
   u32x4 ac;          // A codes, this lane's chunk of its row
   uint32_t as;       // A block scales (two E4M3 bytes)
-  u32x4 bc[2];       // B codes: packed rows r and 32 + r
-  uint32_t bs[2];
+  u32x4 bc[2];       // B codes (NVFP4) or codebook entries: packed rows r and 32 + r
+  uint32_t bs[2];    // B block scales (NVFP4)
+  uint32_t bp[2][3]; // B index bit-planes (codebook)
 };
 
 __device__ __forceinline__ half8_t cat8(half2_t a, half2_t b, half2_t c, half2_t d) {
@@ -621,10 +625,9 @@ __device__ __forceinline__ half8_t cat8(half2_t a, half2_t b, half2_t c, half2_t
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// MODE 0: gate/up NVFP4, 2: down
+// MODE 0: gate/up NVFP4, 1: gate/up codebook, 2: down
 template <int MODE>
 __global__ __launch_bounds__(64 * MWAVES) void grouped_gemm_mid_kernel(FfnArgs a, PrefillWs w, int n_ptiles) {
-  static_assert(MODE == 0 || MODE == 2, "NVFP4 weights only");
   constexpr bool down = MODE == 2;
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * MWAVES + (threadIdx.x >> 6);
@@ -652,9 +655,13 @@ __global__ __launch_bounds__(64 * MWAVES) void grouped_gemm_mid_kernel(FfnArgs a
     ascales = a.x_scales + (size_t)t * (a.H / 16);
     own_scale = a.x_ts[t];
   }
-  const uint8_t* tile = (down ? a.down + (size_t)e * down_expert_bytes(a.H, a.I)
-                              : a.gate_up + (size_t)e * gate_up_expert_bytes(a.H, a.I)) +
-                        (size_t)p * tile_bytes(K);
+  const uint8_t* tile;
+  if (MODE == 1)
+    tile = a.gate_up + (size_t)e * cb_gate_up_expert_bytes(a.H, a.I) + (size_t)p * cb_tile_bytes(K);
+  else
+    tile = (down ? a.down + (size_t)e * down_expert_bytes(a.H, a.I)
+                 : a.gate_up + (size_t)e * gate_up_expert_bytes(a.H, a.I)) +
+           (size_t)p * tile_bytes(K);
   const uint8_t* bcodes = tile + r * 16;
   const uint8_t* bscales = tile + tile_scale_offset(K) + r * 8;
 
@@ -664,8 +671,19 @@ __global__ __launch_bounds__(64 * MWAVES) void grouped_gemm_mid_kernel(FfnArgs a
     o.as = *reinterpret_cast<const uint16_t*>(ascales + ck * 2);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      o.bc[j] = *reinterpret_cast<const u32x4*>(bcodes + (size_t)ck * 1024 + j * 512);
-      o.bs[j] = *reinterpret_cast<const uint16_t*>(bscales + (size_t)(ck >> 2) * 512 + j * 256 + (ck & 3) * 2);
+      if (MODE == 1) {
+        // group ck/4: [64 rows][3 planes x 4 dwords], then [64 rows][8 fp16]
+        const uint8_t* grp = tile + (size_t)(ck >> 2) * cb_group_bytes();
+        const uint32_t* planes = reinterpret_cast<const uint32_t*>(grp + (j * 32 + r) * 48);
+        const int d = ck & 3;
+        o.bp[j][0] = planes[d];
+        o.bp[j][1] = planes[4 + d];
+        o.bp[j][2] = planes[8 + d];
+        o.bc[j] = *reinterpret_cast<const u32x4*>(grp + 64 * 48 + (j * 32 + r) * 16);
+      } else {
+        o.bc[j] = *reinterpret_cast<const u32x4*>(bcodes + (size_t)ck * 1024 + j * 512);
+        o.bs[j] = *reinterpret_cast<const uint16_t*>(bscales + (size_t)(ck >> 2) * 512 + j * 256 + (ck & 3) * 2);
+      }
     }
   };
   float16_t acc[2];
@@ -676,8 +694,13 @@ __global__ __launch_bounds__(64 * MWAVES) void grouped_gemm_mid_kernel(FfnArgs a
   auto step = [&](const MidRegs& o) {
     half2_t av[16], bv[2][16];
     dequant32_nvfp4(o.ac, o.as, av);
-    dequant32_nvfp4(o.bc[0], o.bs[0], bv[0]);
-    dequant32_nvfp4(o.bc[1], o.bs[1], bv[1]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (MODE == 1)
+        dequant32_cb(o.bp[j][0], o.bp[j][1], o.bp[j][2], o.bc[j], bv[j]);
+      else
+        dequant32_nvfp4(o.bc[j], o.bs[j], bv[j]);
+    }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const half8_t af = cat8(av[4 * m], av[4 * m + 1], av[4 * m + 2], av[4 * m + 3]);
@@ -709,8 +732,8 @@ __global__ __launch_bounds__(64 * MWAVES) void grouped_gemm_mid_kernel(FfnArgs a
     const int pr = __shfl(pair, rl);
     if (row0 + rl >= row_end) continue;
     if (!down) {
-      const float g = acc[0][q] * (sc * a.ts_gate[e]);
-      const float u = acc[1][q] * (sc * a.ts_up[e]);
+      const float g = acc[0][q] * (sc * (MODE == 0 ? a.ts_gate[e] : 1.0f));
+      const float u = acc[1][q] * (sc * (MODE == 0 ? a.ts_up[e] : 1.0f));
       w.h[(size_t)(row0 + rl) * a.I + p * 32 + r] = silu_mul(g, u);
     } else {
       const float tsd = a.ts_down[e];
@@ -796,7 +819,8 @@ static bool big_tiles_fit(const FfnArgs& a) {
 int prefill_tile_rows(int E, int H, int I, int k, int T, int fmt) {
   FfnArgs a{};
   a.E = E; a.H = H; a.I = I; a.k = k; a.T = T; a.fmt = fmt;
-  if (fmt == FMT_NVFP4 && (long long)T * k <= (long long)MID_MAX_AVG_ROWS * E) return MB;
+  const int lim = fmt == FMT_CB3G128 ? MID_MAX_AVG_ROWS_CB : MID_MAX_AVG_ROWS;
+  if ((long long)T * k <= (long long)lim * E) return MB;
   return big_tiles_fit(a) ? BB : BM;
 }
 
@@ -810,7 +834,10 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
     if (err != hipSuccess) return err;
     const long long max_mtiles = (N + MB - 1) / MB + a.E;
     const int np_gu = a.I / 32, np_dn = a.H / 64;   // 64-row packed tiles per projection
-    grouped_gemm_mid_kernel<0><<<(max_mtiles * np_gu + MWAVES - 1) / MWAVES, 64 * MWAVES, 0, s>>>(a, w, np_gu);
+    if (a.fmt == FMT_CB3G128)
+      grouped_gemm_mid_kernel<1><<<(max_mtiles * np_gu + MWAVES - 1) / MWAVES, 64 * MWAVES, 0, s>>>(a, w, np_gu);
+    else
+      grouped_gemm_mid_kernel<0><<<(max_mtiles * np_gu + MWAVES - 1) / MWAVES, 64 * MWAVES, 0, s>>>(a, w, np_gu);
     h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
     grouped_gemm_mid_kernel<2><<<(max_mtiles * np_dn + MWAVES - 1) / MWAVES, 64 * MWAVES, 0, s>>>(a, w, np_dn);
     zero_invalid_kernel<<<N < 256 ? N : 256, 256, 0, s>>>(a, w, N);

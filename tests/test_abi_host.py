@@ -49,11 +49,14 @@ def test_prefill_tile_rows_rule():
     assert m.moe_ffn_prefill_tile_rows(fn, 4916) == 256
     assert m.moe_ffn_prefill_tile_rows(fn, 65536) == 256
     cb = m.dims(512, 2560, 640, 10, m.MOE_FMT_CB3G128)
-    assert m.moe_ffn_prefill_tile_rows(cb, 1) == 256           # codebook gate/up: no 32-row path
+    assert m.moe_ffn_prefill_tile_rows(cb, 1) == 32
+    assert m.moe_ffn_prefill_tile_rows(cb, 1638) == 32         # 16380 pairs <= 32 * 512
+    assert m.moe_ffn_prefill_tile_rows(cb, 1639) == 256
     tiny = m.dims(16, 256, 128, 2)
     assert m.moe_ffn_prefill_tile_rows(tiny, 768) == 32
     assert m.moe_ffn_prefill_tile_rows(tiny, 769) == 128       # I = 128 < 256: 128-row tiles
-    assert m.moe_ffn_prefill_tile_rows(m.dims(16, 256, 128, 2, m.MOE_FMT_CB3G128), 4) == 128
+    assert m.moe_ffn_prefill_tile_rows(m.dims(16, 256, 128, 2, m.MOE_FMT_CB3G128), 4) == 32
+    assert m.moe_ffn_prefill_tile_rows(m.dims(16, 256, 128, 2, m.MOE_FMT_CB3G128), 800) == 128
     with pytest.raises(m.MoeError):
         m.moe_ffn_prefill_tile_rows(tiny, 0)
     with pytest.raises(m.MoeError):

@@ -113,11 +113,27 @@ def test_prefill_flash_next_mid_sampled(T):
     say(f"prefill mid T={T}", check_stages(c, x, g, residual=True, check_tokens=[0, T // 2, T - 1]))
 
 
-def test_prefill_codebook_tiny():
+@pytest.mark.parametrize("T,rows", [(40, 32), (800, 128)])
+def test_prefill_codebook_tiny(T, rows):
     c = case("tiny", "host", moe.MOE_FMT_CB3G128)
-    x = synth.activations(c.wl, T=40, stream=79)
+    assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == rows
+    x = synth.activations(c.wl, T=T, stream=79)
     g = run_layer(c, x, prefill=True, residual=True)
-    say("prefill codebook tiny", check_stages(c, x, g, residual=True))
+    say("prefill codebook tiny", T, check_stages(c, x, g, residual=True,
+                                                 check_tokens=None if T <= 40 else range(0, T, 5)))
+
+
+@pytest.mark.parametrize("T", [1, 128])
+def test_prefill_codebook_flash_next_mid(T):
+    """Codebook gate/up at Flash-Next shapes on the 32-row tiles (the only
+    expert FFN that takes this format at small T): every stage on sampled
+    tokens."""
+    c = case("decode", "device", moe.MOE_FMT_CB3G128)
+    assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 32
+    x = synth.activations(synth.WORKLOADS["decode_b8"], T=T, stream=950 + T)
+    g = run_layer(c, x, residual=True, prefill=True)
+    say(f"prefill codebook mid T={T}", check_stages(c, x, g, residual=True,
+                                                    check_tokens=sorted({0, T // 2, T - 1})))
 
 
 def test_prefill_zipf_8k_sampled():
