@@ -252,6 +252,8 @@ def crossover(layers, dev, reps: int = 20, Ts=(1, 2, 4, 8, 16, 32, 64, 128, 256,
             ev1.record(stream)
             torch.cuda.synchronize()
             row[key] = round(ev0.elapsed_time(ev1) * 1e3 / (reps * NL), 2)
+            if mode is True:
+                row["distinct_experts"] = round(sum(torch.unique(b["ids"]).numel() for b in bufs) / NL, 2)
             del g, bufs
             torch.cuda.empty_cache()
         best = min(v for k, v in row.items() if k != "T")
@@ -474,6 +476,8 @@ def main():
     if args.crossover:
         kw = {} if args.crossover_t is None else {"Ts": tuple(int(v) for v in args.crossover_t.split(","))}
         print(json.dumps({"crossover": crossover(layers, dev, **kw), "layers": NL}), flush=True)
+        if args.copy_calibration:
+            copy_calibration(dev)
         return
     if args.ffn_only:
         _, ffn_us, ffn_bytes = time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream, graph=False)
