@@ -87,3 +87,40 @@ def test_fused_graph_replays_match_eager():
             assert torch.equal(fb["y"], eager[i]), (rep, i)
             _ = (fb["y"].float() * 2).sum().item()             # eager work between replays
     say("graph replays match eager")
+
+
+@pytest.mark.parametrize("T", [40, 800])
+def test_grouped_path_graph_replays_match_eager(T):
+    """The separate entry points with the grouped-GEMM expert FFN (32-row
+    tiles at 40 tokens, 128-row tiles at 800) captured in one HIP graph: every
+    replay, with fresh inputs and eager work in between, equals the eager
+    result bit for bit."""
+    c = case("tiny", "host")
+    L = c.L
+    xs = [bf16_tensor(synth.activations(c.wl, T=T, stream=720 + i), DEV) for i in range(3)]
+    xin = torch.empty_like(xs[0])
+    b = L.alloc(T)
+    assert b["prefill"]
+    eager = []
+    for x in xs:
+        xin.copy_(x)
+        L.forward(xin, b, residual=True)
+        torch.cuda.synchronize()
+        eager.append((b["y"].clone(), b["ids"].clone()))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        L.forward(xin, b, residual=True, stream=s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        L.forward(xin, b, residual=True, stream=s)
+    for rep in range(3):
+        for i, x in enumerate(xs):
+            xin.copy_(x)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(b["ids"], eager[i][1]), (rep, i)
+            assert torch.equal(b["y"], eager[i][0]), (rep, i)
+            _ = (b["y"].float() * 2).sum().item()
+    say("grouped path graph replays match eager", T)
