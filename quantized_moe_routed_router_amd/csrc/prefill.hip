@@ -758,7 +758,11 @@ __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, in
   const int lane = threadIdx.x & 63;
   const int pos = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pos >= N) return;
-  if (pos >= w.offsets[a.E]) return;                     // pair with an invalid id
+  if (pos >= w.offsets[a.E]) {                           // pair with an id outside [0, E):
+    const int pair = w.perm[pos];                        // its output row is zero
+    for (int c = lane; c < a.H; c += 64) a.out[(size_t)pair * a.H + c] = 0.0f;
+    return;
+  }
   const int I = a.I, nblk = I / 16;
   const float* hr = w.h + (size_t)pos * I;
   const int pair = w.perm[pos];
@@ -804,15 +808,6 @@ __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, in
   }
 }
 
-// Pairs whose id is outside [0, E): zero output rows (they sit after
-// offsets[E] in sorted order).
-__global__ void zero_invalid_kernel(FfnArgs a, PrefillWs w, int N) {
-  for (int pos = w.offsets[a.E] + blockIdx.x; pos < N; pos += gridDim.x) {
-    const int pair = w.perm[pos];
-    for (int c = threadIdx.x; c < a.H; c += blockDim.x) a.out[(size_t)pair * a.H + c] = 0.0f;
-  }
-}
-
 static bool big_tiles_fit(const FfnArgs& a) {
   return a.H % BB == 0 && (2 * a.I) % BB == 0 && a.I % (2 * BBK) == 0 && a.I >= 4 * BBK &&
          a.H % (2 * BBK) == 0 && a.H >= 4 * BBK;
@@ -846,7 +841,6 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
       grouped_gemm_mid_kernel<0><<<(max_mtiles * np_gu + MWAVES - 1) / MWAVES, 64 * MWAVES, 0, s>>>(a, w, np_gu);
     h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
     grouped_gemm_mid_kernel<2><<<(max_mtiles * np_dn + MWAVES - 1) / MWAVES, 64 * MWAVES, 0, s>>>(a, w, np_dn);
-    zero_invalid_kernel<<<N < 256 ? N : 256, 256, 0, s>>>(a, w, N);
     return hipGetLastError();
   }
   if (rows == BB) {
@@ -862,7 +856,6 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
     h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
     const int nt_dn = a.H / BB;
     grouped_gemm_big_kernel<2><<<max_mtiles * nt_dn, BTHREADS, 0, s>>>(a, w, nt_dn);
-    zero_invalid_kernel<<<N < 256 ? N : 256, 256, 0, s>>>(a, w, N);
     return hipGetLastError();
   }
   hipError_t err = launch_permute(a.ids, a.T, a.k, a.E, w.counts, w.offsets, w.perm, w.inv,
@@ -877,7 +870,6 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
   h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
   const int nt_dn = a.H / BN;
   grouped_gemm_kernel<2><<<max_mtiles * nt_dn, PF_THREADS, 0, s>>>(a, w, nt_dn);
-  zero_invalid_kernel<<<N < 256 ? N : 256, 256, 0, s>>>(a, w, N);
   return hipGetLastError();
 }
 

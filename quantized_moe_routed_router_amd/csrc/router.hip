@@ -193,6 +193,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
 // multiplied; the eight partial tiles are summed in LDS in wave order
 // (deterministic) and the bias added once.
 constexpr int RS_WAVES = 8, RS_NB = 4;
+constexpr int RS16_MAX_T = 128;         // 16 x 16 tiles up to here (below)
 constexpr int RS_MAX_T = 2560;          // above: the 128 x 128 tiles (enough blocks, less re-reading)
 
 __global__ __launch_bounds__(64 * RS_WAVES) void router_splitk_kernel(const uint16_t* __restrict__ x,
@@ -272,6 +273,89 @@ __global__ __launch_bounds__(64 * RS_WAVES) void router_splitk_kernel(const uint
   }
 }
 
+// Few tokens (up to a few hundred): the 32 x 32 tiles above leave most CUs
+// idle (64 blocks at 128 tokens).  Same scheme on 16-token x 16-expert tiles
+// with v_mfma_f32_16x16x32_bf16: lane l gives row l%16 and eight k values at
+// 8*(l/16) of each 32-wide group and gets rows 4*(l/16)..+3 of column l%16.
+// Needs H % 256 == 0 (every wave's slice of H non-empty).
+typedef float float4v_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(64 * RS_WAVES) void router_splitk16_kernel(const uint16_t* __restrict__ x,
+                                                                        const float* __restrict__ W,
+                                                                        const float* __restrict__ bias,
+                                                                        int T, int E, int H,
+                                                                        float* __restrict__ logits) {
+  __shared__ float red[RS_WAVES][16][17];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+  const int r = lane & 15, qd = lane >> 4;
+  // padding rows read row 0 of the tile (valid); their outputs are not stored
+  const uint16_t* xr = x + (size_t)(t0 + r < T ? t0 + r : t0) * H + 8 * qd;
+  const float* wr = W + (size_t)(e0 + r < E ? e0 + r : e0) * H + 8 * qd;
+  const int G = H / 32;                                   // 32-wide k groups
+  const int g0 = wv * G / RS_WAVES, g1 = (wv + 1) * G / RS_WAVES;
+
+  struct Batch { u32x4 xa[RS_NB]; float4_t wa[RS_NB][2]; };
+  auto load = [&](Batch& b, int gb) {
+#pragma unroll
+    for (int i = 0; i < RS_NB; ++i) {
+      const int g = gb + i < g1 ? gb + i : g1 - 1;         // clamped: always in the slice
+      b.xa[i] = *reinterpret_cast<const u32x4*>(xr + 32 * g);
+      b.wa[i][0] = *reinterpret_cast<const float4_t*>(wr + 32 * g);
+      b.wa[i][1] = *reinterpret_cast<const float4_t*>(wr + 32 * g + 4);
+    }
+  };
+  float4v_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto mul = [&](const Batch& b, int gb) {
+#pragma unroll
+    for (int i = 0; i < RS_NB; ++i) {
+      if (gb + i >= g1) break;
+      uint32_t p[3][4];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float wf = b.wa[i][c >> 2][c & 3];
+        const uint32_t hi = bf16_bits_rne(wf);
+        const float r1 = wf - __uint_as_float(hi << 16);
+        const uint32_t mid = bf16_bits_rne(r1);
+        const float r2 = r1 - __uint_as_float(mid << 16);
+        const uint32_t lo = bf16_bits_rne(r2);
+        const int wd = c >> 1, sh = (c & 1) * 16;
+        if (!(c & 1)) { p[0][wd] = hi; p[1][wd] = mid; p[2][wd] = lo; }
+        else { p[0][wd] |= hi << sh; p[1][wd] |= mid << sh; p[2][wd] |= lo << sh; }
+      }
+      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&b.xa[i]);
+#pragma unroll
+      for (int q = 2; q >= 0; --q) {                     // lo, mid, hi
+        const u32x4 pq = {p[q][0], p[q][1], p[q][2], p[q][3]};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, *reinterpret_cast<const bf16x8_t*>(&pq), acc, 0, 0, 0);
+      }
+    }
+  };
+  Batch b0, b1;
+  load(b0, g0);
+  load(b1, g0 + RS_NB);
+  for (int gb = g0; gb < g1; gb += 2 * RS_NB) {
+    mul(b0, gb);
+    load(b0, gb + 2 * RS_NB);
+    mul(b1, gb + RS_NB);
+    load(b1, gb + 3 * RS_NB);
+  }
+  // acc[j]: token row 4*qd + j, expert column r
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[wv][4 * qd + j][r] = acc[j];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
+    const int t = t0 + row, e = e0 + col;
+    if (t < T && e < E) {
+      float s = red[0][row][col];
+#pragma unroll
+      for (int w = 1; w < RS_WAVES; ++w) s += red[w][row][col];
+      logits[(size_t)t * E + e] = s + (bias ? bias[e] : 0.0f);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- top-k
 // One wave per token; lane l holds logits l, l+64, ... (E <= 1024).  Each of
 // the k rounds takes the wave maximum (DPP), then the lowest expert id holding
@@ -304,6 +388,8 @@ hipError_t launch_router(const uint16_t* x, const float* W_r, const float* bias,
   if (T == 0) return hipSuccess;
   if (T <= 16 && H % 4 == 0 && H <= 4096) {
     router_gemv_kernel<<<E, 256, 0, s>>>(x, W_r, bias, T, E, H, logits);
+  } else if (T <= RS16_MAX_T && H % 256 == 0) {
+    router_splitk16_kernel<<<dim3((T + 15) / 16, (E + 15) / 16), 64 * RS_WAVES, 0, s>>>(x, W_r, bias, T, E, H, logits);
   } else if (T <= RS_MAX_T && H % 128 == 0) {
     router_splitk_kernel<<<dim3((T + 31) / 32, (E + 31) / 32), 64 * RS_WAVES, 0, s>>>(x, W_r, bias, T, E, H, logits);
   } else if (H % RG_BK == 0) {

@@ -51,11 +51,12 @@ def test_prefill_matches_decode_path():
     assert r.max() <= 1e-5
 
 
-def test_prefill_skewed_ids_many_tiles():
+@pytest.mark.parametrize("T,rows", [(700, 32), (800, 128)])
+def test_prefill_skewed_ids_many_tiles(T, rows):
     """One expert holds most pairs (many m-tiles, ragged last tile), others
     few or none; includes ids outside [0, E) which give zero rows."""
     c = case("tiny", "host")
-    T = 700
+    assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == rows
     x = synth.activations(c.wl, T=T, stream=78)
     r = np.random.default_rng(1)
     ids = np.stack([np.array([5, r.integers(0, 16)]) for _ in range(T)]).astype(np.int32)
