@@ -256,7 +256,7 @@ def crossover(layers, dev, reps: int = 20, Ts=(1, 2, 4, 8, 16, 32, 64, 128, 256,
                 row["distinct_experts"] = round(sum(torch.unique(b["ids"]).numel() for b in bufs) / NL, 2)
             del g, bufs
             torch.cuda.empty_cache()
-        best = min(v for k, v in row.items() if k != "T")
+        best = min(v for k, v in row.items() if k.endswith("_us"))
         row["best_tok_s"] = round(T / (best * 1e-6), 1)
         row["prefill_tile_rows"] = moe.moe_ffn_prefill_tile_rows(layers[0].d, T)
         log("crossover", row)

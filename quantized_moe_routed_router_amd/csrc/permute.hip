@@ -3,7 +3,7 @@
 // rows form one contiguous group for the grouped GEMM.  (Every picked expert
 // is computed: forum repost, paragraph "Where it stands".)
 //
-// Three passes, no host round trip:
+// Three passes, no host round trip (one launch up to PSB_MAX_N entries):
 //   1. per 1024-entry chunk, a histogram over experts (LDS atomics);
 //   2. per expert, the exclusive prefix of its chunk counts (chunk order), and
 //      the exclusive prefix over experts -> offsets, counts, tile prefix;
@@ -147,6 +147,96 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(const int32_t* __restr
   }
 }
 
+// Small batches (N <= PSB_MAX_N) in one launch: one block of 16 waves, wave
+// w owns the w-th contiguous sixteenth of the entries.  Per-wave histograms
+// in LDS, their exclusive prefix per bin in wave order, the scan over bins
+// (counts, offsets, tile prefix and records as above), then each wave places
+// its entries 64 at a time with the same ballot ranks.  Entry order inside
+// a wave, then wave order, is the original order, so the sort stays stable.
+// Every wave runs the same number of steps, so the per-step barrier is
+// uniform.
+constexpr int PSB_WAVES = 16, PSB_MAX_N = 16384;
+
+__global__ __launch_bounds__(64 * PSB_WAVES) void perm_small_kernel(const int32_t* __restrict__ ids, int N,
+                                                                     int E, int32_t* __restrict__ counts,
+                                                                     int32_t* __restrict__ offsets,
+                                                                     int32_t* __restrict__ perm,
+                                                                     int32_t* __restrict__ inv,
+                                                                     int32_t* __restrict__ tile_prefix,
+                                                                     int32_t* __restrict__ tile_map, int BM) {
+  __shared__ int hist[PSB_WAVES][1025];                // per wave and bin: count, then running position
+  __shared__ int sc[2][1056];
+  __shared__ int st[2][1056];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int i = tid; i < PSB_WAVES * 1025; i += 64 * PSB_WAVES) (&hist[0][0])[i] = 0;
+  for (int e = tid; e < 1056; e += 64 * PSB_WAVES) { sc[0][e] = 0; st[0][e] = 0; }
+  __syncthreads();
+  const int per = (N + PSB_WAVES - 1) / PSB_WAVES;
+  const int c0 = min(wv * per, N), c1 = min(c0 + per, N);
+  for (int g = c0 + lane; g < c1; g += 64) {
+    int e = ids[g];
+    if ((unsigned)e >= (unsigned)E) e = E;
+    atomicAdd(&hist[wv][e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += 64 * PSB_WAVES) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < PSB_WAVES; ++w) {
+      const int v = hist[w][e];
+      hist[w][e] = run;
+      run += v;
+    }
+    sc[0][e] = run;
+    st[0][e] = (e < E && BM > 0) ? (run + BM - 1) / BM : 0;
+  }
+  __syncthreads();
+  int cur = 0;                                          // Hillis-Steele inclusive scan
+  for (int off = 1; off < 1056; off <<= 1) {
+    for (int e = tid; e < 1056; e += 64 * PSB_WAVES) {
+      sc[cur ^ 1][e] = sc[cur][e] + (e >= off ? sc[cur][e - off] : 0);
+      st[cur ^ 1][e] = st[cur][e] + (e >= off ? st[cur][e - off] : 0);
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+  for (int e = tid; e <= E; e += 64 * PSB_WAVES) {
+    const int excl = e ? sc[cur][e - 1] : 0;
+    if (e < E) counts[e] = sc[cur][e] - excl;
+    offsets[e] = excl;
+    if (tile_prefix) tile_prefix[e] = e ? st[cur][e - 1] : 0;
+    if (tile_map && e < E) {
+      const int t0 = e ? st[cur][e - 1] : 0, nt = st[cur][e] - t0, end = sc[cur][e];
+      for (int i = 0; i < nt; ++i)
+        *reinterpret_cast<int4*>(tile_map + (size_t)(t0 + i) * 4) = int4{e, excl + i * BM, end, 0};
+    }
+  }
+  int nbits = 0;
+  while ((1 << nbits) <= E) ++nbits;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int s = 0; s < per; s += 64) {
+    const int g = c0 + s + lane;
+    const bool valid = g < c1;
+    int e = valid ? ids[g] : 0;
+    if ((unsigned)e >= (unsigned)E) e = E;
+    uint64_t mask = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      mask &= bit ? m : ~m;
+    }
+    if (valid) {
+      const int rank = __popcll(mask & below);
+      const int pos = (e ? sc[cur][e - 1] : 0) + hist[wv][e] + rank;
+      perm[pos] = g;
+      inv[g] = pos;
+      const bool last = (mask >> lane) == 1ull;         // highest lane of its group
+      if (last) hist[wv][e] += __popcll(mask);
+    }
+    __syncthreads();
+  }
+}
+
 size_t permute_workspace_bytes(int T, int k, int E) {
   const size_t N = (size_t)T * k;
   const size_t nch = (N + PCH - 1) / PCH;
@@ -157,6 +247,10 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* coun
                           int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
                           int32_t* tile_prefix, int32_t* tile_map, int BM, hipStream_t s) {
   const int N = T * k;
+  if (N <= PSB_MAX_N) {
+    perm_small_kernel<<<1, 64 * PSB_WAVES, 0, s>>>(ids, N, E, counts, offsets, perm, inv, tile_prefix, tile_map, BM);
+    return hipGetLastError();
+  }
   const int nch = (N + PCH - 1) / PCH;
   int32_t* cc = reinterpret_cast<int32_t*>(ws);
   int32_t* cb = cc + (size_t)nch * (E + 1);

@@ -25,10 +25,10 @@ from . import (MOE_FMT_CB3G128, MOE_FMT_NVFP4, dims, moe_combine,
 
 
 # Up to this many tokens the decode GEMVs are the faster expert FFN; above,
-# the grouped GEMM (32-row expert tiles) is (measured at H 2560, I 640, E 512,
-# k 10: 206 vs 230 us per layer step at 32 tokens, 127 vs 131 us at 16 for
-# the fused decode layer).  Both give the same result up to fp32 order.
-DECODE_FFN_MAX_T = 16
+# the grouped GEMM (32-row expert tiles) is (measured layer steps at H 2560,
+# I 640, E 512, k 10: 100 vs 105 us at 12 tokens, 127 vs 117 us at 16, 218 vs
+# 178 us at 32).  Both give the same result up to fp32 order.
+DECODE_FFN_MAX_T = 12
 
 class Layer:
     def __init__(self, E: int, H: int, I: int, k: int, fmt_gate_up: int = MOE_FMT_NVFP4,
