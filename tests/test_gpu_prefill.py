@@ -103,15 +103,16 @@ def test_prefill_mid_tiles_skewed():
     assert np.array_equal(g2["out"][ok], g["out"][ok])
 
 
-@pytest.mark.parametrize("T", [128, 4915])
+@pytest.mark.parametrize("T", [1, 128, 4915])
 def test_prefill_flash_next_mid_sampled(T):
-    """Flash-Next shapes on the 32-row tiling (4915 tokens: the largest T it
-    takes at k = 10, E = 512): sampled tokens through every stage."""
+    """Flash-Next shapes on the 32-row tiling (one token: gate/up split over K
+    in four; 4915 tokens: the largest T it takes at k = 10, E = 512): sampled
+    tokens through every stage."""
     c = case("decode", "device")
     assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 32
     x = synth.activations(synth.WORKLOADS["decode_b8"], T=T, stream=900 + T)
     g = run_layer(c, x, residual=True, prefill=True)
-    say(f"prefill mid T={T}", check_stages(c, x, g, residual=True, check_tokens=[0, T // 2, T - 1]))
+    say(f"prefill mid T={T}", check_stages(c, x, g, residual=True, check_tokens=sorted({0, T // 2, T - 1})))
 
 
 @pytest.mark.parametrize("T,rows", [(40, 32), (800, 128)])
