@@ -10,12 +10,14 @@
 //   permute   stable counting sort of the (t, slot) pairs by expert, plus the
 //             per-expert count of BM-row tiles (prefix in tile_prefix) and one
 //             record per tile {expert, first row, end row} (tile_map)
-//   gate/up   per (expert, row tile, column tile; 256 x 256 when the shapes
-//             allow, else 128 x 128): rows are the expert's
+//   gate/up   per (expert, row tile, column tile): rows are the expert's
 //             pairs (x^ rows gathered through perm), cols 64-row packed weight
-//             tiles (32 gate rows + the same 32 up rows).  Operands are
-//             dequantized into LDS as f16 (E2M1 x E4M3 is exact in f16, so is a
-//             codebook entry) and multiplied with v_mfma_f32_32x32x16_f16 in fp32.
+//             tiles (32 gate rows + the same 32 up rows), multiplied with
+//             v_mfma_f32_32x32x16_f16 in fp32 on operands dequantized to f16
+//             (E2M1 x E4M3 is exact in f16, so is a codebook entry).  Few rows
+//             per expert: 32-row tiles, one wave per tile pair, operands
+//             straight to registers (K split at a handful of rows); else
+//             256 x 256 (or 128 x 128) block tiles staged through LDS.
 //             Epilogue: h = SiLU(g ts_x ts_g) * (u ts_x ts_u), fp32, sorted order.
 //   h quant   NVFP4 of each h row (one tensor scale per (t, slot) row)
 //   down      same GEMM on h^ rows; epilogue scales by ts_h ts_down and
