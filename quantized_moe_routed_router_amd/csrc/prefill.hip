@@ -32,12 +32,13 @@ namespace moe {
 constexpr int BM = 128, BN = 128, BK = 64, LDSK = BK + 8;   // +8 halves: bank spread
 constexpr int PF_THREADS = 256;
 // Up to SPLIT_MAX_N (token, slot) rows (SPLIT_MAX_N_NVFP4 for NVFP4 gate/up)
-// the 32-row gate/up waves take a 1/ksplit share of K each (ksplit <=
-// SPLIT_K_MAX): few expert tiles exist there, and a wave walking all of K
-// alone is VALU- (codebook) or latency- (NVFP4, at a handful of rows) bound.
-// Measured: codebook layer step 97 -> 56 us at 1 token, 224 -> 214 us at 16;
-// NVFP4 71 -> 50 us at 1 token but slower from 4 tokens (partials round trip).
-constexpr int SPLIT_MAX_N = 256, SPLIT_MAX_N_NVFP4 = 16, SPLIT_K_MAX = 4;
+// ksplit waves of one block (ksplit <= SPLIT_K_MAX) share each 32-row gate/up
+// item, each taking 1/ksplit of K, and sum their accumulators in LDS: few
+// expert tiles exist there, and a wave walking all of K alone is VALU-
+// (codebook) or latency- (NVFP4, at a handful of rows) bound.  Measured layer
+// step: codebook 97 -> 51 us at 1 token; NVFP4 71 -> 44 us at 1 token and
+// 67 -> 65 us at 4, slower from 8 tokens (the split waves' registers).
+constexpr int SPLIT_MAX_N = 256, SPLIT_MAX_N_NVFP4 = 40, SPLIT_K_MAX = 4;
 
 struct PrefillWs {
   int32_t* perm_ws;
@@ -51,7 +52,6 @@ struct PrefillWs {
   uint8_t* hq_codes;
   uint8_t* hq_scales;
   float* hq_ts;
-  float* part;           // split-K gate/up partials [ksplit][N][2][I] (small N only)
 };
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -73,7 +73,6 @@ static PrefillWs carve(void* ws, int E, int I, int k, int T, size_t* total) {
   w.hq_codes = take(N * I / 2);
   w.hq_scales = take(N * I / 16);
   w.hq_ts = (float*)take(N * 4);
-  w.part = (float*)take(N <= SPLIT_MAX_N ? (size_t)SPLIT_K_MAX * N * 2 * I * 4 : 0);
   if (total) *total = off;
   return w;
 }
@@ -642,18 +641,22 @@ __device__ __forceinline__ half8_t cat8(half2_t a, half2_t b, half2_t c, half2_t
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// MODE 0: gate/up NVFP4, 1: gate/up codebook, 2: down.  KS: K split (gate/up
-// at small N, partial g and u to w.part), else 1.  The codebook mode is held
+// MODE 0: gate/up NVFP4, 1: gate/up codebook, 2: down.  KS: waves per item,
+// each on 1/KS of K (gate/up at small N), else 1.  The codebook mode is held
 // to 168 VGPRs (three waves per SIMD; a few spilled registers): 4-5 % faster
 // at 16 and 1024 tokens than at 252 VGPRs and two waves.
 template <int MODE, int KS>
 __global__ __launch_bounds__(64 * MWAVES, MODE == 1 ? 3 : 1) void grouped_gemm_mid_kernel(FfnArgs a, PrefillWs w, int n_ptiles) {
   constexpr int ksplit = KS;
+  constexpr int IPB = MWAVES / KS;                 // items per block; KS waves per item
   constexpr bool down = MODE == 2;
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * MWAVES + (threadIdx.x >> 6);
-  if (item >= w.tile_prefix[a.E] * n_ptiles * ksplit) return;
-  const int ks = item % ksplit, tp = item / ksplit;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int slot = wv / KS, ks = wv % KS;
+  const int total_items = w.tile_prefix[a.E] * n_ptiles;
+  if ((int)blockIdx.x * IPB >= total_items) return;               // whole block idle
+  const int item = blockIdx.x * IPB + slot;
+  const bool valid = item < total_items;
+  const int tp = valid ? item : blockIdx.x * IPB;                 // idle waves shadow slot 0
   const int gm = tp / n_ptiles, p = tp % n_ptiles;
   const int4 tr = reinterpret_cast<const int4*>(w.tile_map)[gm];   // {expert, first row, end row}
   const int e = tr.x, row0 = tr.y, row_end = tr.z;
@@ -746,6 +749,24 @@ __global__ __launch_bounds__(64 * MWAVES, MODE == 1 ? 3 : 1) void grouped_gemm_m
   step(o0);
   step(o1);
 
+  if (KS > 1) {                                    // sum the K shares in LDS, share order
+    __shared__ float red[KS > 1 ? (KS - 1) * IPB : 1][32][64];
+    if (ks > 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) red[(ks - 1) * IPB + slot][j * 16 + q][lane] = acc[j][q];
+    }
+    __syncthreads();
+    if (ks > 0) return;
+#pragma unroll
+    for (int k2 = 1; k2 < KS; ++k2)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[j][q] += red[(k2 - 1) * IPB + slot][j * 16 + q][lane];
+  }
+  if (!valid) return;
   // acc[j][q]: tile row (q%4) + 8*(q/4) + 4*hf, column r of sub-tile j
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
@@ -756,13 +777,7 @@ __global__ __launch_bounds__(64 * MWAVES, MODE == 1 ? 3 : 1) void grouped_gemm_m
     if (!down) {
       const float g = acc[0][q] * (sc * (MODE == 0 ? a.ts_gate[e] : 1.0f));
       const float u = acc[1][q] * (sc * (MODE == 0 ? a.ts_up[e] : 1.0f));
-      if (KS == 1) {
-        w.h[(size_t)(row0 + rl) * a.I + p * 32 + r] = silu_mul(g, u);
-      } else {                                       // partial g, u; summed by h_quant_kernel
-        float* pr2 = w.part + ((size_t)ks * a.T * a.k + row0 + rl) * 2 * a.I + p * 32 + r;
-        pr2[0] = g;
-        pr2[a.I] = u;
-      }
+      w.h[(size_t)(row0 + rl) * a.I + p * 32 + r] = silu_mul(g, u);
     } else {
       const float tsd = a.ts_down[e];
 #pragma unroll
@@ -776,10 +791,7 @@ __global__ __launch_bounds__(64 * MWAVES, MODE == 1 ? 3 : 1) void grouped_gemm_m
 // amax is a wave max of the block maxima; also the optional debug copies in
 // (t, slot) order.  I <= 64 * HQ_MAXB * 16.
 constexpr int HQ_MAXB = 4;
-// KS > 1: h is formed here from the split-K gate/up partials.
-template <int KS>
 __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, int N) {
-  constexpr int ksplit = KS;
   const int lane = threadIdx.x & 63;
   const int pos = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pos >= N) return;
@@ -792,34 +804,14 @@ __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, in
   const float* hr = w.h + (size_t)pos * I;
   const int pair = w.perm[pos];
   float v[HQ_MAXB][16];
-  if (KS == 1) {
 #pragma unroll
-    for (int j = 0; j < HQ_MAXB; ++j) {
-      const int b = min(lane + 64 * j, nblk - 1);        // clamped: straight-line loads
-      const float4_t* src = reinterpret_cast<const float4_t*>(hr + b * 16);
+  for (int j = 0; j < HQ_MAXB; ++j) {
+    const int b = min(lane + 64 * j, nblk - 1);          // clamped: straight-line loads
+    const float4_t* src = reinterpret_cast<const float4_t*>(hr + b * 16);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float4_t f = src[r];
-        v[j][4 * r] = f.x; v[j][4 * r + 1] = f.y; v[j][4 * r + 2] = f.z; v[j][4 * r + 3] = f.w;
-      }
-    }
-  } else {
-    // split-K gate/up: h = SiLU(sum of g partials) * (sum of u partials), in split order
-#pragma unroll
-    for (int j = 0; j < HQ_MAXB; ++j) {
-      const int b = min(lane + 64 * j, nblk - 1);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float4_t g = {0.0f, 0.0f, 0.0f, 0.0f}, u = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const float* src = w.part + ((size_t)ks * N + pos) * 2 * I + b * 16 + 4 * r;
-          g += *reinterpret_cast<const float4_t*>(src);
-          u += *reinterpret_cast<const float4_t*>(src + I);
-        }
-        v[j][4 * r] = silu_mul(g.x, u.x); v[j][4 * r + 1] = silu_mul(g.y, u.y);
-        v[j][4 * r + 2] = silu_mul(g.z, u.z); v[j][4 * r + 3] = silu_mul(g.w, u.w);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const float4_t f = src[r];
+      v[j][4 * r] = f.x; v[j][4 * r + 1] = f.y; v[j][4 * r + 2] = f.z; v[j][4 * r + 3] = f.w;
     }
   }
   float amax = 0.0f;
@@ -883,7 +875,7 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
     const int S_gu = a.H / 64;                       // gate/up K steps
     const int split_max = a.fmt == FMT_CB3G128 ? SPLIT_MAX_N : SPLIT_MAX_N_NVFP4;
     const int ksplit = N > split_max ? 1 : S_gu % (2 * SPLIT_K_MAX) == 0 ? SPLIT_K_MAX : S_gu % 4 == 0 ? 2 : 1;
-    const unsigned g_gu = (unsigned)((max_mtiles * np_gu * ksplit + MWAVES - 1) / MWAVES);
+    const unsigned g_gu = (unsigned)((max_mtiles * np_gu * ksplit + MWAVES - 1) / MWAVES);   // KS waves per item
     const bool cb = a.fmt == FMT_CB3G128;
     if (ksplit == 4) {
       if (cb) grouped_gemm_mid_kernel<1, 4><<<g_gu, 64 * MWAVES, 0, s>>>(a, w, np_gu);
@@ -895,9 +887,7 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
       if (cb) grouped_gemm_mid_kernel<1, 1><<<g_gu, 64 * MWAVES, 0, s>>>(a, w, np_gu);
       else grouped_gemm_mid_kernel<0, 1><<<g_gu, 64 * MWAVES, 0, s>>>(a, w, np_gu);
     }
-    if (ksplit == 4) h_quant_kernel<4><<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
-    else if (ksplit == 2) h_quant_kernel<2><<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
-    else h_quant_kernel<1><<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
+    h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
     grouped_gemm_mid_kernel<2, 1><<<(max_mtiles * np_dn + MWAVES - 1) / MWAVES, 64 * MWAVES, 0, s>>>(a, w, np_dn);
     return hipGetLastError();
   }
@@ -911,7 +901,7 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
       grouped_gemm_big_kernel<1><<<max_mtiles * nt_gu, BTHREADS, 0, s>>>(a, w, nt_gu);
     else
       grouped_gemm_big_kernel<0><<<max_mtiles * nt_gu, BTHREADS, 0, s>>>(a, w, nt_gu);
-    h_quant_kernel<1><<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
+    h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
     const int nt_dn = a.H / BB;
     grouped_gemm_big_kernel<2><<<max_mtiles * nt_dn, BTHREADS, 0, s>>>(a, w, nt_dn);
     return hipGetLastError();
@@ -925,7 +915,7 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
     grouped_gemm_kernel<1><<<max_mtiles * nt_gu, PF_THREADS, 0, s>>>(a, w, nt_gu);
   else
     grouped_gemm_kernel<0><<<max_mtiles * nt_gu, PF_THREADS, 0, s>>>(a, w, nt_gu);
-  h_quant_kernel<1><<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
+  h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
   const int nt_dn = a.H / BN;
   grouped_gemm_kernel<2><<<max_mtiles * nt_dn, PF_THREADS, 0, s>>>(a, w, nt_dn);
   return hipGetLastError();
