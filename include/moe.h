@@ -164,7 +164,7 @@ int moe_expert_ffn_prefill(const moe_dims* dims, const moe_experts* experts,
 
 /* Row-tile height of the grouped GEMMs moe_expert_ffn_prefill runs for these
  * dims at T tokens (a host-side query, no device work): 32 while the experts
- * hold few rows on average (T*k <= 96*E, 32*E for codebook gate/up: one wave per
+ * hold few rows on average (T*k <= 96*E, 64*E for codebook gate/up: one wave per
  * 32-row expert tile and 64-row weight tile, operands straight to the matrix
  * cores, each expert tile's weights read once), else 256 where the shapes
  * allow 256 x 256 tiles (H % 256 == 0, I >= 256), else 128.  All three give

@@ -624,7 +624,7 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 // and its row's eight fp16 entries instead.  K % 128 == 0 (even step count).
 constexpr int MB = 32, MWAVES = 4;
 constexpr int MID_MAX_AVG_ROWS = 96;   // 32-row tiles while T*k <= this * E
-constexpr int MID_MAX_AVG_ROWS_CB = 32;   // the same for codebook gate/up (VALU-heavier decode:
+constexpr int MID_MAX_AVG_ROWS_CB = 64;   // the same for codebook gate/up (VALU-heavier decode:
                                           // it repays the big tiles' reuse sooner)
 
 struct MidRegs {

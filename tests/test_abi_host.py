@@ -50,8 +50,8 @@ def test_prefill_tile_rows_rule():
     assert m.moe_ffn_prefill_tile_rows(fn, 65536) == 256
     cb = m.dims(512, 2560, 640, 10, m.MOE_FMT_CB3G128)
     assert m.moe_ffn_prefill_tile_rows(cb, 1) == 32
-    assert m.moe_ffn_prefill_tile_rows(cb, 1638) == 32         # 16380 pairs <= 32 * 512
-    assert m.moe_ffn_prefill_tile_rows(cb, 1639) == 256
+    assert m.moe_ffn_prefill_tile_rows(cb, 3276) == 32         # 32760 pairs <= 64 * 512
+    assert m.moe_ffn_prefill_tile_rows(cb, 3277) == 256
     tiny = m.dims(16, 256, 128, 2)
     assert m.moe_ffn_prefill_tile_rows(tiny, 768) == 32
     assert m.moe_ffn_prefill_tile_rows(tiny, 769) == 128       # I = 128 < 256: 128-row tiles

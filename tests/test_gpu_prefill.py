@@ -125,11 +125,11 @@ def test_prefill_codebook_tiny(T, rows):
                                                  check_tokens=None if T <= 40 else range(0, T, 5)))
 
 
-@pytest.mark.parametrize("T", [1, 128])
+@pytest.mark.parametrize("T", [1, 128, 3276])
 def test_prefill_codebook_flash_next_mid(T):
     """Codebook gate/up at Flash-Next shapes on the 32-row tiles (the only
-    expert FFN that takes this format at small T): every stage on sampled
-    tokens."""
+    expert FFN that takes this format at small T; 3276 tokens is the largest
+    T on them): every stage on sampled tokens."""
     c = case("decode", "device", moe.MOE_FMT_CB3G128)
     assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 32
     x = synth.activations(synth.WORKLOADS["decode_b8"], T=T, stream=950 + T)
