@@ -447,11 +447,12 @@ def main():
     ap.add_argument("--crossover-t", type=str, default=None,
                     help="comma-separated token counts for --crossover")
     ap.add_argument("--crossover", action="store_true",
-                    help="only the small-batch table: decode GEMV path vs grouped-MFMA path, T = 1..256")
+                    help="only the small-batch table: decode GEMV paths vs the grouped-MFMA path, "
+                         "T = 1..1024 (or --crossover-t)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(see DESIGN.md for how it would shard)", file=sys.stderr)
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} asked): the layer has no "
+              "multi-GPU path; run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
