@@ -12,7 +12,8 @@ ones:
         NaN; no infinities; largest finite 448 (0x7E).
 
 Encoders round to nearest with ties to the even code and saturate at the
-largest finite value (readings listed in the design doc).  Test infrastructure only.
+largest finite value (a reading: the pages give the formats, not their rounding).
+Test infrastructure only.
 """
 from __future__ import annotations
 

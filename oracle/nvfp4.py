@@ -7,7 +7,7 @@ Format (public NVFP4 definition; the pages name it in the release post
   one block scale per 16 consecutive elements along the contraction axis.
 
 Quantizer Q(v; scope), every step an fp32 IEEE operation rounded to nearest
-even, in this order (reading):
+even, in this order (a reading: the pages name the format, not these steps):
   1. amax = max |v| over the tensor-scale scope (a whole weight matrix, one
      token row of x, one (token, slot) row of h);
   2. ts = amax / 2688   (2688 = 6 * 448, the largest E2M1 times the largest
