@@ -789,8 +789,11 @@ __global__ __launch_bounds__(64 * MWAVES, MODE == 1 ? 3 : 1) void grouped_gemm_m
 // NVFP4 of each h row (sorted order), one wave per row, one pass: lane l
 // holds the row's 16-element blocks l, l+64, ... (all loads first), the row
 // amax is a wave max of the block maxima; also the optional debug copies in
-// (t, slot) order.  I <= 64 * HQ_MAXB * 16.
+// (t, slot) order.  I <= 64 * HQ_MAXB * 16; NB = blocks per lane, the
+// fewest that cover the row (one up to I = 1024), so no lane holds or loads
+// more than it quantizes.
 constexpr int HQ_MAXB = 4;
+template <int NB>
 __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, int N) {
   const int lane = threadIdx.x & 63;
   const int pos = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -803,9 +806,9 @@ __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, in
   const int I = a.I, nblk = I / 16;
   const float* hr = w.h + (size_t)pos * I;
   const int pair = w.perm[pos];
-  float v[HQ_MAXB][16];
+  float v[NB][16];
 #pragma unroll
-  for (int j = 0; j < HQ_MAXB; ++j) {
+  for (int j = 0; j < NB; ++j) {
     const int b = min(lane + 64 * j, nblk - 1);          // clamped: straight-line loads
     const float4_t* src = reinterpret_cast<const float4_t*>(hr + b * 16);
 #pragma unroll
@@ -816,7 +819,7 @@ __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, in
   }
   float amax = 0.0f;
 #pragma unroll
-  for (int j = 0; j < HQ_MAXB; ++j)
+  for (int j = 0; j < NB; ++j)
     if (lane + 64 * j < nblk) {
 #pragma unroll
       for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(v[j][c]));
@@ -825,7 +828,7 @@ __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, in
   // static mode: the row's expert's calibrated scale
   const float ts = a.h_ts ? a.h_ts[a.ids[pair]] : tensor_scale_from_amax(amax);
 #pragma unroll
-  for (int j = 0; j < HQ_MAXB; ++j) {
+  for (int j = 0; j < NB; ++j) {
     const int b = lane + 64 * j;
     if (b >= nblk) continue;
     uint32_t pk[2];
@@ -843,6 +846,15 @@ __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, in
     w.hq_ts[pos] = ts;
     if (a.dbg_h_ts) a.dbg_h_ts[pair] = ts;
   }
+}
+
+static void launch_h_quant(const FfnArgs& a, const PrefillWs& w, int N, hipStream_t s) {
+  const int nb = (a.I / 16 + 63) / 64;                   // 1..HQ_MAXB (I <= 4096)
+  const unsigned g = (unsigned)((N + 3) / 4);
+  if (nb <= 1) h_quant_kernel<1><<<g, 256, 0, s>>>(a, w, N);
+  else if (nb == 2) h_quant_kernel<2><<<g, 256, 0, s>>>(a, w, N);
+  else if (nb == 3) h_quant_kernel<3><<<g, 256, 0, s>>>(a, w, N);
+  else h_quant_kernel<HQ_MAXB><<<g, 256, 0, s>>>(a, w, N);
 }
 
 static bool big_tiles_fit(const FfnArgs& a) {
@@ -887,7 +899,7 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
       if (cb) grouped_gemm_mid_kernel<1, 1><<<g_gu, 64 * MWAVES, 0, s>>>(a, w, np_gu);
       else grouped_gemm_mid_kernel<0, 1><<<g_gu, 64 * MWAVES, 0, s>>>(a, w, np_gu);
     }
-    h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
+    launch_h_quant(a, w, N, s);
     grouped_gemm_mid_kernel<2, 1><<<(max_mtiles * np_dn + MWAVES - 1) / MWAVES, 64 * MWAVES, 0, s>>>(a, w, np_dn);
     return hipGetLastError();
   }
@@ -901,7 +913,7 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
       grouped_gemm_big_kernel<1><<<max_mtiles * nt_gu, BTHREADS, 0, s>>>(a, w, nt_gu);
     else
       grouped_gemm_big_kernel<0><<<max_mtiles * nt_gu, BTHREADS, 0, s>>>(a, w, nt_gu);
-    h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
+    launch_h_quant(a, w, N, s);
     const int nt_dn = a.H / BB;
     grouped_gemm_big_kernel<2><<<max_mtiles * nt_dn, BTHREADS, 0, s>>>(a, w, nt_dn);
     return hipGetLastError();
@@ -915,7 +927,7 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
     grouped_gemm_kernel<1><<<max_mtiles * nt_gu, PF_THREADS, 0, s>>>(a, w, nt_gu);
   else
     grouped_gemm_kernel<0><<<max_mtiles * nt_gu, PF_THREADS, 0, s>>>(a, w, nt_gu);
-  h_quant_kernel<<<(N + 3) / 4, 256, 0, s>>>(a, w, N);
+  launch_h_quant(a, w, N, s);
   const int nt_dn = a.H / BN;
   grouped_gemm_kernel<2><<<max_mtiles * nt_dn, PF_THREADS, 0, s>>>(a, w, nt_dn);
   return hipGetLastError();

@@ -85,6 +85,10 @@ WORKLOADS = {
     # decode path with a K-split gate/up and a separate h^ step.
     "wide4k": Workload("wide4k", H=4096, I=256, E=16, k=4, T=1, seed=5),
     "wide10k": Workload("wide10k", H=10240, I=128, E=8, k=2, T=1, seed=6),
+    # Wide intermediate size (I = 1152: 72 NVFP4 blocks per h row, more than
+    # one per lane of a wave) on few experts.
+    "wide_i": Workload("wide_i", H=256, I=1152, E=8, k=2, T=4,
+                       router_std=0.05, expert_std=0.02, seed=9),
     # 8192-token prefill with a Zipf(1.1) router bias.
     "prefill8k": Workload("prefill8k", H=2560, I=640, E=512, k=10, T=8192,
                           zipf_s=1.1, seed=3),

@@ -115,6 +115,19 @@ def test_prefill_flash_next_mid_sampled(T):
     say(f"prefill mid T={T}", check_stages(c, x, g, residual=True, check_tokens=sorted({0, T // 2, T - 1})))
 
 
+@pytest.mark.parametrize("T,rows", [(4, 32), (300, 32), (500, 256)])
+def test_prefill_wide_intermediate(T, rows):
+    """I = 1152: each h row has 72 NVFP4 blocks, so the h quantization's lanes
+    hold two blocks each; on the 32-row tiles (split K at 4 tokens) and the
+    256-row tiles."""
+    c = case("wide_i", "host")
+    assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == rows
+    x = synth.activations(c.wl, T=T, stream=40 + T)
+    g = run_layer(c, x, prefill=True, residual=True)
+    say("prefill wide I", T, check_stages(c, x, g, residual=True,
+                                          check_tokens=None if T <= 4 else range(0, T, 9)))
+
+
 @pytest.mark.parametrize("T,rows", [(40, 32), (800, 128)])
 def test_prefill_codebook_tiny(T, rows):
     c = case("tiny", "host", moe.MOE_FMT_CB3G128)
