@@ -183,6 +183,113 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   }
 }
 
+// Large T (>= RM256_MIN_T): the same GEMM on 256-token x 128-expert tiles, 512
+// threads (4 x 2 waves of 64 x 64).  Splitting W into its three bf16 parts is
+// VALU work per block; twice the tokens per W tile halve it per token (router
+// 0.70 -> ~0.5 ms at 65,536 tokens; below 16k tokens the halved block count
+// costs more).
+
+__global__ __launch_bounds__(512) void router_mfma256_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ W,
+                                                          const float* __restrict__ bias, int T,
+                                                          int E, int H,
+                                                          float* __restrict__ logits) {
+  __shared__ __align__(16) uint16_t As[2 * RG_BM][RG_LDK];
+  __shared__ __align__(16) uint16_t Bs[3][RG_BN][RG_LDK];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int t0 = blockIdx.x * (2 * RG_BM), e0 = blockIdx.y * RG_BN;
+  // staging roles: x row r (of 256), K half hf (32 elements); W row rb (of
+  // 128), K quarter qb (16 elements)
+  const int r = tid >> 1, hf = tid & 1, rb = tid >> 2, qb = tid & 3;
+  const bool tv = t0 + r < T, ev = e0 + rb < E;
+  const uint16_t* xr = x + (size_t)(tv ? t0 + r : 0) * H + 32 * hf;    // clamped: always valid
+  const float* wr = W + (size_t)(ev ? e0 + rb : 0) * H + 16 * qb;
+  u32x4 xa[4];
+  float4_t wa[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const u32x4*>(xr + 8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wa[i] = *reinterpret_cast<const float4_t*>(wr + 4 * i);
+
+  float16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  for (int k0 = 0; k0 < H; k0 += RG_BK) {
+    // ---- stage: x as is, W split into three bf16 parts
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(&As[r][32 * hf + 8 * i]) = tv ? xa[i] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      uint32_t p[3][4];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float wf = ev ? wa[i + (c >> 2)][c & 3] : 0.0f;
+        const uint32_t hi = bf16_bits_rne(wf);
+        const float r1 = wf - __uint_as_float(hi << 16);
+        const uint32_t mid = bf16_bits_rne(r1);
+        const float r2 = r1 - __uint_as_float(mid << 16);
+        const uint32_t lo = bf16_bits_rne(r2);
+        const int wd = c >> 1, sh = (c & 1) * 16;
+        if (!(c & 1)) { p[0][wd] = hi; p[1][wd] = mid; p[2][wd] = lo; }
+        else { p[0][wd] |= hi << sh; p[1][wd] |= mid << sh; p[2][wd] |= lo << sh; }
+      }
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        *reinterpret_cast<u32x4*>(&Bs[q][rb][16 * qb + 4 * i]) = u32x4{p[q][0], p[q][1], p[q][2], p[q][3]};
+    }
+    __syncthreads();
+    // ---- next step's loads in flight during this step's MFMAs
+    if (k0 + RG_BK < H) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const u32x4*>(xr + k0 + RG_BK + 8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wa[i] = *reinterpret_cast<const float4_t*>(wr + k0 + RG_BK + 4 * i);
+    }
+#pragma unroll
+    for (int kk = 0; kk < RG_BK; kk += 16) {
+      bf16x8_t af[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&As[wm * 64 + i * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int q = 2; q >= 0; --q) {                 // lo, mid, hi
+        bf16x8_t bq[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bq[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[q][wn * 64 + j * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bq[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // ---- epilogue: acc[i][j][q] is row wm*64 + i*32 + (q%4) + 8(q/4) + 4(lane/32),
+  // column wn*64 + j*32 + lane%32 of the tile
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + wn * 64 + j * 32 + (lane & 31);
+    if (e >= E) continue;
+    const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int t = t0 + wm * 64 + i * 32 + (q & 3) + 8 * (q >> 2) + 4 * (lane >> 5);
+        if (t < T) logits[(size_t)t * E + e] = acc[i][j][q] + b;
+      }
+  }
+}
+
 // Mid token counts (tens to a few thousand tokens): the 128 x 128 tiles above
 // leave most of the chip idle (4 blocks at 128 tokens) and walk H in a serial
 // chain of staged steps.  Here one block of eight waves owns a 32-token x
@@ -194,7 +301,8 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
 // (deterministic) and the bias added once.
 constexpr int RS_WAVES = 8, RS_NB = 4;
 constexpr int RS16_MAX_T = 128;         // 16 x 16 tiles up to here (below)
-constexpr int RS_MAX_T = 2560;          // above: the 128 x 128 tiles (enough blocks, less re-reading)
+constexpr int RS_MAX_T = 2560;
+constexpr int RM256_MIN_T = 16384;      // 256-token tiles from here (fewer blocks below it)          // above: the 128 x 128 tiles (enough blocks, less re-reading)
 
 __global__ __launch_bounds__(64 * RS_WAVES) void router_splitk_kernel(const uint16_t* __restrict__ x,
                                                                       const float* __restrict__ W,
@@ -392,6 +500,8 @@ hipError_t launch_router(const uint16_t* x, const float* W_r, const float* bias,
     router_splitk16_kernel<<<dim3((T + 15) / 16, (E + 15) / 16), 64 * RS_WAVES, 0, s>>>(x, W_r, bias, T, E, H, logits);
   } else if (T <= RS_MAX_T && H % 128 == 0) {
     router_splitk_kernel<<<dim3((T + 31) / 32, (E + 31) / 32), 64 * RS_WAVES, 0, s>>>(x, W_r, bias, T, E, H, logits);
+  } else if (H % RG_BK == 0 && T >= RM256_MIN_T) {
+    router_mfma256_kernel<<<dim3((T + 2 * RG_BM - 1) / (2 * RG_BM), (E + RG_BN - 1) / RG_BN), 512, 0, s>>>(x, W_r, bias, T, E, H, logits);
   } else if (H % RG_BK == 0) {
     router_mfma_kernel<<<dim3((T + RG_BM - 1) / RG_BM, (E + RG_BN - 1) / RG_BN), 256, 0, s>>>(x, W_r, bias, T, E, H, logits);
   } else {

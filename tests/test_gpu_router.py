@@ -51,7 +51,8 @@ def check_router(xbits, W, bias, k):
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("decode", 1), ("decode_b8", 8), ("decode", 16),
-                                    ("decode", 17), ("decode", 200), ("decode", 1100), ("decode", 2600)])
+                                    ("decode", 17), ("decode", 200), ("decode", 1100), ("decode", 2600),
+                                    ("decode", 16400)])
 def test_router_parity(name, T):
     say("router", name, T)
     wl = synth.WORKLOADS[name]
@@ -62,12 +63,13 @@ def test_router_parity(name, T):
 
 def test_router_ragged_tiles():
     """Token and expert counts off the tiles of every router kernel (16 x 16
-    up to 128 tokens, 32 x 32 up to 2560, 128 x 128 above), with a bias."""
+    up to 128 tokens, 32 x 32 up to 2560, 128 x 128 up to 16383, 256 x 128
+    above), with a bias."""
     r = np.random.default_rng(4)
     H, E, k = 384, 50, 3
     W = (r.standard_normal((E, H)) * 0.05).astype(np.float32)
     bias = (r.standard_normal(E) * 0.01).astype(np.float32)
-    for T in (45, 1030, 2600):
+    for T in (45, 1030, 2600, 16400):
         say("router ragged", T)
         x = synth.f32_to_bf16_bits(r.standard_normal((T, H)).astype(np.float32))
         check_router(x, W, bias, k)
