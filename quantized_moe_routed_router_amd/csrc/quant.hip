@@ -16,20 +16,23 @@ namespace moe {
 // One 256-thread block per row: every thread loads its 16-element blocks once,
 // the row amax goes through DPP + LDS, then each thread quantizes its blocks
 // (32 B of bf16 in, 8 B codes + 1 B scale out, coalesced across the block).
+// One wave per token row, four rows per block: many rows in flight per CU
+// (one 256-thread block per row left most of a 2560-wide row's threads idle
+// and few rows in flight).
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x, int T,
                                                         int H, uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales,
                                                         float* __restrict__ ts_out) {
-  __shared__ float red[4];
-  const int row = blockIdx.x;
-  quantize_row_bf16_block(x + (size_t)row * H, H, codes + (size_t)row * (H / 2),
-                          scales + (size_t)row * (H / 16), ts_out + row, threadIdx.x, 256, red);
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= T) return;
+  quantize_row_bf16_wave(x + (size_t)row * H, H, codes + (size_t)row * (H / 2),
+                         scales + (size_t)row * (H / 16), ts_out + row, threadIdx.x & 63);
 }
 
 hipError_t launch_act_quant(const uint16_t* x, int T, int H, uint8_t* codes, uint8_t* scales,
                             float* ts, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  act_quant_kernel<<<T, 256, 0, s>>>(x, T, H, codes, scales, ts);
+  act_quant_kernel<<<(T + 3) / 4, 256, 0, s>>>(x, T, H, codes, scales, ts);
   return hipGetLastError();
 }
 
