@@ -799,8 +799,15 @@ __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, in
   const int pos = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pos >= N) return;
   if (pos >= w.offsets[a.E]) {                           // pair with an id outside [0, E):
-    const int pair = w.perm[pos];                        // its output row is zero
+    const int pair = w.perm[pos];                        // its output row is zero, and so
     for (int c = lane; c < a.H; c += 64) a.out[(size_t)pair * a.H + c] = 0.0f;
+    if (a.dbg_h)                                         // are its debug h and h^ (as in
+      for (int c = lane; c < a.I; c += 64) a.dbg_h[(size_t)pair * a.I + c] = 0.0f;   // the decode path)
+    if (a.dbg_h_codes)
+      for (int c = lane; c < a.I / 2; c += 64) a.dbg_h_codes[(size_t)pair * (a.I / 2) + c] = 0;
+    if (a.dbg_h_scales)
+      for (int c = lane; c < a.I / 16; c += 64) a.dbg_h_scales[(size_t)pair * (a.I / 16) + c] = 0;
+    if (a.dbg_h_ts && lane == 0) a.dbg_h_ts[pair] = 0.0f;
     return;
   }
   const int I = a.I, nblk = I / 16;

@@ -146,6 +146,51 @@ def case(name, source, fmt=moe.MOE_FMT_NVFP4):
     return _cases[key]
 
 
+# Sentinels written into every output buffer (and the workspace) before a
+# call: a row, tile or block a kernel skipped keeps its sentinel, which no
+# correct output holds (NaN floats, bf16 NaN 0xFFFF, an id outside any
+# layer's range, E4M3 scale byte 0xFF, which the quantizers never produce).
+SENT_ID = 0x7EADBEEF
+SENT_BF16 = -1                       # int16 view of 0xFFFF
+
+
+def fill_sentinels(b: dict, dbg: dict | None = None):
+    nan = float("nan")
+    for key in ("w", "x_ts", "out", "logits"):
+        if key in b:
+            b[key].fill_(nan)
+    if "ids" in b:
+        b["ids"].fill_(SENT_ID)
+    for key in ("x_codes", "x_scales", "ws"):
+        if key in b:
+            b[key].fill_(0xFF)
+    if "y" in b:
+        b["y"].fill_(SENT_BF16)
+    if dbg:
+        dbg["h"].fill_(nan)
+        dbg["h_ts"].fill_(nan)
+        dbg["h_codes"].fill_(0xFF)
+        dbg["h_scales"].fill_(0xFF)
+
+
+def assert_no_sentinels(g: dict, E: int):
+    """Every output element was written (g: host copies from run_layer)."""
+    ids = g["ids"]
+    assert not np.any(ids == SENT_ID), "ids not written"
+    assert not np.isnan(g["w"]).any(), "router weights not written"
+    assert not np.isnan(g["out"]).any(), "expert output rows not written"
+    assert not np.any(g["y"].view(np.uint16) == 0xFFFF), "y not written"
+    if "dbg_h" in g:
+        assert not np.isnan(g["dbg_h"]).any(), "debug h not written"
+        assert not np.isnan(g["dbg_h_ts"]).any(), "debug h^ tensor scales not written"
+        assert not np.any(g["dbg_h_scales"] == 0xFF), "debug h^ block scales not written"
+        bad = ~((ids >= 0) & (ids < E)).reshape(-1)
+        if bad.any():                 # pairs with an id outside [0, E): zero rows
+            assert not g["out"].reshape(-1, g["out"].shape[-1])[bad].any()
+            assert not g["dbg_h"][bad].any() and not g["dbg_h_codes"][bad].any()
+            assert not g["dbg_h_scales"][bad].any() and not g["dbg_h_ts"][bad].any()
+
+
 def run_layer(c: LayerCase, xbits: np.ndarray, residual=False, prefill=False, ids_override=None):
     T = xbits.shape[0]
     L = c.L
@@ -155,6 +200,7 @@ def run_layer(c: LayerCase, xbits: np.ndarray, residual=False, prefill=False, id
                h_codes=torch.empty((T * L.k, L.I // 2), dtype=torch.uint8, device=DEV),
                h_scales=torch.empty((T * L.k, L.I // 16), dtype=torch.uint8, device=DEV),
                h_ts=torch.empty(T * L.k, dtype=torch.float32, device=DEV))
+    fill_sentinels(b, dbg)
     if ids_override is None:
         L.forward(x, b, residual=residual, dbg=dbg)
     else:
@@ -166,8 +212,10 @@ def run_layer(c: LayerCase, xbits: np.ndarray, residual=False, prefill=False, id
             b["ws"], b["ws_bytes"], dbg)
         moe.moe_combine(b["out"], b["w"], x if residual else None, T, L.k, L.H, b["y"])
     torch.cuda.synchronize()
-    out = {k: t2n(v) for k, v in b.items() if isinstance(v, torch.Tensor)}
+    out = {k: t2n(v) for k, v in b.items() if isinstance(v, torch.Tensor) and k != "ws"}
     out.update({"dbg_" + k: t2n(v) for k, v in dbg.items()})
+    del b, dbg
+    assert_no_sentinels(out, L.E)
     return out
 
 
@@ -211,3 +259,72 @@ def check_stages(c: LayerCase, xbits, g, residual=False, check_tokens=None, h_ts
     return dict(rel_h=rel_h.max(), rel_o=rel_o.max(), flips=float((~same).mean()), rel_y=rel_y)
 
 
+
+
+def pick_experts(ids: np.ndarray, E: int, tile_rows: int) -> list:
+    """Experts whose every (t, slot) row is compared in the full-size prefill
+    tests: the one with the most rows (many row tiles), the ones whose last
+    row tile is the shortest and the fullest ragged tile, the lowest, middle
+    and highest active ids (their tiles sit in different XCDs' block ranges)
+    and, under skewed routing, a tail expert with one to three rows."""
+    counts = np.bincount(ids.reshape(-1), minlength=E)[:E]
+    act = np.nonzero(counts)[0]
+    chosen = {int(counts.argmax()), int(act.min()), int(act.max()), int(act[len(act) // 2])}
+    rem = counts % tile_rows
+    cand = act[(counts[act] > tile_rows) & (rem[act] > 0)]
+    if len(cand):
+        chosen.add(int(cand[np.argmin(rem[cand])]))
+        chosen.add(int(cand[np.argmax(rem[cand])]))
+    small = act[counts[act] <= 3]
+    if len(small):
+        chosen.add(int(small[0]))
+    return sorted(chosen)
+
+
+def check_pairs(c: LayerCase, xbits, g, pairs, h_ts=None):
+    """Stage-wise comparison on the (t, slot) pairs with flat index
+    t * k + slot in `pairs` (every pair must have a valid id): h against the
+    oracle on the device's ids (row-wise <= 1e-5), h^ bit-exact from the
+    device's h, o against the oracle's down projection of the device's h^
+    (row-wise <= 2e-3), and against the pure oracle on rows whose h^ agrees."""
+    k = c.L.k
+    pairs = np.asarray(pairs, dtype=np.int64)
+    e_sel = g["ids"].reshape(-1)[pairs]
+    assert np.all((e_sel >= 0) & (e_sel < c.wl.E))
+    toks = pairs // k
+    deq = c.oracle_deq(e_sel)
+    ids1 = e_sel.reshape(-1, 1)
+    xq = offn.quantize_act(xbits[toks])                       # one x^ row per pair
+    h_ref = offn.gate_up(deq, xq, ids1)[:, 0]
+    h_dev = g["dbg_h"][pairs]
+    rel_h = rowwise_rel(h_dev, h_ref)
+    assert rel_h.max() <= 1e-5, rel_h.max()
+    ts_rows = None if h_ts is None else np.asarray(h_ts, np.float32)[e_sel]
+    hc, hs, hts = offn.quantize_h(h_dev, ts_rows)
+    dc, ds, dts = g["dbg_h_codes"][pairs], g["dbg_h_scales"][pairs], g["dbg_h_ts"][pairs]
+    assert np.array_equal(dc, nvfp4.pack_nibbles(hc))
+    assert np.array_equal(ds, hs)
+    assert np.array_equal(dts.view(np.uint32), hts.astype(np.float32).view(np.uint32))
+    o_ref = offn.down(deq, (hc, hs, hts), ids1)[:, 0]
+    o_dev = g["out"].reshape(-1, c.L.H)[pairs]
+    rel_o = rowwise_rel(o_dev, o_ref)
+    assert rel_o.max() <= 2e-3, rel_o.max()
+    hq_pure = offn.quantize_h(h_ref, ts_rows)
+    o_pure = offn.down(deq, hq_pure, ids1)[:, 0]
+    same = np.all(nvfp4.pack_nibbles(hq_pure[0]) == dc, axis=1) & np.all(hq_pure[1] == hs, axis=1)
+    rel_p = rowwise_rel(o_dev, o_pure)
+    assert np.all(rel_p[same] <= 2e-3)
+    return dict(pairs=len(pairs), rel_h=float(rel_h.max()), rel_o=float(rel_o.max()),
+                flips=float((~same).mean()))
+
+
+def check_y_all(g, xbits, residual: bool, chunk: int = 2048) -> float:
+    """Every token's y against the oracle combine of the device's o and w:
+    one bf16 rounding of the fp32 slot-order sum."""
+    T = g["y"].shape[0]
+    worst = 0.0
+    for t0 in range(0, T, chunk):
+        sl = slice(t0, min(T, t0 + chunk))
+        y_ref = offn.combine(g["out"][sl], g["w"][sl], xbits[sl] if residual else None)
+        worst = max(worst, assert_bf16_rounding_of(g["y"][sl], y_ref))
+    return worst

@@ -109,11 +109,12 @@ def test_decode_flash_next_b1():
         say("decode b1 stages", check_stages(c, x, g))
 
 
-def test_decode_flash_next_b8_sampled():
+def test_decode_flash_next_b8():
+    """Eight tokens at Flash-Next shapes: every token through every stage."""
     c = case("decode", "device")
     x = synth.activations(synth.WORKLOADS["decode_b8"], T=8, stream=200)
     g = run_layer(c, x, residual=True)
-    say("decode b8 stages", check_stages(c, x, g, residual=True, check_tokens=[0, 5]))
+    say("decode b8 stages", check_stages(c, x, g, residual=True))
 
 
 @pytest.mark.parametrize("T", [32, 64])

@@ -7,9 +7,9 @@ import torch
 
 import synth
 import quantized_moe_routed_router_amd as moe
-from oracle import ffn as offn, router as orouter
-from tests.gpu_helpers import (say, t2n, bf16_tensor, rowwise_rel, assert_bf16_rounding_of,
-                               case, run_layer)
+from oracle import ffn as offn, nvfp4, router as orouter
+from tests.gpu_helpers import (say, t2n, bf16_tensor, rowwise_rel, bf16_half_ulp, case, run_layer,
+                               SENT_BF16)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -19,9 +19,13 @@ def fused(c, xbits, residual):
     L = c.L
     T = xbits.shape[0]
     fb = L.alloc_fused(T)
+    fb["y"].fill_(SENT_BF16)
+    fb["ws"].fill_(0xFF)
     L.forward_fused(bf16_tensor(xbits, DEV), fb, residual=residual)
     torch.cuda.synchronize()
-    return {k: t2n(v) for k, v in fb.items() if isinstance(v, torch.Tensor)}, fb
+    out = {k: t2n(v) for k, v in fb.items() if isinstance(v, torch.Tensor) and k != "ws"}
+    assert not np.any(out["y"].view(np.uint16) == 0xFFFF), "y not written"
+    return out, fb
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny", 4), ("tiny", 16), ("decode", 1),
@@ -40,22 +44,56 @@ def test_fused_equals_separate_path(name, T):
 
 
 def test_fused_vs_oracle_flash_next():
+    """The fused layer at Flash-Next shapes against the oracle, staged: the
+    separate entry points give the same y bit for bit and expose the device's
+    h^.  y = bf16(F) (no residual) or bf16(x + F), F = sum_i w_i o_i, must be
+    one round-to-nearest of the oracle's F on the device's h^ (slack 1e-5 of
+    max |F| for fp32 order), and of the pure oracle's F* with slack 2e-3 of
+    max |F*| (the expert output's budget, not max |y|, which the residual's
+    outliers dominate) whenever every slot's h^ agrees; an h^ code flip at a
+    rounding boundary moves F by about a percent of its largest element and
+    is reported instead.  (A bf16 rounding alone can be 2^-8 of an element,
+    so y itself is not held to 2e-3 row-wise.)"""
     c = case("decode", "device")
-    x = synth.activations(c.wl, T=1, stream=601)
-    f, _ = fused(c, x, True)
-    oids, ow, near, _, _ = orouter.route(x, c.W_r, c.wl.k)
-    assert near[0] or set(f["ids"][0]) == set(oids[0])
-    experts = {int(e): c.oracle_expert(int(e)) for e in f["ids"][0]}
-    xq = offn.quantize_act(x)
-    deq = {e: offn.dequant_expert(q) for e, q in experts.items()}
-    h = offn.gate_up(deq, xq, f["ids"])
-    o = offn.down(deq, offn.quantize_h(h), f["ids"])
-    y_ref = offn.combine(o, f["w"].astype(np.float64), x)
-    # the device's h^ may differ from the oracle's at a rounding boundary; the
-    # result stays within 2e-3 of the pure oracle row-wise
-    y = synth.bf16_bits_to_f32(f["y"].view(np.uint16)).astype(np.float64)
-    fr = rowwise_rel(y - synth.bf16_bits_to_f32(x).astype(np.float64), y_ref - synth.bf16_bits_to_f32(x).astype(np.float64))
-    assert_bf16_rounding_of(f["y"], y_ref, slack_rel=2e-3)
+    flips = 0
+    for stream in (601, 602, 603):
+        x = synth.activations(c.wl, T=1, stream=stream)
+        f, _ = fused(c, x, True)
+        f0, _ = fused(c, x, False)
+        g0 = run_layer(c, x, residual=False)
+        assert np.array_equal(f0["ids"], g0["ids"]) and np.array_equal(f0["y"], g0["y"])
+        oids, ow, near, _, _ = orouter.route(x, c.W_r, c.wl.k)
+        assert near[0] or set(f["ids"][0]) == set(oids[0])
+        ids = f["ids"]
+        deq = c.oracle_deq(ids)
+        w = f["w"].astype(np.float64)
+        hc = nvfp4.unpack_nibbles(g0["dbg_h_codes"])
+        o_tf = offn.down(deq, (hc, g0["dbg_h_scales"], g0["dbg_h_ts"]), ids)
+        F_tf = offn.combine(o_tf, w)
+        y0 = synth.bf16_bits_to_f32(f0["y"].view(np.uint16)).astype(np.float64)
+        fmax = np.abs(F_tf).max(axis=-1, keepdims=True)
+        assert np.all(np.abs(y0 - F_tf) <= bf16_half_ulp(F_tf) * (1 + 1e-6) + 1e-5 * fmax)
+        # with the residual: one rounding of x + F
+        x64 = synth.bf16_bits_to_f32(x).astype(np.float64)
+        y = synth.bf16_bits_to_f32(f["y"].view(np.uint16)).astype(np.float64)
+        bound = bf16_half_ulp(x64 + F_tf) * (1 + 1e-6) + 1e-5 * np.abs(F_tf).max(axis=-1, keepdims=True)
+        assert np.all(np.abs(y - (x64 + F_tf)) <= bound)
+        # the pure oracle (its own h and h^)
+        h = offn.gate_up(deq, offn.quantize_act(x), ids)
+        hq = offn.quantize_h(h)
+        same = np.array_equal(hq[0], hc) and np.array_equal(hq[1], g0["dbg_h_scales"])
+        F_pure = offn.combine(offn.down(deq, hq, ids), w)
+        fp = rowwise_rel(F_tf, F_pure)
+        say("fused flash-next: F on device h^ vs pure oracle F*", float(fp.max()),
+            "h^ agrees" if same else "h^ flip")
+        if same:
+            pmax = np.abs(F_pure).max(axis=-1, keepdims=True)
+            assert fp.max() <= 2e-3
+            assert np.all(np.abs(y0 - F_pure) <= bf16_half_ulp(F_pure) * (1 + 1e-6) + 2e-3 * pmax)
+            assert np.all(np.abs(y - (x64 + F_pure)) <= bf16_half_ulp(x64 + F_pure) * (1 + 1e-6) + 2e-3 * pmax)
+        else:
+            flips += 1
+    assert flips <= 1
 
 
 def test_fused_graph_replays_match_eager():

@@ -7,7 +7,8 @@ import torch
 import synth
 import quantized_moe_routed_router_amd as moe
 from oracle import ffn as offn, router as orouter
-from tests.gpu_helpers import (say, t2n, rowwise_rel, case, run_layer, check_stages)
+from tests.gpu_helpers import (say, t2n, rowwise_rel, case, run_layer, check_stages, check_pairs,
+                               check_y_all, pick_experts)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -151,25 +152,35 @@ def test_prefill_codebook_flash_next_mid(T):
                                                     check_tokens=sorted({0, T // 2, T - 1})))
 
 
-def test_prefill_zipf_8k_sampled():
-    """The 8192-token Zipf-routed layer at full size; oracle on sampled tokens
-    (one on the most popular expert, others spread)."""
-    c = case("decode", "device")
+@pytest.mark.parametrize("fmt", [moe.MOE_FMT_NVFP4, moe.MOE_FMT_CB3G128])
+def test_prefill_zipf_8k_full_rows(fmt):
+    """The 8192-token Zipf-routed layer at full size (256-row tiles for both
+    gate/up formats): every output element written (sentinels), every
+    (t, slot) row of the chosen experts (the most popular, the ragged last
+    tiles, low / middle / high ids, a tail expert) through all stages, y of
+    every token, and the router against the oracle on sampled tokens."""
+    c = case("decode", "device", fmt)
     wl = synth.WORKLOADS["prefill8k"]
     c.L.set_router(torch.from_numpy(synth.router_weights(wl)).to(DEV),
                    torch.from_numpy(synth.router_bias(wl)).to(DEV))
     try:
+        assert moe.moe_ffn_prefill_tile_rows(c.L.d, wl.T) == 256
         x = synth.activations(wl, T=wl.T)
-        g = run_layer(c, x, prefill=True)
+        g = run_layer(c, x, prefill=True, residual=True)
         counts = np.bincount(g["ids"].reshape(-1), minlength=wl.E)
         say("zipf top counts", np.sort(counts)[::-1][:5], "zero experts", int((counts == 0).sum()))
         assert counts.max() > 1000 and (counts == 0).sum() > 100
+        experts = pick_experts(g["ids"], wl.E, 256)
+        say("zipf experts", [(e, int(counts[e])) for e in experts])
+        for e in experts:
+            pairs = np.nonzero(g["ids"].reshape(-1) == e)[0]
+            say("zipf expert", e, check_pairs(c, x, g, pairs))
+        say("zipf y all tokens", check_y_all(g, x, residual=True))
         top = int(counts.argmax())
         t_top = int(np.nonzero((g["ids"] == top).any(1))[0][-1])
-        say("zipf stages", check_stages(c, x, g, check_tokens=[0, t_top, wl.T - 1]))
-        # router ids vs the oracle on the sampled tokens
-        oids, _, near, _, _ = orouter.route(x[[0, t_top]], synth.router_weights(wl), wl.k, synth.router_bias(wl))
-        for i, t in enumerate([0, t_top]):
+        toks = [0, t_top, wl.T - 1]
+        oids, _, near, _, _ = orouter.route(x[toks], synth.router_weights(wl), wl.k, synth.router_bias(wl))
+        for i, t in enumerate(toks):
             if not near[i]:
                 assert set(g["ids"][t]) == set(oids[i])
     finally:
@@ -177,19 +188,27 @@ def test_prefill_zipf_8k_sampled():
 
 
 @pytest.mark.parametrize("fmt", [moe.MOE_FMT_NVFP4, moe.MOE_FMT_CB3G128])
-def test_prefill_64k_sampled(fmt):
+def test_prefill_64k_full_rows(fmt):
     """65536 tokens with uniform routing at full size (the long-prefill
-    workload); oracle on two sampled tokens, properties on all rows."""
+    workload): every output element written (sentinels), every (t, slot) row
+    of the chosen experts through all stages (about 1,300 rows each over six
+    256-row tiles), y of every token."""
     c = case("decode", "device", fmt)
     wl = synth.WORKLOADS["prefill64k"]
     c.L.set_router(torch.from_numpy(synth.router_weights(wl)).to(DEV), None)
     try:
+        assert moe.moe_ffn_prefill_tile_rows(c.L.d, wl.T) == 256
         xt = synth.activations_torch(wl, wl.T, 0, DEV)
         xb = xt.view(torch.int16).cpu().numpy().view(np.uint16)
-        g = run_layer(c, xb, prefill=True)
-        assert np.isfinite(g["out"]).all()
+        del xt
+        g = run_layer(c, xb, prefill=True, residual=True)
         counts = np.bincount(g["ids"].reshape(-1), minlength=wl.E)
         assert counts.min() > 900 and counts.max() < 1700          # ~1280 each
-        say("64k stages", fmt, check_stages(c, xb, g, check_tokens=[12345, wl.T - 1]))
+        experts = pick_experts(g["ids"], wl.E, 256)
+        say("64k experts", fmt, [(e, int(counts[e])) for e in experts])
+        for e in experts:
+            pairs = np.nonzero(g["ids"].reshape(-1) == e)[0]
+            say("64k expert", e, check_pairs(c, xb, g, pairs))
+        say("64k y all tokens", check_y_all(g, xb, residual=True))
     finally:
         c.L.set_router(torch.from_numpy(c.W_r).to(DEV), None)
