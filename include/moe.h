@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 #define MOE_DECODE_MAX_T 64   /* largest token count moe_expert_ffn_decode takes */
 #define MOE_LAYER_MAX_T 16    /* largest token count moe_layer_decode takes */
 #define MOE_MAX_E 1024
@@ -187,6 +187,25 @@ int moe_layer_decode(const moe_dims* dims, const moe_experts* experts, const uin
                      const float* W_r, const float* bias, int T, int add_residual,
                      uint16_t* y, int32_t* ids, float* w, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* The fused decode layer without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, arithmetic and
+ * results as moe_layer_decode, whose kernels it runs; the workspace is a
+ * MOE_NOALLOC_SCRATCH_BYTES array in the library's device memory, one per
+ * GPU, held until the process ends (its address is looked up on the first
+ * call on each device, with that device current).  The call allocates and
+ * frees nothing.  Refused (MOE_ERR_WORKSPACE, with the numbers) when
+ * moe_layer_decode_workspace_bytes(dims, T) exceeds MOE_NOALLOC_SCRATCH_BYTES
+ * (the Flash-Next layer, H 2560, I 640, E 512, k 10, needs about 3.4 MB at
+ * T = 16).  Every call on a GPU uses that GPU's one array: calls that overlap
+ * on one GPU (other streams, other host threads) race and must be ordered by
+ * the caller.  The array's contents left by the last call are never read
+ * before being written.  The stream must belong to the current device. */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_layer_decode_noalloc(const moe_dims* dims, const moe_experts* experts, const uint16_t* x,
+                             const float* W_r, const float* bias, int T, int add_residual,
+                             uint16_t* y, int32_t* ids, float* w, void* stream);
 
 /* Weighted combine (release post, "Why it matters": partial sums are kept in
  * FP32): y[t, :] = bf16_rne( r[t, :] + sum_i w[t, i] * out[t, i, :] ), summed

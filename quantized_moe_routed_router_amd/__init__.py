@@ -79,6 +79,8 @@ _SIGS = {
     "moe_layer_decode_workspace_bytes": (_SZ, [ctypes.POINTER(moe_dims), _I]),
     "moe_layer_decode": (_I, [ctypes.POINTER(moe_dims), ctypes.POINTER(moe_experts), _P, _P, _P, _I,
                               _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_layer_decode_noalloc": (_I, [ctypes.POINTER(moe_dims), ctypes.POINTER(moe_experts), _P, _P, _P,
+                                      _I, _I, _P, _P, _P, _P]),
     "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_stream_read": (_I, [_P, _SZ, _P, _P]),
 }
@@ -244,6 +246,19 @@ def moe_layer_decode(d: moe_dims, experts: dict, x, W_r, bias, T: int, add_resid
     _check(lib().moe_layer_decode(ctypes.byref(d), ctypes.byref(ex), _ptr(x), _ptr(W_r), _ptr(bias),
                                   T, 1 if add_residual else 0, _ptr(y), _ptr(ids), _ptr(w),
                                   _ptr(ws), ws_bytes, _stream(stream)))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def moe_layer_decode_noalloc(d: moe_dims, experts: dict, x, W_r, bias, T: int, add_residual: bool, y,
+                             ids, w, stream=None):
+    """moe_layer_decode on the library's per-GPU scratch array (no workspace
+    argument; calls that overlap on one GPU race)."""
+    ex = _experts(experts)
+    _check(lib().moe_layer_decode_noalloc(ctypes.byref(d), ctypes.byref(ex), _ptr(x), _ptr(W_r),
+                                          _ptr(bias), T, 1 if add_residual else 0, _ptr(y), _ptr(ids),
+                                          _ptr(w), _stream(stream)))
 
 
 # ------------------------------------------------------------------ preparation

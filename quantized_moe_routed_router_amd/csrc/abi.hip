@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "common.hpp"
@@ -281,10 +282,15 @@ size_t moe_layer_decode_workspace_bytes(const moe_dims* d, int T) {
   return moe::layer_decode_workspace_bytes(d->E, d->H, d->I, d->k, T);
 }
 
-int moe_layer_decode(const moe_dims* d, const moe_experts* ex, const uint16_t* x, const float* W_r,
-                     const float* bias, int T, int add_residual, uint16_t* y, int32_t* ids, float* w,
-                     void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "moe_layer_decode";
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by moe_layer_decode and
+// moe_layer_decode_noalloc (which passes the device's scratch array).
+int layer_decode_checked(const char* fn, const moe_dims* d, const moe_experts* ex, const uint16_t* x,
+                         const float* W_r, const float* bias, int T, int add_residual, uint16_t* y,
+                         int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream) {
   int st = check_dims(fn, d);
   if (st) return st;
   if (T < 1 || T > MOE_LAYER_MAX_T)
@@ -311,6 +317,71 @@ int moe_layer_decode(const moe_dims* d, const moe_experts* ex, const uint16_t* x
   L.h_ts = ex->h_ts;
   L.y = y; L.ids_out = ids; L.w_out = w;
   return hip_status(moe::launch_layer_decode(L, ws, as_stream(stream)), fn);
+}
+
+}  // namespace
+
+// The no-allocation variant's workspace: one array per GPU, in the library's
+// device code, held until the process ends.  Host code never passes this
+// name to a kernel (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current, on the entry point's first call there.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+int scratch_of_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "moe_layer_decode_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: device %d outside the %d the library tracks", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "moe_layer_decode_noalloc: hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MOE_ERR_HIP, "%s: hipGetSymbolAddress(scratch) gave NULL on device %d", fn, dev);
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_decode(const moe_dims* d, const moe_experts* ex, const uint16_t* x, const float* W_r,
+                     const float* bias, int T, int add_residual, uint16_t* y, int32_t* ids, float* w,
+                     void* ws, size_t ws_bytes, void* stream) {
+  return layer_decode_checked("moe_layer_decode", d, ex, x, W_r, bias, T, add_residual, y, ids, w, ws,
+                              ws_bytes, stream);
+}
+
+int moe_layer_decode_noalloc(const moe_dims* d, const moe_experts* ex, const uint16_t* x,
+                             const float* W_r, const float* bias, int T, int add_residual, uint16_t* y,
+                             int32_t* ids, float* w, void* stream) {
+  const char* fn = "moe_layer_decode_noalloc";
+  int st = check_dims(fn, d);
+  if (st) return st;
+  if (T < 1 || T > MOE_LAYER_MAX_T)
+    return fail(MOE_ERR_SHAPE, "%s: T = %d outside [1, %d]", fn, T, MOE_LAYER_MAX_T);
+  const size_t need = moe::layer_decode_workspace_bytes(d->E, d->H, d->I, d->k, T);
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "%s: E = %d, H = %d, I = %d, k = %d, T = %d need %zu bytes of workspace, above the "
+                "%zu-byte scratch array (use moe_layer_decode with a workspace)",
+                fn, d->E, d->H, d->I, d->k, T, need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_of_current_device(fn, &ws);
+  if (st) return st;
+  return layer_decode_checked(fn, d, ex, x, W_r, bias, T, add_residual, y, ids, w, ws,
+                              (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int moe_ffn_prefill_tile_rows(const moe_dims* d, int T) {

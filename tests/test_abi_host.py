@@ -26,7 +26,7 @@ def test_library_exports_every_header_function():
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == m.exported_symbols()
-    assert m.moe_abi_version() == 5
+    assert m.moe_abi_version() == 6
 
 
 def test_sizes():
@@ -134,3 +134,19 @@ def test_zero_sized_calls_enqueue_nothing():
     m.moe_rms_norm(None, 0, 256, 1.0, None, 0)
     m.moe_quantize_weights(None, 0, 4, 16, None, None, None, 0)
     m.moe_stream_read(None, 0, None, 0)
+
+
+def test_noalloc_layer_refusals():
+    """The no-allocation decode layer refuses shapes whose workspace exceeds
+    its scratch array, with the numbers, before any device call."""
+    big = m.dims(1024, 4096, 2560, 32)
+    assert m.moe_layer_decode_workspace_bytes(big, 16) > m.MOE_NOALLOC_SCRATCH_BYTES
+    L = m.lib()
+    rc = L.moe_layer_decode_noalloc(ctypes.byref(big), None, None, None, None, 16, 1, None, None, None, None)
+    assert rc == m.MOE_ERR_WORKSPACE
+    msg = m.last_error()
+    assert "8388608" in msg and str(m.moe_layer_decode_workspace_bytes(big, 16)) in msg
+    fn = m.dims(512, 2560, 640, 10)
+    assert m.moe_layer_decode_workspace_bytes(fn, 16) <= m.MOE_NOALLOC_SCRATCH_BYTES
+    assert L.moe_layer_decode_noalloc(ctypes.byref(fn), None, None, None, None, 0, 1, None, None, None,
+                                      None) == m.MOE_ERR_SHAPE
