@@ -7,12 +7,17 @@ path for one token through one layer: router GEMV + top-k, NVFP4 activation
 quantizer, W4A4 expert FFN (gate/up + SiLU, down with re-quantized h), and
 the weighted combine with residual.  To keep every step's expert weights
 coming from HBM (not the 256 MB Infinity Cache or L2), the steps cycle through
-`--layers` independent resident layers and a fresh token each step; the
-sequence of steps is captured once in a HIP graph and replayed.
+`--layers` independent resident layers and a fresh token each step; exactly
+max(--steps, 100) steps are captured once as a HIP graph and timed with HIP
+events around one replay.
 
-Prints one JSON line (rank 0) with the metric, the roofline object of the
-expert FFN (the dominant kernels: all weight bytes stream through them), and
-the CPU oracle's throughput on a bounded sample of the same workload.
+Prints one JSON line with the metric; the roofline object of the timed step
+(its algorithmic bytes over its time, the measured HBM bytes and the dominant
+kernel from the committed rocprofv3 runs); the separate expert-FFN call; the
+48-layer stack; the prefill layers (8,192 Zipf-routed tokens, 65,536
+uniformly routed tokens with NVFP4 and codebook gate/up) with their MFMA
+fractions; and the CPU oracle's throughput on bounded samples of the same
+workloads.
 """
 from __future__ import annotations
 
@@ -42,18 +47,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel_key: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel source."""
+def stored_decode_profile():
+    """From the committed rocprofv3 runs of the decode layer step
+    (profiles/traffic.json): the measured HBM bytes per step (FETCH_SIZE +
+    WRITE_SIZE of its kernels, calibrated) and the dominant kernel's profiled
+    duration against its algorithmic bytes; both null unless they were taken
+    on the current kernel source."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
-        return None
+        return None, None
     with open(p) as f:
         d = json.load(f)
-    ent = d.get(kernel_key)
+    ent = d.get("layer_decode_b1")
     if not ent or ent.get("source_sha") != kernel_source_hash():
-        return None
-    return ent.get("hbm_bytes_per_launch")
+        return None, None
+    return ent.get("hbm_bytes_per_step"), ent.get("dominant_kernel")
 
 
 def build_layers(wl, n_layers, dev):
@@ -77,61 +85,105 @@ def build_layers(wl, n_layers, dev):
     return layers
 
 
-def prefill_64k(L0, dev, steps: int):
-    """The 65,536-token prefill layer (uniform routing): router GEMM + top-k,
-    x quantizer, grouped-GEMM expert FFN (NVFP4; then the 3-bit codebook
-    gate/up variant), combine.  Whole-layer tok/s and the expert FFN's share
-    of dense f16 MFMA peak (2.5 PFLOP/s)."""
+MFMA_PEAK_F16 = 2.5e15          # MI355X dense f16/bf16 matrix-core FLOP/s
+
+
+def time_prefill(L, x, T, steps, stream):
+    """The whole layer (router GEMM + top-k, x quantizer, grouped-GEMM expert
+    FFN, combine with residual) and the expert FFN call alone, each timed with
+    HIP events on the launch stream around `steps` calls (after two warm-up
+    calls).  Returns (ms per layer, ms per FFN call, buffers)."""
+    import torch
+    import quantized_moe_routed_router_amd as moe
+    b = L.alloc(T, prefill=True)
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            L.forward(x, b, residual=True, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            L.forward(x, b, residual=True, stream=stream)
+    e1.record(stream)
+    xq = (b["x_codes"], b["x_scales"], b["x_ts"])
+    f0.record(stream)
+    for _ in range(steps):
+        moe.moe_expert_ffn_prefill(L.d, L.experts(), xq, b["ids"], T, b["out"], b["ws"],
+                                   b["ws_bytes"], None, stream)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, f0.elapsed_time(f1) / steps, b
+
+
+def prefill_record(name, T, k, E, H, I, ms, ffn_ms, ids=None):
+    """tok/s and MFMA fractions of one prefill configuration: the expert
+    FFN's 2 T k 3 H I FLOP over the FFN call's time, and the layer's
+    (expert FFN + router 2 T E H) FLOP over the layer's time, against the
+    dense f16 matrix-core peak."""
+    import numpy as np
+    f_exp = 2.0 * T * k * 3 * H * I
+    f_rt = 2.0 * T * E * H
+    r = {"tokens": T, "tok_s": round(T / (ms * 1e-3), 1), "ms_per_layer": round(ms, 3),
+         "expert_ffn_ms": round(ffn_ms, 3),
+         "expert_ffn_gflop": round(f_exp / 1e9, 1), "router_gflop": round(f_rt / 1e9, 1),
+         "expert_ffn_mfma_frac": round(f_exp / (ffn_ms * 1e-3) / MFMA_PEAK_F16, 4),
+         "layer_mfma_frac": round((f_exp + f_rt) / (ms * 1e-3) / MFMA_PEAK_F16, 4)}
+    if ids is not None:
+        c = np.bincount(ids.reshape(-1), minlength=E)
+        r["routing"] = {"experts_touched": int((c > 0).sum()), "max_rows": int(c.max()),
+                        "experts_over_1000_rows": int((c >= 1000).sum())}
+    log(f"prefill {name}: {ms:.3f} ms/layer ({r['tok_s']:.0f} tok/s), expert FFN {ffn_ms:.3f} ms "
+        f"({r['expert_ffn_mfma_frac']:.3f} of MFMA peak)")
+    return r
+
+
+def prefill_runs(L0, dev, steps: int, want=("zipf8k", "nvfp4_64k", "codebook_64k")):
+    """The prefill configurations on layer 0's experts: 8,192 tokens with the
+    Zipf(1.1)-biased router, then 65,536 tokens with uniform routing, NVFP4
+    gate/up and the 3-bit codebook gate/up variant."""
     import torch
     import synth
     import quantized_moe_routed_router_amd as moe
-    wl = synth.WORKLOADS["prefill64k"]
-    T = wl.T
     res = {}
-    cb = moe.Layer(wl.E, wl.H, wl.I, wl.k, fmt_gate_up=moe.MOE_FMT_CB3G128, device=dev)
-    for e0 in range(0, wl.E, 64):
-        e1 = min(wl.E, e0 + 64)
-        _, _, d = synth.expert_weights_torch(wl, 0, e0, e1, dev)
-        cb.load_experts_fp32(e0, None, None, d)
-        g = synth.codebook_weights_torch(wl, 0, e0, e1, synth.PROJ_GATE, dev)
-        u = synth.codebook_weights_torch(wl, 0, e0, e1, synth.PROJ_UP, dev)
-        cb.load_codebook(e0, g[0], g[1], u[0], u[1])
-        del g, u, d
+    stream = torch.cuda.Stream()
+    W_save, b_save = L0.W_r, L0.bias
+    H, I, E, k = L0.H, L0.I, L0.E, L0.k
+    if "zipf8k" in want:
+        wl = synth.WORKLOADS["prefill8k"]
+        L0.set_router(synth.router_weights_torch(wl, 0, dev), torch.from_numpy(synth.router_bias(wl)).to(dev))
+        x = synth.activations_torch(wl, wl.T, 0, dev).view(torch.int16)
+        ms, ffn_ms, b = time_prefill(L0, x, wl.T, max(steps, 10), stream)
+        res["zipf_8k"] = prefill_record("8k zipf", wl.T, k, E, H, I, ms, ffn_ms, b["ids"].cpu().numpy())
+        del b, x
+        torch.cuda.empty_cache()
+    wl = synth.WORKLOADS["prefill64k"]
     W_r = synth.router_weights_torch(wl, 0, dev)
-    x = synth.activations_torch(wl, T, 0, dev).view(torch.int16)
-    flops = 2.0 * T * wl.k * 3 * wl.H * wl.I
-    for name, L in (("nvfp4", L0), ("codebook_gate_up", cb)):
-        L.set_router(W_r)
-        b = L.alloc(T, prefill=True)
-        stream = torch.cuda.Stream()
-        with torch.cuda.stream(stream):
-            for _ in range(2):
-                L.forward(x, b, residual=True, stream=stream)
-        torch.cuda.synchronize()
-        e0_, e1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0_.record(stream)
-        with torch.cuda.stream(stream):
-            for _ in range(steps):
-                L.forward(x, b, residual=True, stream=stream)
-        e1_.record(stream)
-        xq = (b["x_codes"], b["x_scales"], b["x_ts"])
-        f0.record(stream)
-        for _ in range(steps):
-            moe.moe_expert_ffn_prefill(L.d, L.experts(), xq, b["ids"], T, b["out"], b["ws"],
-                                       b["ws_bytes"], None, stream)
-        f1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0_.elapsed_time(e1_) / steps
-        ffn_ms = f0.elapsed_time(f1) / steps
-        res[name] = {"tok_s": round(T / (ms * 1e-3), 1), "ms_per_layer": round(ms, 3),
-                     "expert_ffn_ms": round(ffn_ms, 3),
-                     "expert_ffn_mfma_frac": round(flops / (ffn_ms * 1e-3) / 2.5e15, 4)}
-        log(f"prefill 64k {name}: {ms:.2f} ms/layer ({T / ms * 1e3:.0f} tok/s), expert FFN {ffn_ms:.2f} ms")
+    x = synth.activations_torch(wl, wl.T, 0, dev).view(torch.int16)
+    if "nvfp4_64k" in want:
+        L0.set_router(W_r)
+        ms, ffn_ms, b = time_prefill(L0, x, wl.T, steps, stream)
+        res["nvfp4"] = prefill_record("64k nvfp4", wl.T, k, E, H, I, ms, ffn_ms)
         del b
         torch.cuda.empty_cache()
-    del cb
-    torch.cuda.empty_cache()
+    if "codebook_64k" in want:
+        cb = moe.Layer(E, H, I, k, fmt_gate_up=moe.MOE_FMT_CB3G128, device=dev)
+        dwl = synth.WORKLOADS["decode"]
+        for e0 in range(0, E, 64):
+            e1 = min(E, e0 + 64)
+            _, _, d = synth.expert_weights_torch(dwl, 0, e0, e1, dev)
+            cb.load_experts_fp32(e0, None, None, d)
+            g = synth.codebook_weights_torch(wl, 0, e0, e1, synth.PROJ_GATE, dev)
+            u = synth.codebook_weights_torch(wl, 0, e0, e1, synth.PROJ_UP, dev)
+            cb.load_codebook(e0, g[0], g[1], u[0], u[1])
+            del g, u, d
+        cb.set_router(W_r)
+        ms, ffn_ms, b = time_prefill(cb, x, wl.T, steps, stream)
+        res["codebook_gate_up"] = prefill_record("64k codebook", wl.T, k, E, H, I, ms, ffn_ms)
+        del b, cb
+        torch.cuda.empty_cache()
+    L0.set_router(W_save, b_save)
     return res
 
 
@@ -264,15 +316,53 @@ def crossover(layers, dev, reps: int = 20, Ts=(1, 2, 4, 8, 16, 32, 64, 128, 256,
     return out
 
 
-def cpu_baseline(wl, n_tokens: int, dev):
+def cpu_info() -> dict:
+    """The host the oracle ran on: CPU model, cores visible to this process,
+    and the BLAS library's thread count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    blas = None
+    try:
+        import threadpoolctl
+        info = [d for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+        if info:
+            blas = {"library": info[0].get("internal_api"), "threads": info[0].get("num_threads")}
+    except Exception:
+        pass
+    return {"cpu_model": model, "cores_visible": cores, "os_cpu_count": os.cpu_count(), "blas": blas}
+
+
+def _blas_threads(n):
+    """Context limiting the BLAS threads to n (None: unchanged)."""
+    import contextlib
+    if n is None:
+        return contextlib.nullcontext()
+    import threadpoolctl
+    return threadpoolctl.threadpool_limits(limits=n, user_api="blas")
+
+
+def oracle_decode(wl, n_tokens: int, dev, threads=None):
     """The oracle on the host: n_tokens single-token steps through layer 0
-    (router, quantizer, expert FFN with on-the-fly dequantization, combine).
-    Weight quantization (preparation) is outside the timed region."""
+    (router, quantizer, expert FFN with on-the-fly dequantization of the
+    picked experts, combine).  Weight quantization (preparation) is outside
+    the timed region.  Returns (tok/s, seconds)."""
     import numpy as np
+    import torch
     import synth
     from oracle import ffn as offn, router as orouter
     W_r = synth.router_weights_torch(wl, 0, dev).cpu().numpy()
-    xs = [synth.activations_torch(wl, 1, 10_000 + i, dev).view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    xs = [synth.activations_torch(wl, 1, 10_000 + i, dev).view(torch.int16).cpu().numpy().view(np.uint16)
           for i in range(n_tokens)]
     need = set()
     for x in xs:
@@ -282,14 +372,116 @@ def cpu_baseline(wl, n_tokens: int, dev):
     for e in sorted(need):
         g, u, d = synth.expert_weights_torch(wl, 0, e, e + 1, dev)
         q[e] = offn.quantize_expert(g[0].cpu().numpy(), u[0].cpu().numpy(), d[0].cpu().numpy())
-    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
-    t0 = time.perf_counter()
-    for x in xs:
-        offn.layer(x, W_r, None, q, wl.k, residual=True)
-    dt = time.perf_counter() - t0
-    return dict(value=n_tokens / dt, unit="tok/s", cores=int(threads), kind="oracle",
-                sample=f"{n_tokens} single-token decode steps through one H2560/I640/E512/k10 layer "
-                       f"(numpy oracle, fp64 matmuls on dequantized weights, {dt:.1f} s)")
+    with _blas_threads(threads):
+        t0 = time.perf_counter()
+        for x in xs:
+            offn.layer(x, W_r, None, q, wl.k, residual=True)
+        dt = time.perf_counter() - t0
+    return n_tokens / dt, dt
+
+
+def oracle_prefill_estimate(wl, dev, T_sample: int, n_exp: int, big_rows: int, threads=None):
+    """The oracle's time for a whole prefill layer, from a bounded sample,
+    scaled linearly:
+      - router, x quantizer and combine: timed on the workload's first
+        T_sample tokens, scaled by T / T_sample (per-token work);
+      - expert dequantization: timed on n_exp experts, scaled by the number of
+        experts the workload touches;
+      - expert FFN (gate/up, SiLU, h quantization, down) of one expert: timed
+        at two row counts (its rows in the sample, and big_rows rows) and fitted
+        as a + b * rows, summed over the experts at the workload's rows per
+        expert (the oracle's own routing of all T tokens when T_sample = T,
+        else T k / E each: uniform routing).
+    The expert weights are layer 0 of the decode workload, as on the GPU.
+    Returns a dict with the estimate and every measured part."""
+    import numpy as np
+    import torch
+    import synth
+    from oracle import ffn as offn, router as orouter
+    dwl = synth.WORKLOADS["decode"]
+    T, k, E, H = wl.T, wl.k, wl.E, wl.H
+    xt = synth.activations_torch(wl, T, 0, dev)[:T_sample]
+    xs = xt.view(torch.int16).cpu().numpy().view(np.uint16)
+    del xt
+    W_r = synth.router_weights_torch(wl, 0, dev).cpu().numpy()
+    bias = synth.router_bias(wl)
+    with _blas_threads(threads):
+        t0 = time.perf_counter()
+        ids, w, *_ = orouter.route(xs, W_r, k, bias)
+        t_route = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        xq = offn.quantize_act(xs)
+        t_xq = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        offn.combine(np.zeros((T_sample, k, H), np.float32), w, xs)
+        t_comb = time.perf_counter() - t0
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    order = np.argsort(-counts, kind="stable")
+    sample = [int(e) for e in order[:n_exp] if counts[e] > 0]
+    q = {}
+    for e in sample:
+        g, u, d = synth.expert_weights_torch(dwl, 0, e, e + 1, dev)
+        q[e] = offn.quantize_expert(g[0].cpu().numpy(), u[0].cpu().numpy(), d[0].cpu().numpy())
+    with _blas_threads(threads):
+        t0 = time.perf_counter()
+        deq = {e: offn.dequant_expert(q[e]) for e in sample}
+        t_deq = (time.perf_counter() - t0) / len(sample)
+        pts = []
+        flat = ids.reshape(-1)
+        for e in sample[:2]:
+            for rows in (np.nonzero(flat == e)[0] // k, np.arange(big_rows) % T_sample):
+                sub = tuple(a[rows] for a in xq[:2]) + (xq[2][rows],)
+                ids1 = np.full((len(rows), 1), e)
+                t0 = time.perf_counter()
+                h = offn.gate_up({e: deq[e]}, sub, ids1)
+                offn.down({e: deq[e]}, offn.quantize_h(h), ids1)
+                pts.append((len(rows), time.perf_counter() - t0))
+    n = np.array([p[0] for p in pts], np.float64)
+    t = np.array([p[1] for p in pts], np.float64)
+    b, a = np.polyfit(n, t, 1)
+    a = max(a, 0.0)
+    if T_sample == T:
+        rows_e = counts[counts > 0].astype(np.float64)
+        touched = int((counts > 0).sum())
+    else:
+        rows_e = np.full(E, T * k / E)
+        touched = E
+    t_ffn = float(np.sum(a + b * rows_e))
+    scale = T / T_sample
+    total = (t_route + t_xq + t_comb) * scale + t_deq * touched + t_ffn
+    return {"tok_s": round(T / total, 2), "layer_s_estimated": round(total, 1),
+            "threads": "all" if threads is None else threads,
+            "parts_s": {"router": round(t_route * scale, 2), "x_quant": round(t_xq * scale, 2),
+                        "combine": round(t_comb * scale, 2), "expert_dequant": round(t_deq * touched, 2),
+                        "expert_ffn": round(t_ffn, 2)},
+            "sample": (f"router/x-quant/combine on the first {T_sample} of {T} tokens (x {scale:g}); "
+                       f"dequantization on {len(sample)} experts (x {touched} touched); expert FFN "
+                       f"fitted as {a * 1e3:.1f} ms + {b * 1e6:.1f} us per row on "
+                       f"{', '.join(str(int(v)) for v in n)} rows, summed over {touched} experts")}
+
+
+def cpu_baseline(wl, n_tokens: int, dev, prefill: bool = True):
+    """The oracle timed on this host (never tuned for it): the decode layer
+    per token on all cores and on one BLAS thread, and the two prefill
+    layers (8,192 Zipf-routed and 65,536 uniformly routed tokens) estimated
+    from bounded samples with stated linear scaling."""
+    info = cpu_info()
+    v_all, dt_all = oracle_decode(wl, n_tokens, dev)
+    n1 = max(2, n_tokens // 3)
+    v_one, dt_one = oracle_decode(wl, n1, dev, threads=1)
+    out = dict(value=v_all, unit="tok/s", cores=info["cores_visible"], kind="oracle",
+               sample=f"{n_tokens} single-token decode steps through one H2560/I640/E512/k10 layer "
+                      f"(numpy oracle, fp64 matmuls on dequantized weights, {dt_all:.1f} s, all cores)",
+               single_thread_value=round(v_one, 3),
+               single_thread_sample=f"{n1} steps with BLAS limited to one thread ({dt_one:.1f} s)",
+               **info)
+    if prefill:
+        import synth
+        out["prefill_8k_zipf"] = oracle_prefill_estimate(synth.WORKLOADS["prefill8k"], dev, 8192, 6, 2048)
+        out["prefill_64k_uniform"] = oracle_prefill_estimate(synth.WORKLOADS["prefill64k"], dev, 2048, 4, 2048)
+        out["prefill_64k_uniform_single_thread"] = oracle_prefill_estimate(
+            synth.WORKLOADS["prefill64k"], dev, 1024, 2, 1024, threads=1)
+    return out
 
 
 def time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream, graph=True):
@@ -427,23 +619,66 @@ def copy_calibration(dev):
     log("copy calibration: 3 x 1 GiB device copies done")
 
 
+# Algorithmic HBM bytes of one decode layer step for one token (the whole
+# hot path): the fp32 router weights E * H * 4 plus the k picked experts'
+# packed gate/up and down weights (codes and E4M3 block scales); the
+# activations (x, y: 10 KB) and intermediates are left out.
+def decode_step_bytes(E, H, I, k):
+    return E * H * 4 + k * ((3 * H * I) // 2 + (3 * H * I) // 16)
+
+
+def decode_graph(step, n_steps, stream):
+    """n_steps steps captured once as one HIP graph (after an eager pass that
+    also loads the code objects)."""
+    import torch
+    with torch.cuda.stream(stream):
+        for i in range(n_steps):
+            step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(n_steps):
+            step(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps, stream):
+    import torch
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=960)
+    ap.add_argument("--steps", type=int, default=960,
+                    help="decode steps timed (at least 100 are timed whatever is asked)")
     ap.add_argument("--warmup", type=int, default=96)
     ap.add_argument("--layers", type=int, default=48, help="distinct resident layers cycled")
-    ap.add_argument("--cpu-tokens", type=int, default=30)
+    ap.add_argument("--cpu-tokens", type=int, default=24)
     ap.add_argument("--path", choices=["fused", "separate"], default="fused",
                     help="fused: moe_layer_decode (3 kernels); separate: the 4 entry points (6 kernels)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true", help="skip the 65,536-token prefill figures")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill figures")
     ap.add_argument("--no-stack", action="store_true", help="skip the 48-layer stack figures")
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for counter calibration)")
     ap.add_argument("--ffn-only", action="store_true",
                     help="only the eager expert-FFN launches (for counter runs): no graph, no prefill")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the eager fused decode layer steps (for counter runs)")
+    ap.add_argument("--prefill-only", type=str, default=None,
+                    help="only these prefill runs (comma list of zipf8k, nvfp4_64k, codebook_64k; "
+                         "for profiler runs)")
     ap.add_argument("--crossover-t", type=str, default=None,
                     help="comma-separated token counts for --crossover")
     ap.add_argument("--crossover", action="store_true",
@@ -462,18 +697,23 @@ def main():
 
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS["decode"]
-    NL = args.layers
+    NL = 1 if args.prefill_only else args.layers
     moe.moe_check_capacity(0, NL * (moe.moe_packed_bytes(moe.dims(wl.E, wl.H, wl.I, wl.k), 0)
                                     + moe.moe_packed_bytes(moe.dims(wl.E, wl.H, wl.I, wl.k), 1)))
     log(f"building {NL} layers on the device")
     layers = build_layers(wl, NL, dev)
+    if args.prefill_only:
+        res = prefill_runs(layers[0], dev, args.prefill_steps, tuple(args.prefill_only.split(",")))
+        if args.copy_calibration:
+            copy_calibration(dev)
+        print(json.dumps({"prefill": res}), flush=True)
+        return
     NX = 64
     xs = torch.stack([synth.activations_torch(wl, 1, s, dev)[0] for s in range(NX)]).view(torch.int16)
     bufs = [L.alloc(1, prefill=False) for L in layers]
     fbufs = [L.alloc_fused(1) for L in layers]
-
     stream = torch.cuda.Stream()
-    cycle = NL * max(1, (NX // NL))            # steps per captured graph
+    cycle = NL * max(1, (NX // NL))
     if args.crossover:
         kw = {} if args.crossover_t is None else {"Ts": tuple(int(v) for v in args.crossover_t.split(","))}
         print(json.dumps({"crossover": crossover(layers, dev, **kw), "layers": NL}), flush=True)
@@ -486,6 +726,7 @@ def main():
             copy_calibration(dev)
         print(json.dumps({"ffn_us_eager": round(ffn_us, 3), "ffn_bytes": ffn_bytes}), flush=True)
         return
+
     def step(i):
         li = i % NL
         x = xs[i % NX:i % NX + 1]
@@ -494,39 +735,37 @@ def main():
         else:
             layers[li].forward(x, bufs[li], residual=True, stream=stream)
 
-    with torch.cuda.stream(stream):
-        for i in range(cycle):                 # eager warm-up, also loads the code objects
-            step(i)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(cycle):
-            step(i)
-    torch.cuda.synchronize()
+    if args.decode_only:
+        with torch.cuda.stream(stream):
+            for i in range(max(args.steps, cycle)):
+                step(i)
+        torch.cuda.synchronize()
+        if args.copy_calibration:
+            copy_calibration(dev)
+        print(json.dumps({"decode_steps": max(args.steps, cycle)}), flush=True)
+        return
 
-    reps_w = max(1, args.warmup // cycle)
-    reps = max(1, args.steps // cycle)
-    steps = reps * cycle
+    # the headline: exactly n_steps layer steps (at least 100), one token
+    # each, layers and tokens cycling so every step's experts come from HBM,
+    # captured as one HIP graph; untimed warm-up replays first
+    n_steps = max(args.steps, 100)
+    g = decode_graph(step, n_steps, stream)
+    reps_w = max(1, -(-args.warmup // n_steps))
     with torch.cuda.stream(stream):
         for _ in range(reps_w):
             g.replay()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_host0 = time.perf_counter()
-    ev0.record(stream)
-    with torch.cuda.stream(stream):
-        for _ in range(reps):
-            g.replay()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms_total = time_graph(g, 1, stream)
     t_host = time.perf_counter() - t_host0
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / steps
-    log(f"graph: {steps} steps in {ms_total:.3f} ms (host {t_host * 1e3:.1f} ms): {ms_step * 1e3:.2f} us/step")
+    ms_step = ms_total / n_steps
+    log(f"graph: {n_steps} steps in {ms_total:.3f} ms (host {t_host * 1e3:.1f} ms): {ms_step * 1e3:.3f} us/step")
+    del g
 
+    step_bytes = decode_step_bytes(wl.E, wl.H, wl.I, wl.k)
+    achieved = step_bytes / (ms_step * 1e-3) / 1e9
     ffn_us, ffn_eager_us, ffn_bytes = time_ffn(layers, bufs, xs, NL, NX, cycle, wl, stream)
-    achieved = ffn_bytes / (ffn_us * 1e-6) / 1e9
+    ffn_gbps = ffn_bytes / (ffn_us * 1e-6) / 1e9
 
     # the same layer cycle with static (calibrated) h tensor scales: h^ is
     # quantized in the gate/up kernel, the down kernel reads it
@@ -534,41 +773,21 @@ def main():
     if args.path == "fused":
         for li, L in enumerate(layers):
             L.set_static_h_scales(torch.from_numpy(synth.static_h_scales(wl, li)).to(dev))
-        gs = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            for i in range(cycle):
-                step(i)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(gs, stream=stream):
-            for i in range(cycle):
-                step(i)
-        torch.cuda.synchronize()
+        gs = decode_graph(step, n_steps, stream)
         with torch.cuda.stream(stream):
             gs.replay()
-        torch.cuda.synchronize()
-        ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev2.record(stream)
-        with torch.cuda.stream(stream):
-            for _ in range(reps):
-                gs.replay()
-        ev3.record(stream)
-        torch.cuda.synchronize()
-        us_s = ev2.elapsed_time(ev3) * 1e3 / steps
+        us_s = time_graph(gs, 1, stream) * 1e3 / n_steps
         static_h = {"us_per_step": round(us_s, 3), "tok_s": round(1e6 / us_s, 1)}
         log(f"static h scales: {us_s:.2f} us/step")
         for L in layers:
             L.set_static_h_scales(None)
         del gs
 
-    # whole step's algorithmic HBM bytes: router weights + k experts + activations
-    step_bytes = wl.E * wl.H * 4 + ffn_bytes + wl.H * 2 * 2 + wl.k * wl.H * 4
-    layer_gbps = step_bytes / (ms_step * 1e-3) / 1e9
-
     if args.copy_calibration:
         copy_calibration(dev)
 
     stream_ref = read_stream(dev, ffn_bytes)
-    stream_ref["ffn_call_frac_of_stream"] = round(achieved / stream_ref["gbps"], 3)
+    stream_ref["ffn_call_frac_of_stream"] = round(ffn_gbps / stream_ref["gbps"], 3)
 
     stack = None
     if not args.no_stack:
@@ -576,21 +795,23 @@ def main():
 
     prefill = None
     if not args.no_prefill:
-        prefill = prefill_64k(layers[0], dev, args.prefill_steps)
+        prefill = prefill_runs(layers[0], dev, args.prefill_steps)
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
-        cpu = cpu_baseline(wl, args.cpu_tokens, dev)
+        log(f"cpu baseline: oracle on {args.cpu_tokens} decode tokens, prefill samples")
+        cpu = cpu_baseline(wl, args.cpu_tokens, dev, prefill=not args.no_prefill)
 
-    traffic = stored_traffic("ffn_decode_b1")
+    traffic, dominant = stored_decode_profile()
     out = {
         "metric": METRIC,
         "value": round(1e3 / ms_step, 1),
         "unit": "tok/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": reps_w * cycle,
+        "steps": n_steps,
+        "steps_requested": args.steps,
+        "warmup": reps_w * n_steps,
+        "warmup_requested": args.warmup,
         "ms_per_step": round(ms_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -599,20 +820,27 @@ def main():
         "data": "synthetic",
         "config": {"workload": "flash_next_decode_layer_b1", "H": wl.H, "I": wl.I, "E": wl.E,
                    "k": wl.k, "tokens_per_step": 1, "resident_layers_cycled": NL,
-                   "hip_graph": True, "path": args.path,
-                   "achieved_layer_hbm_gbps": round(layer_gbps, 1),
-                   "layer_bytes_per_step": step_bytes},
+                   "hip_graph": True, "path": args.path},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "moe_expert_ffn_decode (gate_up_decode_kernel, down_slice_kernel)",
-                     "bytes_per_launch": ffn_bytes, "us_per_launch": round(ffn_us, 3),
-                     "timing": "HIP events around graph replays of the calls (layers and tokens cycling)",
-                     "us_per_launch_eager": round(ffn_eager_us, 3)},
+                     "traffic": traffic,
+                     "kernel": ("one decode layer step, moe_layer_decode (router_quant_kernel, "
+                                "gate_up_decode_kernel<1,10,true>, down_slice_kernel<true,true>)"),
+                     "bytes_per_launch": step_bytes, "us_per_launch": round(ms_step * 1e3, 3),
+                     "timing": ("HIP events on the launch stream around one replay of the graph of "
+                                f"{n_steps} steps (the headline timed region)"),
+                     "dominant_kernel": dominant},
+        "expert_ffn_call": {"kernel": "moe_expert_ffn_decode (gate_up_decode_kernel<1,10,false>, "
+                                      "down_slice_kernel<false,true>)",
+                            "bytes_per_call": ffn_bytes, "us_per_call": round(ffn_us, 3),
+                            "gbps": round(ffn_gbps, 1), "frac": round(ffn_gbps / HBM_PEAK_GBPS, 4),
+                            "us_per_call_eager": round(ffn_eager_us, 3),
+                            "timing": "HIP events around graph replays of the calls (layers and tokens cycling)"},
         "read_stream": stream_ref,
         "cpu_baseline": cpu,
         "decode_static_h_scale": static_h,
         "stack_decode": stack,
-        "prefill_64k": prefill,
+        "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
 
