@@ -274,17 +274,28 @@ __device__ __forceinline__ float dpp_wave_sum(float v) {
       [](int a, int b) { return __float_as_int(__int_as_float(a) + __int_as_float(b)); }));
 }
 
-// Top-k of one token's logits by one wave (E <= 64 * PER).  Lane l holds
-// logits l*PER .. l*PER+PER-1 as order-preserving integer keys (-0 folded into
-// +0), sorted descending with the lower id first among equal keys.  Each of
-// the k rounds: the wave maximum M of the lanes' heads (DPP), the lowest lane
-// whose head equals M (ballot; lower lane = lower ids, so exact ties go to the
-// lower expert id) pops its head and writes the head's id to LDS slot 64 + r
-// (every other lane writes its own dummy slot, so the store needs no exec
-// mask).  Keys and ids live in vector registers (ext_vector), which keeps the
-// compiler from turning the selects into indexed private-array accesses.
-// The winners' softmax, renormalised over the k, is summed on DPP as well.
-// Lane r < k returns winner r.  scr: 64 + k ints of LDS owned by this wave.
+// Top-k of one token's logits by one wave (E <= 64 * PER, k <= TOPK_MAX_K).
+// Lane l holds logits l*PER .. l*PER+PER-1 as order-preserving integer keys
+// (-0 folded into +0); the order is (key descending, id ascending), so exact
+// ties go to the lower expert id.
+// Fast path: the k-th largest of the 64 lane maxima is a lower bound of the
+// k-th largest logit (the k largest lane maxima are k distinct logits), so
+// every winner's key is at or above that lane maximum's top 16 bits, found
+// bit by bit from ballot counts.  The few keys at or above it (typically
+// k to 2k) are compacted into LDS, each candidate lane counts the candidates
+// that beat it (its rank), and the winners land in LDS slots by rank.  When
+// more than 64 keys pass the bound (many equal or nearly equal logits) the
+// full selection runs instead: each lane sorts its keys, then k rounds take
+// the wave maximum of the lanes' heads (DPP) and pop it from the lowest lane
+// holding it (lower lane = lower ids).  Keys and ids live in vector
+// registers (ext_vector), which keeps the compiler from turning the selects
+// into indexed private-array accesses.  The winners' softmax, renormalised
+// over the k, is summed on DPP with winner r in lane r either way, so both
+// paths give the same weights bit for bit.  Lane r < k returns winner r.
+// scr: TOPK_SCR_INTS ints of LDS owned by this wave.
+constexpr int TOPK_MAX_K = 32;
+constexpr int TOPK_SCR_INTS = 128 + 2 * TOPK_MAX_K;
+
 __device__ __forceinline__ int float_order_key(float f) {
   const int i = __float_as_int(f + 0.0f);             // -0 -> +0
   return i ^ ((i >> 31) & 0x7FFFFFFF);
@@ -298,6 +309,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, int E,
                                           int* scr, int* out_id, float* out_w) {
   typedef int ivec __attribute__((ext_vector_type(PER)));
   constexpr int KMIN = (int)0x80000000;
+  constexpr int CBITS = PER >= 16 ? 5 : PER >= 8 ? 4 : PER >= 4 ? 3 : PER >= 2 ? 2 : 1;
   ivec key, id;
   if (E == 64 * PER) {                       // full lanes: plain loads, all in flight at once
 #pragma unroll
@@ -313,42 +325,94 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, int E,
       key[i] = e < E ? float_order_key(lrow[e]) : KMIN;
     }
   }
-  // sort descending by (key desc, id asc): odd-even transposition network
+  // ---- lower bound: top 16 bits of the k-th largest lane maximum
+  int m = key[0];
 #pragma unroll
-  for (int pass = 0; pass < PER; ++pass) {
+  for (int i = 1; i < PER; ++i) m = max(m, key[i]);
+  const uint32_t mp = ((uint32_t)m ^ 0x80000000u) >> 16;           // unsigned order, 16-bit prefix
+  uint32_t P = 0;
 #pragma unroll
-    for (int i = pass & 1; i + 1 < PER; i += 2) {
-      const int a = key[i], b = key[i + 1], ia = id[i], ib = id[i + 1];
-      const bool sw = b > a;                           // equal keys keep id order
-      key[i] = sw ? b : a;
-      key[i + 1] = sw ? a : b;
-      id[i] = sw ? ib : ia;
-      id[i + 1] = sw ? ia : ib;
-    }
+  for (int b = 15; b >= 0; --b) {
+    const uint32_t c = P | (1u << b);
+    if (__popcll(__ballot(mp >= c)) >= (unsigned)k) P = c;
   }
-  int mykey = KMIN, key0 = KMIN;
-  for (int r = 0; r < k; ++r) {
-    const int M = dpp_wave_reduce(key[0], KMIN, [](int a, int b) { return max(a, b); });
-    const uint64_t hit = __ballot(key[0] == M);
-    const int wl = __ffsll((unsigned long long)hit) - 1;        // lowest lane holding M
-    const bool pop = lane == wl;
-    scr[pop ? 64 + r : lane] = id[0];
-    mykey = lane == r ? M : mykey;
-    key0 = r == 0 ? M : key0;
-    ivec ks, is;
+  const int thr = (int)((P << 16) ^ 0x80000000u);
+  // ---- candidates (keys >= thr): per-lane count, exclusive prefix over lanes
+  int cnt = 0;
 #pragma unroll
-    for (int i = 0; i + 1 < PER; ++i) {
-      ks[i] = key[i + 1];
-      is[i] = id[i + 1];
-    }
-    ks[PER - 1] = KMIN;
-    is[PER - 1] = id[PER - 1];
-    key = pop ? ks : key;
-    id = pop ? is : id;
+  for (int i = 0; i < PER; ++i) cnt += key[i] >= thr ? 1 : 0;
+  int off = 0, n_c = 0;
+#pragma unroll
+  for (int b = 0; b < CBITS; ++b) {
+    const uint64_t bm = __ballot((cnt >> b) & 1);
+    off += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u)) << b;
+    n_c += __popcll(bm) << b;
   }
+  int* wid = scr + 128;                      // winner r's id
+  int* wkey = scr + 128 + TOPK_MAX_K;        // winner r's key
+  if (n_c <= 64) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (key[i] >= thr) {
+        scr[off] = key[i];
+        scr[64 + off] = id[i];
+        ++off;
+      }
+    }
+    wave_lds_sync();
+    const int ck = lane < n_c ? scr[lane] : KMIN;
+    const int ci = lane < n_c ? scr[64 + lane] : 0x7FFFFFFF;
+    int rank = 0;
+    for (int j = 0; j < n_c; ++j) {
+      const int kj = __builtin_amdgcn_readlane(ck, j), ij = __builtin_amdgcn_readlane(ci, j);
+      rank += (kj > ck || (kj == ck && ij < ci)) ? 1 : 0;
+    }
+    if (lane < n_c && rank < k) {
+      wid[rank] = ci;
+      wkey[rank] = ck;
+    }
+    wave_lds_sync();
+  } else {
+    // sort descending by (key desc, id asc): odd-even transposition network
+#pragma unroll
+    for (int pass = 0; pass < PER; ++pass) {
+#pragma unroll
+      for (int i = pass & 1; i + 1 < PER; i += 2) {
+        const int a = key[i], b = key[i + 1], ia = id[i], ib = id[i + 1];
+        const bool sw = b > a;                           // equal keys keep id order
+        key[i] = sw ? b : a;
+        key[i + 1] = sw ? a : b;
+        id[i] = sw ? ib : ia;
+        id[i + 1] = sw ? ia : ib;
+      }
+    }
+    for (int r = 0; r < k; ++r) {
+      const int M = dpp_wave_reduce(key[0], KMIN, [](int a, int b) { return max(a, b); });
+      const uint64_t hit = __ballot(key[0] == M);
+      const int wl = __ffsll((unsigned long long)hit) - 1;        // lowest lane holding M
+      const bool pop = lane == wl;
+      scr[pop ? 64 + r : lane] = id[0];
+      if (lane == 0) wkey[r] = M;
+      ivec ks, is;
+#pragma unroll
+      for (int i = 0; i + 1 < PER; ++i) {
+        ks[i] = key[i + 1];
+        is[i] = id[i + 1];
+      }
+      ks[PER - 1] = KMIN;
+      is[PER - 1] = id[PER - 1];
+      key = pop ? ks : key;
+      id = pop ? is : id;
+    }
+    wave_lds_sync();
+    if (lane < k) wid[lane] = scr[64 + lane];
+    wave_lds_sync();
+  }
+  const int mykey = wkey[lane < k ? lane : 0];
+  const int key0 = wkey[0];
   const float z = lane < k ? __expf(order_key_float(mykey) - order_key_float(key0)) : 0.0f;
   const float sum = dpp_wave_sum(z);
-  *out_id = scr[64 + (lane < k ? lane : 0)];
+  *out_id = wid[lane < k ? lane : 0];
   *out_w = z / sum;
 }
 

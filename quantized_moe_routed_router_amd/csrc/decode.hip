@@ -41,6 +41,7 @@
 namespace moe {
 
 constexpr int DEC_MAX_WAVES = 8;
+static_assert(MOE_MAX_K <= TOPK_MAX_K, "top-k scratch holds MOE_MAX_K winners");
 constexpr int DEC_CPW = 10;            // chunks (32 elements) per wave held in registers
 
 // ---------------------------------------------------------------- helpers
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
   float* red = reinterpret_cast<float*>(smem + (size_t)MAXP * a.H * 2);   // [nw][MAXP][64]
   __shared__ int list[MAXP];
   __shared__ int sids[TOPK ? MOE_MAX_K : 1];             // ranked ids (one token)
-  __shared__ int tscr[TOPK ? DEC_MAX_WAVES : 1][64 + MOE_MAX_K];
+  __shared__ int tscr[TOPK ? DEC_MAX_WAVES : 1][TOPK_SCR_INTS];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int npairs = a.T * a.k, p = blockIdx.x, j = blockIdx.y, split = blockIdx.z;
   const int KS = gridDim.z;

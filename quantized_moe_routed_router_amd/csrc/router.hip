@@ -465,14 +465,13 @@ __global__ __launch_bounds__(64 * RS_WAVES) void router_splitk16_kernel(const ui
 }
 
 // ---------------------------------------------------------------- top-k
-// One wave per token; lane l holds logits l, l+64, ... (E <= 1024).  Each of
-// the k rounds takes the wave maximum (DPP), then the lowest expert id holding
-// it (exact ties go to the lower id), and retires that entry.  The winners'
-// softmax, renormalised over the k, is summed on DPP as well.
+// One wave per token (topk_wave: a lower bound from the lane maxima, then
+// the few candidates above it ranked; exact ties go to the lower id), then
+// the winners' softmax renormalised over the k.
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
-  __shared__ int scr[4][64 + MOE_MAX_K];
+  __shared__ int scr[4][TOPK_SCR_INTS];
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;                                  // wave-uniform; no block barrier below
