@@ -83,6 +83,26 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// (token tile, expert tile) of this block for the token-tile x expert-tile
+// GEMM grids: blocks are dealt to the eight XCDs round-robin in dispatch
+// order, so each XCD's consecutive blocks take every expert tile of one token
+// tile before the next token tile: the token rows (the large operand, read
+// once per expert tile) then come from that XCD's L2 after the first read
+// instead of from HBM once per expert tile.  A bijection on the grid; grids
+// whose token-tile count is not a multiple of eight keep the plain order.
+__device__ __forceinline__ void router_tile_of_block(int& tt, int& et) {
+  const int ntok = gridDim.x, nexp = gridDim.y;
+  const int b = blockIdx.x + ntok * blockIdx.y;
+  if (ntok % 8 == 0) {
+    const int xcd = b & 7, i = b >> 3;
+    tt = (i / nexp) * 8 + xcd;
+    et = i % nexp;
+  } else {
+    tt = blockIdx.x;
+    et = blockIdx.y;
+  }
+}
+
 __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ W,
                                                           const float* __restrict__ bias, int T,
@@ -92,7 +112,9 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   __shared__ __align__(16) uint16_t Bs[3][RG_BN][RG_LDK];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
-  const int t0 = blockIdx.x * RG_BM, e0 = blockIdx.y * RG_BN;
+  int tt, et;
+  router_tile_of_block(tt, et);
+  const int t0 = tt * RG_BM, e0 = et * RG_BN;
   // staging role: tile row r, K half hf (32 elements)
   const int r = tid >> 1, hf = tid & 1;
   const bool tv = t0 + r < T, ev = e0 + r < E;
@@ -198,7 +220,9 @@ __global__ __launch_bounds__(512) void router_mfma256_kernel(const uint16_t* __r
   __shared__ __align__(16) uint16_t Bs[3][RG_BN][RG_LDK];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
-  const int t0 = blockIdx.x * (2 * RG_BM), e0 = blockIdx.y * RG_BN;
+  int tt, et;
+  router_tile_of_block(tt, et);
+  const int t0 = tt * (2 * RG_BM), e0 = et * RG_BN;
   // staging roles: x row r (of 256), K half hf (32 elements); W row rb (of
   // 128), K quarter qb (16 elements)
   const int r = tid >> 1, hf = tid & 1, rb = tid >> 2, qb = tid & 3;

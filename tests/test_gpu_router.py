@@ -52,8 +52,12 @@ def check_router(xbits, W, bias, k):
 
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("decode", 1), ("decode_b8", 8), ("decode", 16),
                                     ("decode", 17), ("decode", 200), ("decode", 1100), ("decode", 2600),
-                                    ("decode", 16400)])
+                                    ("decode", 4000), ("decode", 16400), ("decode", 18332)])
 def test_router_parity(name, T):
+    """Every router kernel: GEMV (T <= 16), split-K tiles (<= 2560), 128-token
+    tiles (< 16384) and 256-token tiles; 4000 and 18332 tokens give tile
+    counts divisible by eight (the XCD-grouped block order) with a ragged
+    last tile, 2600 and 16400 the plain order."""
     say("router", name, T)
     wl = synth.WORKLOADS[name]
     x = synth.activations(wl, T=T, stream=3)
