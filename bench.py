@@ -191,7 +191,8 @@ def stack_decode(layers, dev, reps: int):
     """The full-depth decode stack: one token (then eight) carried through all
     resident layers, each layer with the residual add and its own router with
     logits scaled to N(0, 1) (the 48-layer recipe), each output brought back
-    to the first layer's input RMS (moe_rms_norm) for the next layer; the
+    to the first layer's input RMS for the next layer inside that layer's
+    first kernel (moe_layer_decode_rescaled: three kernels per layer); the
     whole pass captured as one HIP graph.  The experts are the resident
     layers' own."""
     import copy
@@ -208,16 +209,18 @@ def stack_decode(layers, dev, reps: int):
     import quantized_moe_routed_router_amd as moe
     for T in (1, 8):
         fbs = [S.alloc_fused(T) for S in st]
-        xns = [torch.empty((T, swl.H), dtype=torch.int16, device=dev) for _ in st]
         x0 = synth.activations_torch(swl, T, 950 + T, dev).view(torch.int16)
         stream = torch.cuda.Stream()
 
         def chain():
-            x = x0
-            for S, fb, xn in zip(st, fbs, xns):
-                S.forward_fused(x, fb, residual=True, stream=stream)
-                moe.moe_rms_norm(fb["y"], T, swl.H, synth.STACK_INPUT_RMS, xn, stream)
-                x = xn
+            # layer 0 takes the input as is; every later layer brings the
+            # previous output back to the input RMS inside its first kernel
+            S0, fb0 = st[0], fbs[0]
+            S0.forward_fused(x0, fb0, residual=True, stream=stream)
+            y = fb0["y"]
+            for S, fb in zip(st[1:], fbs[1:]):
+                S.forward_stack(y, fb, synth.STACK_INPUT_RMS, stream=stream)
+                y = fb["y"]
 
         with torch.cuda.stream(stream):
             chain()
@@ -247,7 +250,7 @@ def stack_decode(layers, dev, reps: int):
                         "layer_hbm_gbps": round(step_bytes / (ms * 1e-3 / len(st)) / 1e9, 1)}
         log(f"stack {len(st)} layers, {T} token(s): {ms * 1e3:.1f} us per pass, "
             f"{T / ms * 1e3:.0f} tok/s, {distinct:.1f} distinct experts per layer")
-        del fbs, xns, g
+        del fbs, g
         torch.cuda.empty_cache()
     return res
 

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 #define MOE_DECODE_MAX_T 64   /* largest token count moe_expert_ffn_decode takes */
 #define MOE_LAYER_MAX_T 16    /* largest token count moe_layer_decode takes */
 #define MOE_MAX_E 1024
@@ -187,6 +187,24 @@ int moe_layer_decode(const moe_dims* dims, const moe_experts* experts, const uin
                      const float* W_r, const float* bias, int T, int add_residual,
                      uint16_t* y, int32_t* ids, float* w, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* One layer of the full-depth decode stack in the same three kernels as
+ * moe_layer_decode: x_in [T, H] bf16 is the previous layer's output, the
+ * layer's input is x = bf16_rne(x_in * s) with s = target_rms / sqrt(mean_h
+ * x_in^2) per token (fp32, the same fixed-order sum and IEEE division and
+ * square root as moe_rms_norm, so x is bit-identical to moe_rms_norm's
+ * output), and y = bf16_rne(x + sum_i w_i FFN_{ids_i}(x^)) (the residual is
+ * the rescaled input).  The same result as moe_rms_norm followed by
+ * moe_layer_decode with add_residual = 1; at one token the rescale runs
+ * inside the layer's first kernel (one launch fewer), at several tokens a
+ * rescale kernel writes the rows into the workspace first.  The rescale is
+ * the glue this project puts between the 48 stacked layers (not one of the
+ * pages' steps; see moe_rms_norm).  Arguments and workspace as for
+ * moe_layer_decode; target_rms positive and finite. */
+int moe_layer_decode_rescaled(const moe_dims* dims, const moe_experts* experts, const uint16_t* x_in,
+                              float target_rms, const float* W_r, const float* bias, int T,
+                              uint16_t* y, int32_t* ids, float* w, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /* The fused decode layer without a workspace argument, for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving

@@ -79,6 +79,8 @@ _SIGS = {
     "moe_layer_decode_workspace_bytes": (_SZ, [ctypes.POINTER(moe_dims), _I]),
     "moe_layer_decode": (_I, [ctypes.POINTER(moe_dims), ctypes.POINTER(moe_experts), _P, _P, _P, _I,
                               _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_layer_decode_rescaled": (_I, [ctypes.POINTER(moe_dims), ctypes.POINTER(moe_experts), _P,
+                                       ctypes.c_float, _P, _P, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_layer_decode_noalloc": (_I, [ctypes.POINTER(moe_dims), ctypes.POINTER(moe_experts), _P, _P, _P,
                                       _I, _I, _P, _P, _P, _P]),
     "moe_permute": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -246,6 +248,17 @@ def moe_layer_decode(d: moe_dims, experts: dict, x, W_r, bias, T: int, add_resid
     _check(lib().moe_layer_decode(ctypes.byref(d), ctypes.byref(ex), _ptr(x), _ptr(W_r), _ptr(bias),
                                   T, 1 if add_residual else 0, _ptr(y), _ptr(ids), _ptr(w),
                                   _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_layer_decode_rescaled(d: moe_dims, experts: dict, x_in, target_rms: float, W_r, bias, T: int, y,
+                              ids, w, ws, ws_bytes: int, stream=None):
+    """One stack layer: input bf16(x_in * target_rms / rms(x_in)), then the
+    fused layer with the residual add (moe_rms_norm + moe_layer_decode in one
+    call, bit for bit)."""
+    ex = _experts(experts)
+    _check(lib().moe_layer_decode_rescaled(ctypes.byref(d), ctypes.byref(ex), _ptr(x_in), float(target_rms),
+                                           _ptr(W_r), _ptr(bias), T, _ptr(y), _ptr(ids), _ptr(w), _ptr(ws),
+                                           ws_bytes, _stream(stream)))
 
 
 MOE_NOALLOC_SCRATCH_BYTES = 8 << 20

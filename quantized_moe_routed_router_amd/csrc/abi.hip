@@ -290,7 +290,8 @@ namespace {
 // moe_layer_decode_noalloc (which passes the device's scratch array).
 int layer_decode_checked(const char* fn, const moe_dims* d, const moe_experts* ex, const uint16_t* x,
                          const float* W_r, const float* bias, int T, int add_residual, uint16_t* y,
-                         int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream) {
+                         int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream,
+                         float in_rms = 0.0f) {
   int st = check_dims(fn, d);
   if (st) return st;
   if (T < 1 || T > MOE_LAYER_MAX_T)
@@ -316,6 +317,7 @@ int layer_decode_checked(const char* fn, const moe_dims* d, const moe_experts* e
   L.ts_gate = ex->ts_gate; L.ts_up = ex->ts_up; L.ts_down = ex->ts_down;
   L.h_ts = ex->h_ts;
   L.y = y; L.ids_out = ids; L.w_out = w;
+  L.in_rms = in_rms;
   return hip_status(moe::launch_layer_decode(L, ws, as_stream(stream)), fn);
 }
 
@@ -361,6 +363,16 @@ int moe_layer_decode(const moe_dims* d, const moe_experts* ex, const uint16_t* x
                      void* ws, size_t ws_bytes, void* stream) {
   return layer_decode_checked("moe_layer_decode", d, ex, x, W_r, bias, T, add_residual, y, ids, w, ws,
                               ws_bytes, stream);
+}
+
+int moe_layer_decode_rescaled(const moe_dims* d, const moe_experts* ex, const uint16_t* x_in,
+                              float target_rms, const float* W_r, const float* bias, int T, uint16_t* y,
+                              int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_layer_decode_rescaled";
+  if (!(target_rms > 0.0f) || !(target_rms < 3.0e38f))
+    return fail(MOE_ERR_INVALID, "%s: target_rms = %g must be positive and finite", fn, (double)target_rms);
+  if (d && d->H % 8) return fail(MOE_ERR_SHAPE, "%s: H = %d is not a multiple of 8", fn, d->H);
+  return layer_decode_checked(fn, d, ex, x_in, W_r, bias, T, 1, y, ids, w, ws, ws_bytes, stream, target_rms);
 }
 
 int moe_layer_decode_noalloc(const moe_dims* d, const moe_experts* ex, const uint16_t* x,

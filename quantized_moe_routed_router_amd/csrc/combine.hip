@@ -10,11 +10,14 @@ namespace moe {
 
 // One thread per 8 consecutive hidden elements of one token: reads k x 32 B of
 // o and 16 B of residual, writes 16 B of y.
+// res_scale [T] or null: the residual is bf16(residual * res_scale[t]) (the
+// stack's rescaled layer input).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ out,
                                                       const float* __restrict__ w,
                                                       const uint16_t* __restrict__ residual,
                                                       int T, int k, int H,
-                                                      uint16_t* __restrict__ y) {
+                                                      uint16_t* __restrict__ y,
+                                                      const float* __restrict__ res_scale) {
   const int per_row = H / 8;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)T * per_row) return;
@@ -46,6 +49,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
   if (residual) {
     u32x4 r = *reinterpret_cast<const u32x4*>(residual + (size_t)t * H + c * 8);
+    if (res_scale) {
+      const float rs = res_scale[t];
+      r = u32x4{bf16x2_scaled(r.x, rs), bf16x2_scaled(r.y, rs), bf16x2_scaled(r.z, rs), bf16x2_scaled(r.w, rs)};
+    }
     uint32_t rw[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -60,10 +67,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 hipError_t launch_combine(const float* out, const float* w, const uint16_t* residual, int T, int k,
-                          int H, uint16_t* y, hipStream_t s) {
+                          int H, uint16_t* y, hipStream_t s, const float* res_scale) {
   if (T == 0) return hipSuccess;
   const size_t n = (size_t)T * (H / 8);
-  combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(out, w, residual, T, k, H, y);
+  combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(out, w, residual, T, k, H, y, res_scale);
   return hipGetLastError();
 }
 
@@ -76,33 +83,15 @@ hipError_t launch_combine(const float* out, const float* w, const uint16_t* resi
 __global__ __launch_bounds__(256) void rms_norm_kernel(const uint16_t* __restrict__ x, int H,
                                                        float target, uint16_t* __restrict__ y) {
   __shared__ float red[4];
-  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ float rsc[1];
+  const int t = blockIdx.x, tid = threadIdx.x;
   const uint16_t* xr = x + (size_t)t * H;
-  float ss = 0.0f;
+  rows_rms_scales(xr, 1, H, target, tid, red, rsc);
+  const float sc = rsc[0];
   for (int c = tid * 8; c < H; c += 256 * 8) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
-    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = bf16_to_f32(vw[i] & 0xFFFF), b = bf16_to_f32(vw[i] >> 16);
-      ss = fmaf(a, a, ss);
-      ss = fmaf(b, b, ss);
-    }
-  }
-  ss = dpp_wave_sum(ss);
-  if (lane == 0) red[wv] = ss;
-  __syncthreads();
-  const float total = ((red[0] + red[1]) + red[2]) + red[3];
-  const float ms = __fdiv_rn(total, (float)H);
-  const float sc = ms > 0.0f ? __fdiv_rn(target, __fsqrt_rn(ms)) : 0.0f;
-  for (int c = tid * 8; c < H; c += 256 * 8) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
-    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = f32_to_bf16_rne(bf16_to_f32(vw[i] & 0xFFFF) * sc) | (f32_to_bf16_rne(bf16_to_f32(vw[i] >> 16) * sc) << 16);
-    *reinterpret_cast<u32x4*>(y + (size_t)t * H + c) = u32x4{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<u32x4*>(y + (size_t)t * H + c) =
+        u32x4{bf16x2_scaled(v.x, sc), bf16x2_scaled(v.y, sc), bf16x2_scaled(v.z, sc), bf16x2_scaled(v.w, sc)};
   }
 }
 

@@ -108,6 +108,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// bf16_rne(x * s) of a bf16 value (bits), and of both halves of a word.
+__device__ __forceinline__ uint32_t bf16_scaled(uint32_t b, float s) {
+  return f32_to_bf16_rne(bf16_to_f32(b & 0xFFFF) * s);
+}
+__device__ __forceinline__ uint32_t bf16x2_scaled(uint32_t w, float s) {
+  return bf16_scaled(w & 0xFFFF, s) | (bf16_scaled(w >> 16, s) << 16);
+}
+
+
 // Quantize one 16-element block given its row's tensor scale ts (fp32 steps,
 // no contraction): returns the E4M3 scale code and writes 8 code bytes
 // (element 2j in the low nibble of byte j).
@@ -416,6 +425,43 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ lrow, int E,
   *out_w = z / sum;
 }
 
+// Input rescale of the full-depth decode stack (each layer's output brought
+// back to a target RMS before the next layer): s = target / sqrt(mean_h x^2)
+// of bf16 rows, by a 256-thread block, in one fixed order that every caller
+// shares, so the same row gives the same s bits in the standalone rescale
+// kernel, the router blocks and the quantizer blocks: thread t sums the
+// squares of elements 8t .. 8t+7, 8t+2048 .. (fp32 FMAs in element order),
+// then a DPP sum per wave and ((w0 + w1) + w2) + w3; IEEE division and square
+// root; 0 for a zero row.  T rows at once (T <= 16): red holds 4 T floats,
+// rsc receives the T scales (block-uniform after the call).  Every thread of
+// the block must call it.
+__device__ __forceinline__ void rows_rms_scales(const uint16_t* __restrict__ x, int T, int H, float target,
+                                                int tid, float* red, float* rsc) {
+  for (int t = 0; t < T; ++t) {
+    const uint16_t* xr = x + (size_t)t * H;
+    float ss = 0.0f;
+    for (int c = tid * 8; c < H; c += 256 * 8) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+      const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = bf16_to_f32(vw[i] & 0xFFFF), b = bf16_to_f32(vw[i] >> 16);
+        ss = fmaf(a, a, ss);
+        ss = fmaf(b, b, ss);
+      }
+    }
+    ss = dpp_wave_sum(ss);
+    if ((tid & 63) == 0) red[4 * t + (tid >> 6)] = ss;
+  }
+  __syncthreads();
+  if (tid < T) {
+    const float total = ((red[4 * tid] + red[4 * tid + 1]) + red[4 * tid + 2]) + red[4 * tid + 3];
+    const float ms = __fdiv_rn(total, (float)H);
+    rsc[tid] = ms > 0.0f ? __fdiv_rn(target, __fsqrt_rn(ms)) : 0.0f;
+  }
+  __syncthreads();
+}
+
 // One router logit row (expert `row`) for T <= 16 tokens by a 256-thread
 // block: thread t reads float4s t, t+256, ... of the fp32 row (all loads
 // issued first) and the matching bf16 x; fp32 FMAs, a DPP sum per wave and a
@@ -428,7 +474,7 @@ constexpr int RROW_MAXF4 = 4;            // H <= 4096
 template <int TB>
 __device__ __forceinline__ void router_row_tokens(const uint16_t* __restrict__ x,
                                                   const float4_t (&wv)[RROW_MAXF4], int t0, int T,
-                                                  int H, int tid, float* red) {
+                                                  int H, int tid, float* red, const float* rsc) {
   const int nf4 = H / 4;
   u32x2 xb[TB][RROW_MAXF4];
 #pragma unroll
@@ -441,10 +487,15 @@ __device__ __forceinline__ void router_row_tokens(const uint16_t* __restrict__ x
   for (int tt = 0; tt < TB; ++tt) {
     if (t0 + tt >= T) break;
     float acc = 0.0f;
+    const float sc = rsc ? rsc[t0 + tt] : 1.0f;
 #pragma unroll
     for (int i = 0; i < RROW_MAXF4; ++i) {
       const bool ok = tid + 256 * i < nf4;
-      const uint32_t lo = ok ? xb[tt][i].x : 0u, hi = ok ? xb[tt][i].y : 0u;
+      uint32_t lo = ok ? xb[tt][i].x : 0u, hi = ok ? xb[tt][i].y : 0u;
+      if (rsc) {                                         // the rescaled input bf16(x s)
+        lo = bf16x2_scaled(lo, sc);
+        hi = bf16x2_scaled(hi, sc);
+      }
       acc = fmaf(wv[i].x, bf16_to_f32(lo & 0xFFFF), acc);
       acc = fmaf(wv[i].y, bf16_to_f32(lo >> 16), acc);
       acc = fmaf(wv[i].z, bf16_to_f32(hi & 0xFFFF), acc);
@@ -460,20 +511,25 @@ __device__ __forceinline__ void router_row_tokens(const uint16_t* __restrict__ x
 // loads, all issued first) and reads the matching bf16 x of up to eight
 // tokens at once; fp32 FMAs, a DPP sum per wave and a fixed-order sum of the
 // four waves through LDS (red: 4*16 floats).
+// in_rms > 0: the input is rescaled to RMS in_rms per token (the logits are
+// those of bf16(x s)); the scales are taken into rsc (T floats of LDS) while
+// the weight row's loads are in flight.
 __device__ __forceinline__ void router_row_block(const uint16_t* __restrict__ x,
                                                  const float* __restrict__ W,
                                                  const float* __restrict__ bias, int T, int E, int H,
                                                  int row, float* __restrict__ logits, int tid,
-                                                 float* red) {
+                                                 float* red, float in_rms = 0.0f, float* rsc = nullptr) {
   const int nf4 = H / 4;
   float4_t wv[RROW_MAXF4];
   const float4_t* wr = reinterpret_cast<const float4_t*>(W + (size_t)row * H);
 #pragma unroll
   for (int i = 0; i < RROW_MAXF4; ++i) wv[i] = wr[min(tid + 256 * i, nf4 - 1)];
+  if (in_rms > 0.0f) rows_rms_scales(x, T, H, in_rms, tid, red, rsc);
+  else rsc = nullptr;
   if (T == 1) {
-    router_row_tokens<1>(x, wv, 0, T, H, tid, red);
+    router_row_tokens<1>(x, wv, 0, T, H, tid, red, rsc);
   } else {
-    for (int t0 = 0; t0 < T; t0 += 8) router_row_tokens<8>(x, wv, t0, T, H, tid, red);
+    for (int t0 = 0; t0 < T; t0 += 8) router_row_tokens<8>(x, wv, t0, T, H, tid, red, rsc);
   }
   __syncthreads();
   if (tid < T) {
@@ -496,11 +552,13 @@ __device__ __forceinline__ void topk_wave_any(const float* __restrict__ lrow, in
 // thread loads its 16-element blocks once, the row amax goes through DPP and
 // LDS (red: one float per wave), then each thread quantizes its blocks.
 // Every thread of the block must call it.
+// rescale: quantize bf16(x s) instead of x (the stack's rescaled input).
 __device__ __forceinline__ void quantize_row_bf16_block(const uint16_t* __restrict__ xr, int H,
                                                         uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales,
                                                         float* __restrict__ ts_out, int tid,
-                                                        int nthreads, float* red) {
+                                                        int nthreads, float* red,
+                                                        bool rescale = false, float s = 1.0f) {
   constexpr int MAXB = 4;
   const int nblk = H / 16;
   u32x4 raw[MAXB][2];
@@ -511,6 +569,12 @@ __device__ __forceinline__ void quantize_row_bf16_block(const uint16_t* __restri
       const u32x4* p = reinterpret_cast<const u32x4*>(xr + b * 16);
       raw[i][0] = p[0];
       raw[i][1] = p[1];
+      if (rescale) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          raw[i][h] = u32x4{bf16x2_scaled(raw[i][h].x, s), bf16x2_scaled(raw[i][h].y, s),
+                            bf16x2_scaled(raw[i][h].z, s), bf16x2_scaled(raw[i][h].w, s)};
+      }
     }
   }
   float amax = 0.0f;

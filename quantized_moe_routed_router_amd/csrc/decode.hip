@@ -692,7 +692,8 @@ template <bool COMBINE, bool HQ>
 __global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, DecodeWs ws,
                                                                   const float* __restrict__ w_comb,
                                                                   const uint16_t* __restrict__ residual,
-                                                                  uint16_t* __restrict__ y) {
+                                                                  uint16_t* __restrict__ y,
+                                                                  const float* __restrict__ res_scale) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int npairs = a.T * a.k;
   half2_t* hs = reinterpret_cast<half2_t*>(smem);                              // [npairs][I/2]
@@ -717,6 +718,7 @@ __global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, Dec
     // no residual: read y's own column instead (unused), keeping the load unconditional
     const uint16_t* rp = residual ? residual : y;
     res = rp[(size_t)(cidx >> 4) * a.H + n0 + (cidx & 15)];
+    if (res_scale) res = (uint16_t)bf16_scaled(res, res_scale[cidx >> 4]);
   }
   const int item = tid < nitems ? tid : nitems - 1;
   const int jq = item / nblk, jb = item % nblk;
@@ -834,23 +836,37 @@ __global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, Dec
 // Fused layer, kernel 1 (256 threads): blocks 0..E-1 compute one router logit
 // row each (the same routine as the standalone router), the T blocks after
 // them quantize one token row each.
+// in_rms > 0 (the stack's rescaled input, one token): every block takes the
+// token's scale s = in_rms / rms(x) (the shared fixed-order routine, so all
+// blocks agree bit for bit; router blocks while their weight row loads are
+// in flight), the router rows use bf16(x s), the quantizer block quantizes it
+// and stores s for the down step's residual.
 __global__ __launch_bounds__(256) void router_quant_kernel(const uint16_t* __restrict__ x,
                                                            const float* __restrict__ W,
                                                            const float* __restrict__ bias, int T, int E,
                                                            int H, float* __restrict__ logits,
                                                            uint8_t* __restrict__ xc,
                                                            uint8_t* __restrict__ xsc,
-                                                           float* __restrict__ xts) {
+                                                           float* __restrict__ xts, float in_rms,
+                                                           float* __restrict__ xscale) {
   __shared__ float red[64];
+  __shared__ float rsc[MOE_LAYER_MAX_T];
   const int tid = threadIdx.x;
   const int blk = blockIdx.x;
+  const bool rescale = in_rms > 0.0f;
   if (blk >= E) {
     const int t = blk - E;
+    float sc = 1.0f;
+    if (rescale) {
+      rows_rms_scales(x + (size_t)t * H, 1, H, in_rms, tid, red, rsc);
+      sc = rsc[0];
+      if (tid == 0) xscale[t] = sc;
+    }
     quantize_row_bf16_block(x + (size_t)t * H, H, xc + (size_t)t * (H / 2), xsc + (size_t)t * (H / 16),
-                            xts + t, tid, 256, red);
+                            xts + t, tid, 256, red, rescale, sc);
     return;
   }
-  router_row_block(x, W, bias, T, E, H, blk, logits, tid, red);
+  router_row_block(x, W, bias, T, E, H, blk, logits, tid, red, in_rms, rsc);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -895,7 +911,8 @@ static bool decode_h_mode(int T, int npairs, int H, int I) {
 
 template <int MAXP, int PC, bool FUSED>
 static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logits, int32_t* ids_out,
-                               float* w_out, const uint16_t* residual, uint16_t* y, hipStream_t s) {
+                               float* w_out, const uint16_t* residual, uint16_t* y, hipStream_t s,
+                               const float* res_scale = nullptr) {
   const int npairs = a.T * a.k;
   const int KS = dec_ks(a.H, a.T);
   const int nw1 = dec_waves(a.H / 32 / KS);
@@ -914,24 +931,24 @@ static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logit
   if (hm) {
     const size_t lds = slice_lds_bytes(npairs, a.I);
     if (a.h_ts) {                              // static h scale: h^ written by gate/up
-      if (FUSED) down_slice_kernel<true, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y);
-      else down_slice_kernel<false, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
+      if (FUSED) down_slice_kernel<true, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y, res_scale);
+      else down_slice_kernel<false, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr, nullptr);
     } else {
-      if (FUSED) down_slice_kernel<true, true><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y);
-      else down_slice_kernel<false, true><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
+      if (FUSED) down_slice_kernel<true, true><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y, res_scale);
+      else down_slice_kernel<false, true><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr, nullptr);
     }
     return;
   }
   h_quant_decode_kernel<<<npairs, 64 * ((a.I / 4 + 63) / 64), 0, s>>>(a, ws);
   if (slice_fits(npairs, a.H, a.I)) {
     const size_t lds = slice_lds_bytes(npairs, a.I);
-    if (FUSED) down_slice_kernel<true, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y);
-    else down_slice_kernel<false, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr);
+    if (FUSED) down_slice_kernel<true, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y, res_scale);
+    else down_slice_kernel<false, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr, nullptr);
   } else {
     const int nw2 = dec_waves(a.I / 32);
     const size_t lds2 = (size_t)MAXP * a.I * 2 + (size_t)nw2 * MAXP * 64 * 4;
     down_decode_kernel<MAXP, DEC_CPW, PC><<<dim3(npairs, a.H / 64), 64 * nw2, lds2, s>>>(a, ws);
-    if (FUSED) (void)launch_combine(a.out, w_out, residual, a.T, a.k, a.H, y, s);
+    if (FUSED) (void)launch_combine(a.out, w_out, residual, a.T, a.k, a.H, y, s, res_scale);
   }
 }
 
@@ -947,7 +964,7 @@ hipError_t launch_ffn_decode(const FfnArgs& a, void* ws, hipStream_t s) {
 // workspace (gate/up partials, h^), o.
 struct LayerWs {
   float* logits; int32_t* ids; float* w; uint8_t* xc; uint8_t* xs; float* xts;
-  float* gu; float* out;
+  float* gu; float* out; float* xscale; uint16_t* xr;
 };
 
 static LayerWs carve_layer(void* ws, int E, int H, int I, int k, int T, size_t* total) {
@@ -963,6 +980,8 @@ static LayerWs carve_layer(void* ws, int E, int H, int I, int k, int T, size_t* 
   w.xts = (float*)take((size_t)T * 4);
   w.gu = (float*)take(decode_workspace_bytes(E, H, I, k, T));
   w.out = (float*)take((size_t)T * k * H * 4);
+  w.xscale = (float*)take((size_t)T * 4);
+  w.xr = (uint16_t*)take((size_t)T * H * 2);            // rescaled input rows (T > 1)
   if (total) *total = off;
   return w;
 }
@@ -975,7 +994,19 @@ size_t layer_decode_workspace_bytes(int E, int H, int I, int k, int T) {
 
 hipError_t launch_layer_decode(const LayerArgs& L, void* ws, hipStream_t s) {
   LayerWs w = carve_layer(ws, L.E, L.H, L.I, L.k, L.T, nullptr);
-  router_quant_kernel<<<L.E + L.T, 256, 0, s>>>(L.x, L.W_r, L.bias, L.T, L.E, L.H, w.logits, w.xc, w.xs, w.xts);
+  if (L.in_rms > 0.0f && L.T > 1) {
+    // several tokens: every router block would take every token's scale, so
+    // the rows are rescaled once by the standalone kernel (the same routine,
+    // the same bits) and the layer runs on them
+    hipError_t e = launch_rms_norm(L.x, L.T, L.H, L.in_rms, w.xr, s);
+    if (e != hipSuccess) return e;
+    LayerArgs L2 = L;
+    L2.x = w.xr;
+    L2.in_rms = 0.0f;
+    return launch_layer_decode(L2, ws, s);
+  }
+  router_quant_kernel<<<L.E + L.T, 256, 0, s>>>(L.x, L.W_r, L.bias, L.T, L.E, L.H, w.logits, w.xc, w.xs, w.xts,
+                                                L.in_rms, w.xscale);
   FfnArgs a{};
   a.E = L.E; a.H = L.H; a.I = L.I; a.k = L.k; a.T = L.T; a.fmt = FMT_NVFP4;
   a.gate_up = L.gate_up; a.down = L.down;
@@ -987,10 +1018,11 @@ hipError_t launch_layer_decode(const LayerArgs& L, void* ws, hipStream_t s) {
   a.out = w.out;
   DecodeWs dw = carve_decode(w.gu, L.H, L.I, L.T * L.k, nullptr);
   const uint16_t* res = L.residual ? L.x : nullptr;
+  const float* rsc = L.residual && L.in_rms > 0.0f ? w.xscale : nullptr;
   if (L.T == 1)
-    launch_decode_pair<1, 1, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s);
+    launch_decode_pair<1, 1, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s, rsc);
   else
-    launch_decode_pair<4, 8, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s);
+    launch_decode_pair<4, 8, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s, rsc);
   return hipGetLastError();
 }
 

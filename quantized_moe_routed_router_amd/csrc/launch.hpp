@@ -60,6 +60,7 @@ struct LayerArgs {
   uint16_t* y;
   int32_t* ids_out;
   float* w_out;
+  float in_rms;        // > 0: the layer's input is bf16(x s), s = in_rms / rms(x) per token
 };
 size_t layer_decode_workspace_bytes(int E, int H, int I, int k, int T);
 hipError_t launch_layer_decode(const LayerArgs& L, void* ws, hipStream_t s);
@@ -70,8 +71,9 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s);
 // Row-tile height (32, 128 or 256) launch_ffn_prefill uses for these shapes.
 int prefill_tile_rows(int E, int H, int I, int k, int T, int fmt);
 
+// res_scale [T] or null: the residual is bf16(residual * res_scale[t]).
 hipError_t launch_combine(const float* out, const float* w, const uint16_t* residual, int T, int k,
-                          int H, uint16_t* y, hipStream_t s);
+                          int H, uint16_t* y, hipStream_t s, const float* res_scale = nullptr);
 hipError_t launch_rms_norm(const uint16_t* x, int T, int H, float target, uint16_t* y, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 

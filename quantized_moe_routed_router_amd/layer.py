@@ -18,7 +18,8 @@ import torch
 
 from . import (MOE_FMT_CB3G128, MOE_FMT_NVFP4, dims, moe_combine,
                moe_expert_ffn_decode, moe_expert_ffn_prefill, moe_ffn_workspace_bytes,
-               moe_layer_decode, moe_layer_decode_workspace_bytes, moe_pack_codebook,
+               moe_layer_decode, moe_layer_decode_rescaled, moe_layer_decode_workspace_bytes,
+               moe_pack_codebook,
                moe_pack_nvfp4, moe_packed_bytes, moe_quantize_act, moe_quantize_weights,
                moe_router_topk)
 
@@ -151,4 +152,13 @@ class Layer:
         xb = x.view(torch.int16) if x.dtype == torch.bfloat16 else x
         moe_layer_decode(self.d, self.experts(), xb, self.W_r, self.bias, b["T"], residual,
                          b["y"], b["ids"], b["w"], b["ws"], b["ws_bytes"], stream)
+        return b["y"]
+
+    def forward_stack(self, x_in: torch.Tensor, b: dict, target_rms: float, stream=None):
+        """One layer of the stack: x_in (the previous layer's output) brought
+        back to target_rms per token, then the fused layer with the residual
+        add (moe_rms_norm + forward_fused in one call, bit for bit)."""
+        xb = x_in.view(torch.int16) if x_in.dtype == torch.bfloat16 else x_in
+        moe_layer_decode_rescaled(self.d, self.experts(), xb, target_rms, self.W_r, self.bias, b["T"],
+                                  b["y"], b["ids"], b["w"], b["ws"], b["ws_bytes"], stream)
         return b["y"]

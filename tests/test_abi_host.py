@@ -26,7 +26,7 @@ def test_library_exports_every_header_function():
     for n in names:
         assert hasattr(L, n), n
     assert sorted(names) == m.exported_symbols()
-    assert m.moe_abi_version() == 6
+    assert m.moe_abi_version() == 7
 
 
 def test_sizes():

@@ -7,7 +7,9 @@ router logits scaled to N(0, 1) so routing is near uniform.
 Every layer: ids distinct and in range, w a renormalised softmax, y finite.
 Sampled layers: the fused layer equals the separate entry points bit for
 bit, the router agrees with the oracle outside near-ties, and every stage
-(h, h^, o, y) matches the oracle on that layer's actual input."""
+(h, h^, o, y) matches the oracle on that layer's actual input.  The stack
+with the rescale folded into each layer's first kernel
+(moe_layer_decode_rescaled) equals the separate sequence bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -59,6 +61,34 @@ def run_stack(cases, x0):
     return ins, outs
 
 
+def run_stack_rescaled(cases, x0):
+    """The same stack with the rescale folded into each later layer's first
+    kernel (moe_layer_decode_rescaled); returns each layer's fused outputs."""
+    T, H = x0.shape
+    outs = []
+    y = bf16_tensor(x0, DEV)
+    for li, c in enumerate(cases):
+        fb = c.L.alloc_fused(T)
+        fb["ws"].fill_(0xFF)
+        if li == 0:
+            c.L.forward_fused(y, fb, residual=True)
+        else:
+            c.L.forward_stack(y, fb, synth.STACK_INPUT_RMS)
+        y = fb["y"]
+        outs.append(fb)
+    torch.cuda.synchronize()
+    return [{k: t2n(v) for k, v in fb.items() if isinstance(v, torch.Tensor) and k != "ws"} for fb in outs]
+
+
+def check_rescaled_equal(cases, x0, outs):
+    """The folded rescale gives every layer's ids, weights and y bit for bit."""
+    outs_r = run_stack_rescaled(cases, x0)
+    for li, (f, g) in enumerate(zip(outs, outs_r)):
+        assert np.array_equal(f["ids"], g["ids"]), li
+        assert np.array_equal(f["w"].view(np.uint32), g["w"].view(np.uint32)), li
+        assert np.array_equal(f["y"], g["y"]), li
+
+
 def check_properties(ins, outs, k, E):
     for li, (x, f) in enumerate(zip(ins, outs)):
         ids, w = f["ids"], f["w"]
@@ -93,6 +123,7 @@ def test_stack48_one_token(stack):
     x0 = synth.activations(WL, T=1, stream=900)
     ins, outs = run_stack(stack, x0)
     check_properties(ins, outs, WL.k, WL.E)
+    check_rescaled_equal(stack, x0, outs)
     check_sampled(stack, ins, outs)
     rms = [float(np.sqrt(np.mean(synth.bf16_bits_to_f32(f["y"].view(np.uint16)).astype(np.float64) ** 2)))
            for f in outs]
@@ -105,7 +136,8 @@ def test_stack48_eight_tokens(stack):
     x0 = synth.activations(WL, T=8, stream=901)
     ins, outs = run_stack(stack, x0)
     check_properties(ins, outs, WL.k, WL.E)
-    check_sampled(stack, ins, outs, check_tokens=[0, 5])
+    check_rescaled_equal(stack, x0, outs)
+    check_sampled(stack, ins, outs)
     distinct = [len(np.unique(f["ids"])) for f in outs]
     say("stack48 B=8 distinct experts per layer: mean", float(np.mean(distinct)), "min", min(distinct))
     assert np.mean(distinct) > 60                        # near-uniform routing: ~74.7 expected
