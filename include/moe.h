@@ -115,8 +115,8 @@ typedef struct moe_ffn_debug {
 /* Hot path                                                            */
 /* ------------------------------------------------------------------ */
 
-/* Router (blog "Capy Flash ...", section "Where the experts live": every
- * token activates a subset of the experts; ranking per the forum repost,
+/* Router (blog "Capy Flash ...", section "Where the experts live": each
+ * token runs only some of the experts; rank order per the forum repost,
  * "Where it stands").
  *   logits[t, e] = sum_h x[t, h] * W_r[e, h] (+ bias[e])   fp32
  *   keep the k largest (ties to the lower id), in descending order
@@ -254,15 +254,21 @@ size_t moe_ffn_workspace_bytes(const moe_dims* dims, int T, int prefill);
  * weights for all E experts; 0 on invalid dims. */
 size_t moe_packed_bytes(const moe_dims* dims, int which);
 
-/* NVFP4 weight quantizer, batched over n_mat matrices of [rows, cols], each
- * with its own tensor scale (one expert projection each).
+/* NVFP4 weight quantizer (the experts' weight format: release post
+ * "capy-flash v0.7.1 ...", section "What shipped", NVFP4 experts; the format's
+ * steps as at the top of this header), batched over n_mat matrices of
+ * [rows, cols], each with its own tensor scale (one expert projection each).
  * W [n_mat, rows, cols] fp32 -> codes [n_mat, rows, cols/2],
  * scales [n_mat, rows, cols/16], ts [n_mat].  cols % 16 == 0.
  * Bit-exact with the fp32 step definition.  ts is also used as scratch. */
 int moe_quantize_weights(const float* W, int n_mat, int rows, int cols,
                          uint8_t* codes, uint8_t* scales, float* ts, void* stream);
 
-/* Write experts e0 .. e0+n-1 of a layer into the packed layouts.
+/* Write experts e0 .. e0+n-1 of a layer into the packed layouts (the resident
+ * expert weights: release post, section "What shipped": every layer's routed
+ * experts with gate/up weights and down projections; here all of them stay in
+ * device memory, where the pages split them between host RAM and a GPU
+ * cache).
  * Plain inputs per expert, NVFP4 (codes element 2j in the low nibble):
  *   gate/up codes [n, I, H/2], scales [n, I, H/16];
  *   down codes [n, H, I/2], scales [n, H, I/16].
@@ -292,8 +298,11 @@ int moe_pack_codebook(const moe_dims* dims, int e0, int n,
                       const uint16_t* up_cb, const uint8_t* up_idx,
                       void* gate_up, void* stream);
 
-/* Stable token-by-expert counting sort of the T*k (t, slot) pairs, flat
- * index i = t*k + slot: counts [E], offsets [E+1] (exclusive prefix sum),
+/* Stable token-by-expert counting sort of the T*k (t, slot) pairs (each
+ * expert then runs over the tokens routed to it, as a batch: the routing of
+ * the blog "Capy Flash ...", section "Where the experts live", grouped by
+ * expert id as in the release post, section "Why it matters"), flat index
+ * i = t*k + slot: counts [E], offsets [E+1] (exclusive prefix sum),
  * perm [T*k] (perm[j] = i at sorted position j, sorted by (expert, i)),
  * inv [T*k] (inv[perm[j]] = j).  ws: moe_permute_workspace_bytes bytes. */
 size_t moe_permute_workspace_bytes(int T, int k, int E);

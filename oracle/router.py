@@ -1,9 +1,9 @@
 """Softmax top-k router (test infrastructure only).
 
-The pages say every token activates a subset of the experts (blog "Capy
-Flash ... two consumer GPUs", section "Where the experts live") and that the
-engine computes every expert the model picks, ranked (forum repost,
-paragraph "Where it stands").  The router computed here: fp32-exact logits of
+Each token runs only some of the experts (blog "Capy Flash ... two consumer
+GPUs", section "Where the experts live"), and the engine computes all of the
+experts the model picks, in rank order (forum repost, paragraph "Where it
+stands").  The router computed here: fp32-exact logits of
 the unquantized bf16 activations against fp32 router weights (plus an optional
 per-expert bias), softmax over all experts, keep the k largest, renormalise.
 Renormalising the top-k of a softmax is the softmax over the k selected

@@ -1,9 +1,9 @@
 // Softmax top-k router: fp32 logits of the bf16 hidden state against fp32
 // router weights (+ optional per-expert bias), then per token the k largest
 // logits (ties to the lower expert id) and their softmax renormalised over the
-// selected k.  The pages: every token activates a subset of the experts (blog
-// "Capy Flash ...", section "Where the experts live"); picked experts are
-// ranked (forum repost, paragraph "Where it stands").
+// selected k.  Each token runs only some of the experts (blog "Capy Flash
+// ...", section "Where the experts live"); the picked experts come in rank
+// order (forum repost, paragraph "Where it stands").
 #include "../../include/moe.h"
 #include "common.hpp"
 #include "launch.hpp"
