@@ -181,7 +181,24 @@ def prefill_runs(L0, dev, steps: int, want=("zipf8k", "nvfp4_64k", "codebook_64k
         cb.set_router(W_r)
         ms, ffn_ms, b = time_prefill(cb, x, wl.T, steps, stream)
         res["codebook_gate_up"] = prefill_record("64k codebook", wl.T, k, E, H, I, ms, ffn_ms)
-        del b, cb
+        del b
+        torch.cuda.empty_cache()
+        # the same codebook layer decoding one token per step (the fused
+        # three-kernel layer, 64 fresh tokens cycled, 100 steps in one graph):
+        # one layer's 1.3 GB of experts, so a step's experts may hit the
+        # 256 MB Infinity Cache somewhat more often than in the 48-layer cycle
+        dwl = synth.WORKLOADS["decode"]
+        cb.set_router(synth.router_weights_torch(dwl, 0, dev))
+        xs1 = [synth.activations_torch(dwl, 1, s, dev).view(torch.int16) for s in range(64)]
+        fb = cb.alloc_fused(1)
+        g = decode_graph(lambda i: cb.forward_fused(xs1[i % 64], fb, residual=True, stream=stream), 100, stream)
+        with torch.cuda.stream(stream):
+            g.replay()
+        us = time_graph(g, 1, stream) * 1e3 / 100
+        res["codebook_decode_b1"] = {"us_per_step": round(us, 3), "tok_s": round(1e6 / us, 1),
+                                     "path": "moe_layer_decode, codebook gate/up GEMV"}
+        log(f"codebook decode, one token: {us:.2f} us/step")
+        del g, fb, cb
         torch.cuda.empty_cache()
     L0.set_router(W_save, b_save)
     return res

@@ -146,7 +146,10 @@ int moe_quantize_act(const uint16_t* x, int T, int H, uint8_t* codes,
  * matters": W4A4).  Each distinct expert's weights are read once per call.
  * out [T, k, H] fp32.  ws: device workspace of at least
  * moe_ffn_workspace_bytes(dims, T, 0) bytes (contents need not be
- * initialised).  dbg may be NULL.  NVFP4 gate/up only. */
+ * initialised).  dbg may be NULL.  Both gate/up formats; the codebook format
+ * needs whole 128-element groups per K split (H / 128 divisible by the split
+ * count, 1 at one token up to H = 2560, else 2 or 4) and is refused with
+ * MOE_ERR_UNSUPPORTED otherwise (the prefill entry takes every shape). */
 int moe_expert_ffn_decode(const moe_dims* dims, const moe_experts* experts,
                           const moe_actq* xq, const int32_t* ids, int T, float* out,
                           void* ws, size_t ws_bytes, const moe_ffn_debug* dbg,
@@ -181,7 +184,8 @@ int moe_ffn_prefill_tile_rows(const moe_dims* dims, int T);
  * y [T, H] bf16 out; ids [T, k] int32 and w [T, k] fp32 outputs, or NULL.
  * ws: at least moe_layer_decode_workspace_bytes(dims, T) bytes (contents
  * need not be initialised); calls sharing a workspace must not overlap.
- * NVFP4 gate/up only; H % 256 == 0, H <= 4096, I <= 2560. */
+ * Both gate/up formats (as moe_expert_ffn_decode); H % 256 == 0, H <= 4096,
+ * I <= 2560. */
 size_t moe_layer_decode_workspace_bytes(const moe_dims* dims, int T);
 int moe_layer_decode(const moe_dims* dims, const moe_experts* experts, const uint16_t* x,
                      const float* W_r, const float* bias, int T, int add_residual,

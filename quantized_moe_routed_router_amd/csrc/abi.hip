@@ -267,8 +267,10 @@ int moe_expert_ffn_decode(const moe_dims* d, const moe_experts* ex, const moe_ac
     return fail(MOE_ERR_SHAPE, "%s: T = %d outside [1, %d]", fn, T, MOE_DECODE_MAX_T);
   int st = check_ffn(fn, d, ex, xq, ids, T, out, ws, ws_bytes, dbg, false);
   if (st) return st;
-  if (d->fmt_gate_up != MOE_FMT_NVFP4)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: gate/up format %d is prefill-only", fn, d->fmt_gate_up);
+  if (!moe::decode_fmt_ok(d->H, T, d->fmt_gate_up))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: codebook gate/up at H = %d, T = %d: the decode kernels need whole "
+                "128-element groups per K split and at most 3 groups per wave (use moe_expert_ffn_prefill)",
+                fn, d->H, T);
   if (T > 1 && d->H > 3072)
     return fail(MOE_ERR_SHAPE, "%s: H = %d above 3072 needs T = 1 (activation staging is 8*H*2 bytes of LDS)", fn, d->H);
   if (d->H > 10240 || d->I > 2560)
@@ -296,15 +298,17 @@ int layer_decode_checked(const char* fn, const moe_dims* d, const moe_experts* e
   if (st) return st;
   if (T < 1 || T > MOE_LAYER_MAX_T)
     return fail(MOE_ERR_SHAPE, "%s: T = %d outside [1, %d]", fn, T, MOE_LAYER_MAX_T);
-  if (d->fmt_gate_up != MOE_FMT_NVFP4)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: gate/up format %d is prefill-only", fn, d->fmt_gate_up);
+  if (!moe::decode_fmt_ok(d->H, T, d->fmt_gate_up))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: codebook gate/up at H = %d, T = %d: the decode kernels need whole "
+                "128-element groups per K split and at most 3 groups per wave", fn, d->H, T);
   if (d->H % 256 || d->H > 4096)
     return fail(MOE_ERR_SHAPE, "%s: H = %d must be a multiple of 256 and <= 4096", fn, d->H);
   if (d->I > 2560) return fail(MOE_ERR_SHAPE, "%s: I = %d above 2560", fn, d->I);
   if (T > 1 && d->H > 3072)
     return fail(MOE_ERR_SHAPE, "%s: H = %d above 3072 needs T = 1", fn, d->H);
   if (!ex) return fail(MOE_ERR_INVALID, "%s: experts is NULL", fn);
-  NEED_PTR(ex->gate_up); NEED_PTR(ex->down); NEED_PTR(ex->ts_gate); NEED_PTR(ex->ts_up); NEED_PTR(ex->ts_down);
+  NEED_PTR(ex->gate_up); NEED_PTR(ex->down); NEED_PTR(ex->ts_down);
+  if (d->fmt_gate_up == MOE_FMT_NVFP4) { NEED_PTR(ex->ts_gate); NEED_PTR(ex->ts_up); }
   OPT_PTR(ex->h_ts);
   NEED_PTR(x); NEED_PTR(W_r); OPT_PTR(bias); NEED_PTR(y); OPT_PTR(ids); OPT_PTR(w); NEED_PTR(ws);
   const size_t need = moe::layer_decode_workspace_bytes(d->E, d->H, d->I, d->k, T);
@@ -318,6 +322,7 @@ int layer_decode_checked(const char* fn, const moe_dims* d, const moe_experts* e
   L.h_ts = ex->h_ts;
   L.y = y; L.ids_out = ids; L.w_out = w;
   L.in_rms = in_rms;
+  L.fmt = d->fmt_gate_up;
   return hip_status(moe::launch_layer_decode(L, ws, as_stream(stream)), fn);
 }
 

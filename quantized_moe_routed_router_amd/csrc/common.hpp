@@ -717,4 +717,40 @@ __device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
+// 32 codebook elements: 3-bit indices from three bit-plane words (bit b of
+// plane p = bit p of element b's index), 8 fp16 entries in cb (4 dwords).
+// The table is split into the entries' low bytes and high bytes (8 bytes
+// each), so one byte permute looks up a byte of two elements.  Per four
+// elements, each plane's 4 bits are spread to the bytes of a word by one
+// 24-bit multiply and a mask, and the three planes merge into the four
+// indices as bytes; per two elements, two permutes of those bytes make the
+// lookup selectors ({i_a, 12, i_b, 12} and {12, i_a, 12, i_b}: selector 12
+// gives a zero byte), two permutes of the table halves give the low and the
+// high bytes, and an OR joins them into two fp16 values.
+__device__ __forceinline__ uint32_t spread4_bytes(uint32_t plane, int shift) {
+  // bits 0..3 of (plane >> shift) -> bit 0 of bytes 0..3 (x * (1 + 2^7 + 2^14 + 2^21))
+  return __umul24((plane >> shift) & 0xFu, 0x204081u) & 0x01010101u;
+}
+
+__device__ __forceinline__ void dequant32_cb(uint32_t p0, uint32_t p1, uint32_t p2, u32x4 cb,
+                                             half2_t (&o)[16]) {
+  // low bytes of entries 0..3 / 4..7 and high bytes of entries 0..3 / 4..7
+  const uint32_t tlo0 = __builtin_amdgcn_perm(cb.y, cb.x, 0x06040200u);
+  const uint32_t tlo1 = __builtin_amdgcn_perm(cb.w, cb.z, 0x06040200u);
+  const uint32_t thi0 = __builtin_amdgcn_perm(cb.y, cb.x, 0x07050301u);
+  const uint32_t thi1 = __builtin_amdgcn_perm(cb.w, cb.z, 0x07050301u);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t idx = spread4_bytes(p0, 4 * j) | (spread4_bytes(p1, 4 * j) << 1) |
+                         (spread4_bytes(p2, 4 * j) << 2);          // byte m: index of element 4j+m
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t sel_lo = __builtin_amdgcn_perm(0x0C0C0C0Cu, idx, q ? 0x04030402u : 0x04010400u);
+      const uint32_t sel_hi = __builtin_amdgcn_perm(0x0C0C0C0Cu, idx, q ? 0x03040204u : 0x01040004u);
+      const uint32_t word = __builtin_amdgcn_perm(tlo1, tlo0, sel_lo) | __builtin_amdgcn_perm(thi1, thi0, sel_hi);
+      o[2 * j + q] = *reinterpret_cast<const half2_t*>(&word);
+    }
+  }
+}
+
 }  // namespace moe

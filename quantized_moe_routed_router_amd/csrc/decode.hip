@@ -195,6 +195,103 @@ __device__ __forceinline__ float dot_chunks_row(const u32x4 (&cw)[CPW], const ui
   return acc;
 }
 
+// ---- gate/up weights in either format, held in registers per wave
+// NVFP4 (FMT 0): CPW chunks of 32 elements (16 code bytes + 2 scale bytes per
+// lane).  Codebook (FMT 1): CB_GPW groups of 128 elements (three 16-byte
+// bit-planes of 3-bit indices + eight fp16 entries per lane); a weight is
+// its group's entry, with no block or tensor scale.
+constexpr int CB_GPW = 3;
+template <int FMT, int CPW> struct GuRegs;
+template <int CPW> struct GuRegs<0, CPW> {
+  u32x4 cw[CPW];
+  uint32_t sw[CPW];
+};
+template <int CPW> struct GuRegs<1, CPW> {
+  u32x4 p[CB_GPW][3];
+  u32x4 c[CB_GPW];
+};
+// K elements per work unit of a wave (a chunk or a group)
+template <int FMT> __host__ __device__ constexpr int gu_unit() { return FMT == 1 ? 128 : 32; }
+
+// Groups g0 .. g0+ng-1 of a codebook tile, straight-line (slots past ng
+// re-read group g0, a cache hit, never used).
+__device__ __forceinline__ void load_groups(const uint8_t* __restrict__ tile, int K, int g0, int ng,
+                                            int lane, u32x4 (&p)[CB_GPW][3], u32x4 (&c)[CB_GPW]) {
+  const int glast = K / 128 - 1;
+#pragma unroll
+  for (int i = 0; i < CB_GPW; ++i) {
+    const int g = min(i < ng ? g0 + i : g0, glast);
+    const uint8_t* grp = tile + (size_t)g * cb_group_bytes();
+    const u32x4* pl = reinterpret_cast<const u32x4*>(grp + lane * 48);
+    p[i][0] = pl[0];
+    p[i][1] = pl[1];
+    p[i][2] = pl[2];
+    c[i] = *reinterpret_cast<const u32x4*>(grp + 64 * 48 + lane * 16);
+  }
+}
+
+template <int FMT, int CPW>
+__device__ __forceinline__ void gu_load(GuRegs<FMT, CPW>& R, const uint8_t* __restrict__ tile, int K, int u0,
+                                        int nu, int lane) {
+  if constexpr (FMT == 1) load_groups(tile, K, u0, nu, lane, R.p, R.c);
+  else load_chunks<CPW>(tile, K, u0, nu, lane, R.cw, R.sw);
+}
+
+// sum over one codebook group of entry * activation (f16 products exact in
+// fp32, fp32 accumulation), four independent chains
+__device__ __forceinline__ float group_dot(const u32x4 (&p)[3], u32x4 c, const half2_t* __restrict__ xs) {
+  float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    half2_t w[16];
+    dequant32_cb(p[0][d], p[1][d], p[2][d], c, w);
+    const u32x4* xp = reinterpret_cast<const u32x4*>(xs + 16 * d);
+    half2_t x[16];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4*>(&x[4 * r]) = xp[r];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) b[d] = dot2(w[j], x[j], b[d]);
+  }
+  return (b[0] + b[1]) + (b[2] + b[3]);
+}
+
+// One activation row: units past nu count 0 (their loads were clamped).
+template <int FMT, int CPW>
+__device__ __forceinline__ float gu_dot_row(const GuRegs<FMT, CPW>& R, int u0, int nu, int K,
+                                            const half2_t* __restrict__ act) {
+  if constexpr (FMT == 1) {
+    const int glast = K / 128 - 1;
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CB_GPW; ++i) {
+      const float gsum = group_dot(R.p[i], R.c[i], act + (size_t)min(u0 + i, glast) * 64);
+      acc += i < nu ? gsum : 0.0f;
+    }
+    return acc;
+  } else {
+    return dot_chunks_row<CPW>(R.cw, R.sw, u0, nu, K / 32 - 1, act);
+  }
+}
+
+// acc[q] += dot with activation row slot[q] (wave-uniform slots).
+template <int FMT, int CPW, int MAXP>
+__device__ __forceinline__ void gu_dot(const GuRegs<FMT, CPW>& R, int u0, int nu, int n,
+                                       const half2_t* __restrict__ act, int act_stride,
+                                       const int (&slot)[MAXP], float (&acc)[MAXP]) {
+  if constexpr (FMT == 1) {
+#pragma unroll
+    for (int i = 0; i < CB_GPW; ++i) {
+      if (i < nu) {
+#pragma unroll
+        for (int q = 0; q < MAXP; ++q)
+          if (q < n) acc[q] += group_dot(R.p[i], R.c[i], act + (size_t)slot[q] * act_stride + (size_t)(u0 + i) * 64);
+      }
+    }
+  } else {
+    dot_chunks<CPW, MAXP>(R.cw, R.sw, u0, nu, n, act, act_stride, slot, acc);
+  }
+}
+
 // All pair ids of the call in registers (lane l holds pair l + 64 i, PC
 // chunks of 64 pairs: 1 for one token, 8 up to 16 tokens, 32 up to 64), so
 // the owner test and the pair lists come from ballots, not dependent loads.
@@ -296,7 +393,7 @@ struct DecodeWs {
 // ---------------------------------------------------------------- gate/up
 // TOPK: rank the router logits in-block first (fused layer), writing ids and
 // w once (block 0,0,0); otherwise read ids.
-template <int MAXP, int CPW, bool TOPK, int PC>
+template <int MAXP, int CPW, bool TOPK, int PC, int FMT>
 __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
     FfnArgs a, DecodeWs ws, const float* __restrict__ logits, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out, int hmode) {
@@ -381,14 +478,15 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
     }
     return;
   }
-  const uint8_t* tile = a.gate_up + (size_t)e * gate_up_expert_bytes(a.H, a.I) + (size_t)j * tile_bytes(a.H);
-  const int nchunk_b = a.H / 32 / KS;
-  const int cpw = (nchunk_b + nw - 1) / nw;
-  const int c0 = split * nchunk_b + wv * cpw;
-  const int nc = max(0, min(cpw, nchunk_b - wv * cpw));
-  u32x4 cw[CPW];
-  uint32_t sw[CPW];
-  load_chunks<CPW>(tile, a.H, c0, nc, lane, cw, sw);          // all weight loads in flight
+  const uint8_t* tile = FMT == 1
+      ? a.gate_up + (size_t)e * cb_gate_up_expert_bytes(a.H, a.I) + (size_t)j * cb_tile_bytes(a.H)
+      : a.gate_up + (size_t)e * gate_up_expert_bytes(a.H, a.I) + (size_t)j * tile_bytes(a.H);
+  const int nunit_b = a.H / gu_unit<FMT>() / KS;                // chunks or groups of this block
+  const int upw = (nunit_b + nw - 1) / nw;
+  const int c0 = split * nunit_b + wv * upw;
+  const int nc = max(0, min(upw, nunit_b - wv * upw));
+  GuRegs<FMT, CPW> R;
+  gu_load<FMT, CPW>(R, tile, a.H, c0, nc, lane);              // all weight loads in flight
   if (by_token) {
     if (!TOPK && MAXP == 1) {
       act_store(xr, a.x_codes, a.x_scales, xtot, xs, tid, blockDim.x);
@@ -412,10 +510,10 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
     // expert has the same x, so the dots run once, straight-line, and the
     // partial goes to each such pair; tensor scales load per lane beside
     // the weights
-    const float tsw = (lane < 32 ? a.ts_gate : a.ts_up)[e];
+    const float tsw = FMT == 1 ? 1.0f : (lane < 32 ? a.ts_gate : a.ts_up)[e];
     const float xts = a.x_ts[lane < a.T ? lane : a.T - 1];
     __syncthreads();                                           // x^ staged
-    const float acc = dot_chunks_row<CPW>(cw, sw, c0, nc, a.H / 32 - 1, xs);
+    const float acc = gu_dot_row<FMT, CPW>(R, c0, nc, a.H, xs);
     red[wv * 64 + lane] = acc;
     __syncthreads();
     if (wv == 0) {
@@ -505,7 +603,7 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
       float acc[MAXP];
   #pragma unroll
       for (int i = 0; i < MAXP; ++i) acc[i] = 0.0f;
-      dot_chunks<CPW, MAXP>(cw, sw, c0, nc, n, xs, a.H / 2, slot, acc);
+      gu_dot<FMT, CPW, MAXP>(R, c0, nc, n, xs, a.H / 2, slot, acc);
   #pragma unroll
       for (int i = 0; i < MAXP; ++i) red[(wv * MAXP + i) * 64 + lane] = acc[i];
       __syncthreads();
@@ -516,7 +614,7 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void gate_up_decode_kernel(
           // lane < 32: gate row 32j + lane; lane >= 32: up row 32j + lane - 32;
           // the partial carries its tensor scales (x row, weight matrix)
           const int q = list[i];
-          const float sc = a.x_ts[q / a.k] * (lane < 32 ? a.ts_gate[e] : a.ts_up[e]);
+          const float sc = a.x_ts[q / a.k] * (FMT == 1 ? 1.0f : (lane < 32 ? a.ts_gate[e] : a.ts_up[e]));
           gu[(size_t)q * 2 * a.I + (lane >> 5) * a.I + 32 * j + (lane & 31)] = v * sc;
         }
       }
@@ -909,7 +1007,18 @@ static bool decode_h_mode(int T, int npairs, int H, int I) {
          I / 32 <= 64;
 }
 
-template <int MAXP, int PC, bool FUSED>
+// Whether the decode kernels take these shapes in gate/up format fmt: the
+// codebook format needs whole 128-element groups per K-split and at most
+// CB_GPW groups per wave.
+bool decode_fmt_ok(int H, int T, int fmt) {
+  if (fmt != FMT_CB3G128) return true;
+  const int KS = dec_ks(H, T);
+  if ((H / 128) % KS) return false;
+  const int nw = dec_waves(H / 32 / KS);
+  return (H / 128 / KS + nw - 1) / nw <= CB_GPW;
+}
+
+template <int MAXP, int PC, bool FUSED, int FMT>
 static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logits, int32_t* ids_out,
                                float* w_out, const uint16_t* residual, uint16_t* y, hipStream_t s,
                                const float* res_scale = nullptr) {
@@ -924,9 +1033,9 @@ static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logit
   // them once in the top-k kernel first.
   if constexpr (FUSED && MAXP > 1) {
     (void)launch_topk(logits, a.T, a.E, a.k, ids_out, w_out, s);
-    gate_up_decode_kernel<MAXP, DEC_CPW, false, PC><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out, hm);
+    gate_up_decode_kernel<MAXP, DEC_CPW, false, PC, FMT><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out, hm);
   } else {
-    gate_up_decode_kernel<MAXP, DEC_CPW, FUSED, PC><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out, hm);
+    gate_up_decode_kernel<MAXP, DEC_CPW, FUSED, PC, FMT><<<dim3(npairs, a.I / 32, KS), 64 * nw1, lds1, s>>>(a, ws, logits, ids_out, w_out, hm);
   }
   if (hm) {
     const size_t lds = slice_lds_bytes(npairs, a.I);
@@ -952,11 +1061,17 @@ static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logit
   }
 }
 
+template <int FMT>
+static void launch_ffn_decode_fmt(const FfnArgs& a, DecodeWs w, hipStream_t s) {
+  if (a.T == 1) launch_decode_pair<1, 1, false, FMT>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
+  else if (a.T * a.k <= 512) launch_decode_pair<4, 8, false, FMT>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
+  else launch_decode_pair<4, 32, false, FMT>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
+}
+
 hipError_t launch_ffn_decode(const FfnArgs& a, void* ws, hipStream_t s) {
   DecodeWs w = carve_decode(ws, a.H, a.I, a.T * a.k, nullptr);
-  if (a.T == 1) launch_decode_pair<1, 1, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
-  else if (a.T * a.k <= 512) launch_decode_pair<4, 8, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
-  else launch_decode_pair<4, 32, false>(a, w, nullptr, nullptr, nullptr, nullptr, nullptr, s);
+  if (a.fmt == FMT_CB3G128) launch_ffn_decode_fmt<1>(a, w, s);
+  else launch_ffn_decode_fmt<0>(a, w, s);
   return hipGetLastError();
 }
 
@@ -1008,7 +1123,7 @@ hipError_t launch_layer_decode(const LayerArgs& L, void* ws, hipStream_t s) {
   router_quant_kernel<<<L.E + L.T, 256, 0, s>>>(L.x, L.W_r, L.bias, L.T, L.E, L.H, w.logits, w.xc, w.xs, w.xts,
                                                 L.in_rms, w.xscale);
   FfnArgs a{};
-  a.E = L.E; a.H = L.H; a.I = L.I; a.k = L.k; a.T = L.T; a.fmt = FMT_NVFP4;
+  a.E = L.E; a.H = L.H; a.I = L.I; a.k = L.k; a.T = L.T; a.fmt = L.fmt;
   a.gate_up = L.gate_up; a.down = L.down;
   a.ts_gate = L.ts_gate; a.ts_up = L.ts_up; a.ts_down = L.ts_down; a.h_ts = L.h_ts;
   a.x_codes = w.xc; a.x_scales = w.xs; a.x_ts = w.xts;
@@ -1019,10 +1134,13 @@ hipError_t launch_layer_decode(const LayerArgs& L, void* ws, hipStream_t s) {
   DecodeWs dw = carve_decode(w.gu, L.H, L.I, L.T * L.k, nullptr);
   const uint16_t* res = L.residual ? L.x : nullptr;
   const float* rsc = L.residual && L.in_rms > 0.0f ? w.xscale : nullptr;
-  if (L.T == 1)
-    launch_decode_pair<1, 1, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s, rsc);
-  else
-    launch_decode_pair<4, 8, true>(a, dw, w.logits, ids_out, w_out, res, L.y, s, rsc);
+  if (L.fmt == FMT_CB3G128) {
+    if (L.T == 1) launch_decode_pair<1, 1, true, 1>(a, dw, w.logits, ids_out, w_out, res, L.y, s, rsc);
+    else launch_decode_pair<4, 8, true, 1>(a, dw, w.logits, ids_out, w_out, res, L.y, s, rsc);
+  } else {
+    if (L.T == 1) launch_decode_pair<1, 1, true, 0>(a, dw, w.logits, ids_out, w_out, res, L.y, s, rsc);
+    else launch_decode_pair<4, 8, true, 0>(a, dw, w.logits, ids_out, w_out, res, L.y, s, rsc);
+  }
   return hipGetLastError();
 }
 

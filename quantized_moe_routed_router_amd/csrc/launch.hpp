@@ -61,7 +61,10 @@ struct LayerArgs {
   int32_t* ids_out;
   float* w_out;
   float in_rms;        // > 0: the layer's input is bf16(x s), s = in_rms / rms(x) per token
+  int fmt;             // gate/up weight format
 };
+// Whether the decode kernels take gate/up format fmt at these shapes.
+bool decode_fmt_ok(int H, int T, int fmt);
 size_t layer_decode_workspace_bytes(int E, int H, int I, int k, int T);
 hipError_t launch_layer_decode(const LayerArgs& L, void* ws, hipStream_t s);
 hipError_t launch_ffn_decode(const FfnArgs& a, void* ws, hipStream_t s);

@@ -99,32 +99,6 @@ __device__ __forceinline__ void dequant32_nvfp4(u32x4 cw, uint32_t sw, half2_t (
   o[14] = fp4x2_to_f16x2<2>(cw.w) * b; o[15] = fp4x2_to_f16x2<3>(cw.w) * b;
 }
 
-// 32 codebook elements: 3-bit indices from three bit-plane words (bit b of
-// plane p = bit p of element b's index), 8 fp16 entries in cb (4 dwords).
-// Elements 2i and 2i+1 are decoded together: their index bits 0-1 form a byte
-// selector (bytes 2*idx, 2*idx+1 of an 8-byte half of the table), one byte
-// permute reads entries 0-3 and one entries 4-7, and index bit 2 picks the
-// half per element.
-__device__ __forceinline__ uint32_t spread2(uint32_t m) {   // bit 0 -> 0, bit 1 -> 16
-  return (m * 0x8001u) & 0x10001u;
-}
-
-__device__ __forceinline__ void dequant32_cb(uint32_t p0, uint32_t p1, uint32_t p2, u32x4 cb,
-                                             half2_t (&o)[16]) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t t0 = spread2((p0 >> (2 * i)) & 3u);
-    const uint32_t t1 = spread2((p1 >> (2 * i)) & 3u);
-    const uint32_t t2 = spread2((p2 >> (2 * i)) & 3u);
-    const uint32_t sel = 0x01000100u + (t0 + 2u * t1) * 0x0202u;
-    const uint32_t lo = __builtin_amdgcn_perm(cb.y, cb.x, sel);   // entries 0-3
-    const uint32_t hi = __builtin_amdgcn_perm(cb.w, cb.z, sel);   // entries 4-7
-    const uint32_t mask = t2 * 0xFFFFu;
-    const uint32_t word = (hi & mask) | (lo & ~mask);
-    o[i] = *reinterpret_cast<const half2_t*>(&word);
-  }
-}
-
 __device__ __forceinline__ void store32(_Float16* dst, const half2_t (&o)[16]) {
   u32x4* d = reinterpret_cast<u32x4*>(dst);
 #pragma unroll

@@ -27,8 +27,9 @@ from . import (MOE_FMT_CB3G128, MOE_FMT_NVFP4, dims, moe_combine,
 
 # Up to this many tokens the decode GEMVs are the faster expert FFN; above,
 # the grouped GEMM (32-row expert tiles) is (measured layer steps at H 2560,
-# I 640, E 512, k 10: 100 vs 105 us at 12 tokens, 127 vs 117 us at 16, 218 vs
-# 178 us at 32).  Both give the same result up to fp32 order.
+# I 640, E 512, k 10, NVFP4 gate/up: 100 vs 105 us at 12 tokens, 127 vs 117 us
+# at 16, 218 vs 178 us at 32; codebook gate/up: 145 vs 150 us at 12 tokens,
+# 191 vs 180 us at 16).  Both give the same result up to fp32 order.
 DECODE_FFN_MAX_T = 12
 
 class Layer:
@@ -107,7 +108,7 @@ class Layer:
         """Every buffer one step at T tokens needs (so a step allocates nothing)."""
         dev = self.device
         if prefill is None:
-            prefill = T > DECODE_FFN_MAX_T or self.fmt != MOE_FMT_NVFP4
+            prefill = T > DECODE_FFN_MAX_T
         ws_bytes = moe_ffn_workspace_bytes(self.d, T, prefill)
         return dict(
             T=T, prefill=prefill,

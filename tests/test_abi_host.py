@@ -95,9 +95,11 @@ def test_validation_null_and_shape():
     ex2 = dict(ex, ts_gate=None)
     code, msg = _err(m.moe_expert_ffn_decode, d, ex2, (1024, 1024, 1024), 1024, 4, 1024, 1024, 1 << 20, None, 0)
     assert code == m.MOE_ERR_INVALID and "ts_gate" in msg
-    dcb = m.dims(16, 256, 128, 2, m.MOE_FMT_CB3G128)
-    code, msg = _err(m.moe_expert_ffn_decode, dcb, ex, (1024, 1024, 1024), 1024, 4, 1024, 1024, 1 << 20, None, 0)
-    assert code == m.MOE_ERR_UNSUPPORTED
+    # codebook gate/up: refused where a K split would cut a 128-element group
+    # (H = 2688 is 21 groups; at 4 tokens the GEMVs split K in two)
+    dcb = m.dims(16, 2688, 128, 2, m.MOE_FMT_CB3G128)
+    code, msg = _err(m.moe_expert_ffn_decode, dcb, ex, (1024, 1024, 1024), 1024, 4, 1024, 1024, 1 << 30, None, 0)
+    assert code == m.MOE_ERR_UNSUPPORTED and "H = 2688" in msg
     code, msg = _err(m.moe_combine, 1024, 1024, None, 3, 0, 256, 1024, 0)
     assert code == m.MOE_ERR_SHAPE
     code, msg = _err(m.moe_pack_nvfp4, d, 10, 7, 1024, 1024, 1024, 1024, None, None, 1024, None, 0)

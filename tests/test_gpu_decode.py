@@ -171,3 +171,36 @@ def test_combine_parity():
             torch.cuda.synchronize()
             ref = offn.combine(o, w, res if use_res else None)
             assert_bf16_rounding_of(t2n(y), ref)
+
+
+@pytest.mark.parametrize("name,src,Ts", [("tiny", "host", (1, 5, 12)), ("decode", "device", (1, 8, 12))])
+def test_decode_codebook_gate_up(name, src, Ts):
+    """The decode GEMVs on 3-bit group-128 codebook gate/up weights (down
+    NVFP4): every token through every stage (h against the oracle's codebook
+    dequantization, h^ bit-exact, o, y), and the fused layer equal to the
+    separate entry points bit for bit."""
+    c = case(name, src, moe.MOE_FMT_CB3G128)
+    wl = synth.WORKLOADS["decode_b8" if name == "decode" else name]
+    for T in Ts:
+        x = synth.activations(wl, T=T, stream=1400 + T)
+        g = run_layer(c, x, residual=True, prefill=False)
+        say(name, "codebook decode T", T, check_stages(c, x, g, residual=True))
+        fb = c.L.alloc_fused(T)
+        fb["ws"].fill_(0xFF)
+        c.L.forward_fused(bf16_tensor(x, DEV), fb, residual=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(t2n(fb["ids"]), g["ids"])
+        assert np.array_equal(t2n(fb["y"]), g["y"])
+
+
+def test_decode_codebook_static_h_scale():
+    c = case("tiny", "host", moe.MOE_FMT_CB3G128)
+    h_ts = synth.static_h_scales(c.wl)
+    c.L.set_static_h_scales(torch.from_numpy(h_ts).to(DEV))
+    try:
+        for T in (1, 4):
+            x = synth.activations(c.wl, T=T, stream=1500 + T)
+            g = run_layer(c, x, residual=True, prefill=False)
+            say("codebook static h T", T, check_stages(c, x, g, residual=True, h_ts=h_ts))
+    finally:
+        c.L.set_static_h_scales(None)
