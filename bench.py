@@ -699,6 +699,8 @@ def main():
     ap.add_argument("--prefill-only", type=str, default=None,
                     help="only these prefill runs (comma list of zipf8k, nvfp4_64k, codebook_64k; "
                          "for profiler runs)")
+    ap.add_argument("--stack-only", action="store_true",
+                    help="only the 48-layer stack figures (for profiler runs)")
     ap.add_argument("--crossover-t", type=str, default=None,
                     help="comma-separated token counts for --crossover")
     ap.add_argument("--crossover", action="store_true",
@@ -755,6 +757,9 @@ def main():
         else:
             layers[li].forward(x, bufs[li], residual=True, stream=stream)
 
+    if args.stack_only:
+        print(json.dumps({"stack_decode": stack_decode(layers, dev, reps=5)}), flush=True)
+        return
     if args.decode_only:
         with torch.cuda.stream(stream):
             for i in range(max(args.steps, cycle)):

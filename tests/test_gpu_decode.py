@@ -118,15 +118,15 @@ def test_decode_flash_next_b8():
 
 
 @pytest.mark.parametrize("T", [32, 64])
-def test_decode_flash_next_many_tokens_sampled(T):
+def test_decode_flash_next_many_tokens(T):
     """Decode GEMVs at 32 and 64 tokens (320 and 640 (t, slot) pairs; above 512
-    pairs the kernels hold 32 chunks of pair ids per lane): sampled tokens
+    pairs the kernels hold 32 chunks of pair ids per lane): every token
     through every stage, and the whole output against the grouped-GEMM
     (prefill) entry on the same ids."""
     c = case("decode", "device")
     x = synth.activations(synth.WORKLOADS["decode_b8"], T=T, stream=300 + T)
-    g = run_layer(c, x, residual=True)
-    say(f"decode T={T} stages", check_stages(c, x, g, residual=True, check_tokens=[0, T // 2, T - 1]))
+    g = run_layer(c, x, residual=True, prefill=False)
+    say(f"decode T={T} stages", check_stages(c, x, g, residual=True))
     gp = run_layer(c, x, residual=True, prefill=True)
     assert np.array_equal(g["ids"], gp["ids"])
     assert rowwise_rel(g["out"], gp["out"]).max() <= 2e-3

@@ -105,15 +105,22 @@ def test_prefill_mid_tiles_skewed():
 
 
 @pytest.mark.parametrize("T", [1, 128, 4915])
-def test_prefill_flash_next_mid_sampled(T):
+def test_prefill_flash_next_mid(T):
     """Flash-Next shapes on the 32-row tiling (one token: gate/up split over K
-    in four; 4915 tokens: the largest T it takes at k = 10, E = 512): sampled
-    tokens through every stage."""
+    in four; 4915 tokens: the largest T it takes at k = 10, E = 512): every
+    stage on every token up to 128 tokens; at 4915 every (t, slot) row of the
+    chosen experts (most rows, ragged last tiles, low / middle / high ids) and
+    y of every token."""
     c = case("decode", "device")
     assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 32
     x = synth.activations(synth.WORKLOADS["decode_b8"], T=T, stream=900 + T)
     g = run_layer(c, x, residual=True, prefill=True)
-    say(f"prefill mid T={T}", check_stages(c, x, g, residual=True, check_tokens=sorted({0, T // 2, T - 1})))
+    if T <= 128:
+        say(f"prefill mid T={T}", check_stages(c, x, g, residual=True))
+        return
+    for e in pick_experts(g["ids"], c.wl.E, 32):
+        say(f"prefill mid T={T} expert {e}", check_pairs(c, x, g, np.nonzero(g["ids"].reshape(-1) == e)[0]))
+    say(f"prefill mid T={T} y all tokens", check_y_all(g, x, residual=True))
 
 
 @pytest.mark.parametrize("T,rows", [(4, 32), (300, 32), (500, 256)])
@@ -141,15 +148,19 @@ def test_prefill_codebook_tiny(T, rows):
 
 @pytest.mark.parametrize("T", [1, 128, 3276])
 def test_prefill_codebook_flash_next_mid(T):
-    """Codebook gate/up at Flash-Next shapes on the 32-row tiles (the only
-    expert FFN that takes this format at small T; 3276 tokens is the largest
-    T on them): every stage on sampled tokens."""
+    """Codebook gate/up at Flash-Next shapes on the 32-row tiles (3276 tokens
+    is the largest T on them): every stage on every token up to 128 tokens;
+    at 3276 every (t, slot) row of the chosen experts and y of every token."""
     c = case("decode", "device", moe.MOE_FMT_CB3G128)
     assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 32
     x = synth.activations(synth.WORKLOADS["decode_b8"], T=T, stream=950 + T)
     g = run_layer(c, x, residual=True, prefill=True)
-    say(f"prefill codebook mid T={T}", check_stages(c, x, g, residual=True,
-                                                    check_tokens=sorted({0, T // 2, T - 1})))
+    if T <= 128:
+        say(f"prefill codebook mid T={T}", check_stages(c, x, g, residual=True))
+        return
+    for e in pick_experts(g["ids"], c.wl.E, 32):
+        say(f"prefill codebook mid T={T} expert {e}", check_pairs(c, x, g, np.nonzero(g["ids"].reshape(-1) == e)[0]))
+    say(f"prefill codebook mid T={T} y all tokens", check_y_all(g, x, residual=True))
 
 
 @pytest.mark.parametrize("fmt", [moe.MOE_FMT_NVFP4, moe.MOE_FMT_CB3G128])
