@@ -732,24 +732,43 @@ __device__ __forceinline__ uint32_t spread4_bytes(uint32_t plane, int shift) {
   return __umul24((plane >> shift) & 0xFu, 0x204081u) & 0x01010101u;
 }
 
-__device__ __forceinline__ void dequant32_cb(uint32_t p0, uint32_t p1, uint32_t p2, u32x4 cb,
-                                             half2_t (&o)[16]) {
-  // low bytes of entries 0..3 / 4..7 and high bytes of entries 0..3 / 4..7
-  const uint32_t tlo0 = __builtin_amdgcn_perm(cb.y, cb.x, 0x06040200u);
-  const uint32_t tlo1 = __builtin_amdgcn_perm(cb.w, cb.z, 0x06040200u);
-  const uint32_t thi0 = __builtin_amdgcn_perm(cb.y, cb.x, 0x07050301u);
-  const uint32_t thi1 = __builtin_amdgcn_perm(cb.w, cb.z, 0x07050301u);
+// The table split of one group's entries: low bytes of entries 0..3 / 4..7,
+// high bytes of entries 0..3 / 4..7.
+struct CbTable {
+  uint32_t lo0, lo1, hi0, hi1;
+};
+__device__ __forceinline__ CbTable cb_table(u32x4 cb) {
+  return CbTable{__builtin_amdgcn_perm(cb.y, cb.x, 0x06040200u), __builtin_amdgcn_perm(cb.w, cb.z, 0x06040200u),
+                 __builtin_amdgcn_perm(cb.y, cb.x, 0x07050301u), __builtin_amdgcn_perm(cb.w, cb.z, 0x07050301u)};
+}
+
+// Elements shift .. shift+7 of a 32-element chunk (plane words p0..p2) as
+// four f16 pairs.
+__device__ __forceinline__ void cb_decode8(uint32_t p0, uint32_t p1, uint32_t p2, int shift, const CbTable& t,
+                                           half2_t (&o)[4]) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t idx = spread4_bytes(p0, 4 * j) | (spread4_bytes(p1, 4 * j) << 1) |
-                         (spread4_bytes(p2, 4 * j) << 2);          // byte m: index of element 4j+m
+  for (int h = 0; h < 2; ++h) {
+    const int sh = shift + 4 * h;
+    const uint32_t idx = spread4_bytes(p0, sh) | (spread4_bytes(p1, sh) << 1) | (spread4_bytes(p2, sh) << 2);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const uint32_t sel_lo = __builtin_amdgcn_perm(0x0C0C0C0Cu, idx, q ? 0x04030402u : 0x04010400u);
       const uint32_t sel_hi = __builtin_amdgcn_perm(0x0C0C0C0Cu, idx, q ? 0x03040204u : 0x01040004u);
-      const uint32_t word = __builtin_amdgcn_perm(tlo1, tlo0, sel_lo) | __builtin_amdgcn_perm(thi1, thi0, sel_hi);
-      o[2 * j + q] = *reinterpret_cast<const half2_t*>(&word);
+      const uint32_t word = __builtin_amdgcn_perm(t.lo1, t.lo0, sel_lo) | __builtin_amdgcn_perm(t.hi1, t.hi0, sel_hi);
+      o[2 * h + q] = *reinterpret_cast<const half2_t*>(&word);
     }
+  }
+}
+
+__device__ __forceinline__ void dequant32_cb(uint32_t p0, uint32_t p1, uint32_t p2, u32x4 cb,
+                                             half2_t (&o)[16]) {
+  const CbTable t = cb_table(cb);
+#pragma unroll
+  for (int s8 = 0; s8 < 4; ++s8) {
+    half2_t o4[4];
+    cb_decode8(p0, p1, p2, 8 * s8, t, o4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[4 * s8 + i] = o4[i];
   }
 }
 

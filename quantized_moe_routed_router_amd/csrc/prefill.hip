@@ -434,7 +434,13 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
     TileP Bd = b ? Bs0 : Bs1;
     const uint32_t asw = avalid ? R.asw : 0u;
     const _Float16 as0 = (_Float16)e4m3_to_f32(asw & 0xFF), as1 = (_Float16)e4m3_to_f32((asw >> 8) & 0xFF);
-    const _Float16 bs0 = (_Float16)e4m3_to_f32(R.bsw & 0xFF), bs1 = (_Float16)e4m3_to_f32((R.bsw >> 8) & 0xFF);
+    _Float16 bs0 = 0, bs1 = 0;
+    CbTable cbt{};
+    if constexpr (MODE == 1) cbt = cb_table(R.bcw);
+    else {
+      bs0 = (_Float16)e4m3_to_f32(R.bsw & 0xFF);
+      bs1 = (_Float16)e4m3_to_f32((R.bsw >> 8) & 0xFF);
+    }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       half8_t af[4], bf[2];
@@ -447,14 +453,20 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
       // staging part kk: dword kk of each chunk (elements 8kk..8kk+7)
       {
         const uint32_t aw = kk == 0 ? R.acw.x : kk == 1 ? R.acw.y : kk == 2 ? R.acw.z : R.acw.w;
-        const uint32_t bw = kk == 0 ? R.bcw.x : kk == 1 ? R.bcw.y : kk == 2 ? R.bcw.z : R.bcw.w;
-        const _Float16 sa = kk < 2 ? as0 : as1, sb = kk < 2 ? bs0 : bs1;
-        const half2_t a2 = {sa, sa}, b2 = {sb, sb};
+        const _Float16 sa = kk < 2 ? as0 : as1;
+        const half2_t a2 = {sa, sa};
         half2_t oa[4], ob[4];
         oa[0] = fp4x2_to_f16x2<0>(aw) * a2; oa[1] = fp4x2_to_f16x2<1>(aw) * a2;
         oa[2] = fp4x2_to_f16x2<2>(aw) * a2; oa[3] = fp4x2_to_f16x2<3>(aw) * a2;
-        ob[0] = fp4x2_to_f16x2<0>(bw) * b2; ob[1] = fp4x2_to_f16x2<1>(bw) * b2;
-        ob[2] = fp4x2_to_f16x2<2>(bw) * b2; ob[3] = fp4x2_to_f16x2<3>(bw) * b2;
+        if constexpr (MODE == 1) {
+          cb_decode8(R.p0, R.p1, R.p2, 8 * kk, cbt, ob);      // codebook entries, no scale
+        } else {
+          const uint32_t bw = kk == 0 ? R.bcw.x : kk == 1 ? R.bcw.y : kk == 2 ? R.bcw.z : R.bcw.w;
+          const _Float16 sb = kk < 2 ? bs0 : bs1;
+          const half2_t b2 = {sb, sb};
+          ob[0] = fp4x2_to_f16x2<0>(bw) * b2; ob[1] = fp4x2_to_f16x2<1>(bw) * b2;
+          ob[2] = fp4x2_to_f16x2<2>(bw) * b2; ob[3] = fp4x2_to_f16x2<3>(bw) * b2;
+        }
         *reinterpret_cast<u32x4*>(&Ad[sr][32 * sc + 8 * kk]) = *reinterpret_cast<const u32x4*>(oa);
         *reinterpret_cast<u32x4*>(&Bd[sr][32 * sc + 8 * kk]) = *reinterpret_cast<const u32x4*>(ob);
       }
@@ -463,12 +475,13 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      // this slice: fragment reads, then MFMA / VALU alternating, then the two writes
+      // this slice: fragment reads, then MFMA / VALU alternating (the
+      // codebook decode has about five times the VALU work), then the writes
       __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, MODE == 1 ? 6 : 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
     }
@@ -486,20 +499,10 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
   load_step(R0, 2);
   int st = 0;
   for (; st + 4 < S; st += 2) {
-    if constexpr (MODE == 1) {
-      mfma_step(B0{});
-      stage(R1, B1{});
-    } else {
-      mfma_stage_step(B0{}, R1);
-    }
+    mfma_stage_step(B0{}, R1);
     load_step(R1, st + 3);
     __syncthreads();
-    if constexpr (MODE == 1) {
-      mfma_step(B1{});
-      stage(R0, B0{});
-    } else {
-      mfma_stage_step(B1{}, R0);
-    }
+    mfma_stage_step(B1{}, R0);
     load_step(R0, st + 4);
     __syncthreads();
   }
