@@ -81,6 +81,10 @@ WORKLOADS = {
                         router_std=0.05, expert_std=0.02, seed=7),
     "tiny_all": Workload("tiny_all", H=256, I=128, E=16, k=16, T=4,
                          router_std=0.05, expert_std=0.02, seed=8),
+    # The largest expert count and top-k the library takes (E = 1024, k = 32)
+    # on the tiny widths.
+    "max_ek": Workload("max_ek", H=256, I=128, E=1024, k=32, T=4,
+                       router_std=0.05, expert_std=0.02, seed=10),
     # Wide single layers (few experts): one token with H above 2560 takes the
     # decode path with a K-split gate/up and a separate h^ step.
     "wide4k": Workload("wide4k", H=4096, I=256, E=16, k=4, T=1, seed=5),

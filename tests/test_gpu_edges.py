@@ -70,3 +70,58 @@ def test_empty_batch_enqueues_nothing():
     with pytest.raises(moe.MoeError):
         moe.moe_expert_ffn_decode(L.d, L.experts(), (b["x_codes"], b["x_scales"], b["x_ts"]), b["ids"],
                                   moe.MOE_DECODE_MAX_T + 1, b["out"], b["ws"], b["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("T,path", [(1, "decode"), (16, "decode"), (64, "decode"), (40, "prefill"),
+                                    (3100, "prefill")])
+def test_largest_expert_count_and_topk(T, path):
+    """E = 1024 experts and k = 32, the largest the library takes: the top-k
+    over 16 logits per lane, 2048 (t, slot) pairs through the decode GEMVs at
+    64 tokens (the most their pair lists hold), 512 pairs through the fused
+    layer at 16 tokens, the 32-row and 128-row grouped GEMMs; every stage of
+    every token (sampled tokens at 3100) against the oracle, the router
+    against the oracle outside near-ties, the fused layer equal to the
+    separate entry points."""
+    c = case("max_ek", "device")
+    wl = c.wl
+    x = synth.activations(wl, T=T, stream=60 + T)
+    g = run_layer(c, x, residual=True, prefill=(path == "prefill"))
+    oids, ow, near, _, _ = orouter.route(x, c.W_r, wl.k)
+    for t in range(T):
+        assert len(set(g["ids"][t].tolist())) == wl.k
+        if not near[t]:
+            assert set(g["ids"][t].tolist()) == set(oids[t].tolist()), t
+    if path == "prefill":
+        assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == (32 if T * wl.k <= 96 * wl.E else 128)
+    toks = None if T <= 64 else sorted({0, 1, T // 3, T // 2, T - 2, T - 1})
+    say("max E/k", T, path, check_stages(c, x, g, residual=True, check_tokens=toks))
+    if path == "decode" and T <= moe.MOE_LAYER_MAX_T:
+        fb = c.L.alloc_fused(T)
+        fb["ws"].fill_(0xFF)
+        c.L.forward_fused(bf16_tensor(x, DEV), fb, residual=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(t2n(fb["ids"]), g["ids"])
+        assert np.array_equal(t2n(fb["y"]), g["y"])
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill", "fused"])
+def test_zero_input(path):
+    """x = 0 (with and without the residual): every logit is 0, an exact tie,
+    so the ids are 0 .. k-1 in order with weights 1/k; x^ has tensor scale 0,
+    so h, h^, o and y are exactly 0."""
+    c = case("tiny", "host")
+    T, k = 5, c.wl.k
+    x = np.zeros((T, c.wl.H), np.uint16)
+    if path == "fused":
+        fb = c.L.alloc_fused(T)
+        fb["ws"].fill_(0xFF)
+        c.L.forward_fused(bf16_tensor(x, DEV), fb, residual=True)
+        torch.cuda.synchronize()
+        g = {kk: t2n(v) for kk, v in fb.items() if isinstance(v, torch.Tensor) and kk != "ws"}
+    else:
+        g = run_layer(c, x, residual=True, prefill=(path == "prefill"))
+        assert not g["out"].any() and not g["dbg_h"].any() and not g["dbg_h_codes"].any()
+        assert not g["dbg_h_scales"].any() and not g["dbg_h_ts"].any()
+    assert np.array_equal(g["ids"], np.tile(np.arange(k, dtype=np.int32), (T, 1)))
+    assert np.all(g["w"] == np.float32(1.0 / k))
+    assert not g["y"].view(np.uint16).any()
