@@ -307,4 +307,10 @@ def moe_permute(ids, T: int, k: int, E: int, counts, offsets, perm, inv, ws, ws_
                              _ptr(inv), _ptr(ws), ws_bytes, _stream(stream)))
 
 
-from .layer import Layer  # noqa: E402,F401  (allocation helpers over the ABI)
+def __getattr__(name):
+    # Layer (allocation helpers over the ABI) needs torch; the bare C-ABI
+    # wrappers above do not, so torch is imported only when Layer is used
+    if name == "Layer":
+        from .layer import Layer
+        return Layer
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")

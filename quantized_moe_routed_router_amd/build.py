@@ -1,6 +1,7 @@
 """Build libmoe.so (gfx950 only) in-tree with hipcc.
 
     python -m quantized_moe_routed_router_amd.build   [-j N] [--verbose]
+    python -m quantized_moe_routed_router_amd.build --host-sanitized DIR
 
 Every source under csrc/ is compiled to an object in _build/ and linked into
 quantized_moe_routed_router_amd/libmoe.so.  Always rebuilds.
@@ -67,12 +68,58 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side sanitizer build: the host code of every source (argument
+# validation, workspace carving, launch set-up) with AddressSanitizer and
+# UndefinedBehaviorSanitizer; the device code is built as usual, without
+# them.  Each -fsanitize= applies to the host pass only.
+SANITIZE_HOST = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
+def asan_runtime() -> str:
+    """Path of the AddressSanitizer runtime that the sanitized library needs
+    preloaded into the (uninstrumented) interpreter."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError(f"AddressSanitizer runtime not found (hipcc printed {path!r})")
+    return path
+
+
+def build_host_sanitized(out_dir: str, jobs: int = 8) -> str:
+    os.makedirs(out_dir, exist_ok=True)
+    flags = [*FLAGS, "-g", *SANITIZE_HOST]
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.basename(src).replace(".hip", ".o"))
+        r = subprocess.run([HIPCC, *flags, "-c", src, "-o", obj], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (host, sanitized) failed for {src}:\n{r.stdout}{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(one, sources()))
+    lib = os.path.join(out_dir, "libmoe_host_sanitized.so")
+    r = subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *SANITIZE_HOST, "-shared-libsan",
+                        *objs, "-o", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stdout}{r.stderr}")
+    return lib
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", type=int, default=min(8, os.cpu_count() or 1))
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--host-sanitized", metavar="DIR",
+                    help="instead: the host code only, with ASan + UBSan, into DIR")
     a = ap.parse_args(argv)
-    print(build(a.j, a.verbose))
+    if a.host_sanitized:
+        print(build_host_sanitized(a.host_sanitized, a.j))
+    else:
+        print(build(a.j, a.verbose))
 
 
 if __name__ == "__main__":
