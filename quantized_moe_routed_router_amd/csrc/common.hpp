@@ -42,8 +42,13 @@ __host__ __device__ constexpr size_t down_expert_bytes(int H, int I) {
   return (size_t)(H / 64) * tile_bytes(I);
 }
 // Codebook gate/up tiles (3-bit indices, fp16 codebook per 128-group):
-//   per group g: [64 lanes][3 bit-planes x 16 B] then [64 lanes][8 x fp16]
-//   bit-plane p, dword d, bit b = bit p of the index of element 32d + b.
+//   per group g: [64 lanes][3 index words x 4 dwords] then [64 lanes][8 x fp16]
+//   chunk d = elements 32d .. 32d+31 of the group, in dword d of each index
+//   word: word 0 holds bits 0-1 of the index of element 32d + 4m + j (m, j in
+//   0..3) at bits 8j + 2m, 8j + 2m + 1; word 1 the same for elements
+//   32d + 16 + 4m + j; word 2 bit 2 of element 32d + 4m + j (m in 0..7) at
+//   bit 8j + m.  So four consecutive indices come to the bytes of one word by
+//   shifts and masks.
 __host__ __device__ constexpr size_t cb_group_bytes() { return 64 * 48 + 64 * 16; }
 __host__ __device__ constexpr size_t cb_tile_bytes(int K) { return (size_t)(K / 128) * cb_group_bytes(); }
 __host__ __device__ constexpr size_t cb_gate_up_expert_bytes(int H, int I) {
@@ -717,19 +722,23 @@ __device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
-// 32 codebook elements: 3-bit indices from three bit-plane words (bit b of
-// plane p = bit p of element b's index), 8 fp16 entries in cb (4 dwords).
-// The table is split into the entries' low bytes and high bytes (8 bytes
-// each), so one byte permute looks up a byte of two elements.  Per four
-// elements, each plane's 4 bits are spread to the bytes of a word by one
-// 24-bit multiply and a mask, and the three planes merge into the four
-// indices as bytes; per two elements, two permutes of those bytes make the
-// lookup selectors ({i_a, 12, i_b, 12} and {12, i_a, 12, i_b}: selector 12
-// gives a zero byte), two permutes of the table halves give the low and the
-// high bytes, and an OR joins them into two fp16 values.
-__device__ __forceinline__ uint32_t spread4_bytes(uint32_t plane, int shift) {
-  // bits 0..3 of (plane >> shift) -> bit 0 of bytes 0..3 (x * (1 + 2^7 + 2^14 + 2^21))
-  return __umul24((plane >> shift) & 0xFu, 0x204081u) & 0x01010101u;
+// 32 codebook elements: 3-bit indices from three index words (layout above:
+// w0 and w1 hold bits 0-1 of elements 0-15 and 16-31, two bits per element,
+// w2 bit 2 of all 32), 8 fp16 entries in cb (4 dwords).  The table is split
+// into the entries' low bytes and high bytes (8 bytes each).  Per four
+// elements 4q .. 4q+3: one shift and mask bring their bits 0-1 to bits 0-1 of
+// bytes 0-3, one shift and one and-or add bit 2, so byte j holds element
+// 4q + j's index, which is also the byte number of its entry in either table
+// half; two byte permutes of the table halves by that word give the four low
+// bytes and the four high bytes, and two more interleave them into two pairs
+// of fp16 values.  Four VALU operations per element fewer than spreading three
+// bit-planes by multiplies and building a selector per element pair.
+template <int Q>
+__device__ __forceinline__ uint32_t cb_quad_index(uint32_t w0, uint32_t w1, uint32_t w2) {
+  static_assert(Q >= 0 && Q < 8, "quad of a 32-element chunk");
+  const uint32_t lo = ((Q < 4 ? w0 : w1) >> (2 * (Q & 3))) & 0x03030303u;
+  const uint32_t b2 = Q >= 2 ? (w2 >> (Q - 2)) : (w2 << (2 - Q));
+  return (b2 & 0x04040404u) | lo;
 }
 
 // The table split of one group's entries: low bytes of entries 0..3 / 4..7,
@@ -742,34 +751,34 @@ __device__ __forceinline__ CbTable cb_table(u32x4 cb) {
                  __builtin_amdgcn_perm(cb.y, cb.x, 0x07050301u), __builtin_amdgcn_perm(cb.w, cb.z, 0x07050301u)};
 }
 
-// Elements shift .. shift+7 of a 32-element chunk (plane words p0..p2) as
-// four f16 pairs.
-__device__ __forceinline__ void cb_decode8(uint32_t p0, uint32_t p1, uint32_t p2, int shift, const CbTable& t,
-                                           half2_t (&o)[4]) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int sh = shift + 4 * h;
-    const uint32_t idx = spread4_bytes(p0, sh) | (spread4_bytes(p1, sh) << 1) | (spread4_bytes(p2, sh) << 2);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t sel_lo = __builtin_amdgcn_perm(0x0C0C0C0Cu, idx, q ? 0x04030402u : 0x04010400u);
-      const uint32_t sel_hi = __builtin_amdgcn_perm(0x0C0C0C0Cu, idx, q ? 0x03040204u : 0x01040004u);
-      const uint32_t word = __builtin_amdgcn_perm(t.lo1, t.lo0, sel_lo) | __builtin_amdgcn_perm(t.hi1, t.hi0, sel_hi);
-      o[2 * h + q] = *reinterpret_cast<const half2_t*>(&word);
-    }
-  }
+// Elements 4q .. 4q+3 (q = Q) as two f16 pairs.
+template <int Q>
+__device__ __forceinline__ void cb_decode4(uint32_t w0, uint32_t w1, uint32_t w2, const CbTable& t,
+                                           half2_t& e01, half2_t& e23) {
+  const uint32_t idx = cb_quad_index<Q>(w0, w1, w2);
+  const uint32_t lo = __builtin_amdgcn_perm(t.lo1, t.lo0, idx);
+  const uint32_t hi = __builtin_amdgcn_perm(t.hi1, t.hi0, idx);
+  const uint32_t a = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // {lo0, hi0, lo1, hi1}
+  const uint32_t b = __builtin_amdgcn_perm(hi, lo, 0x07030602u);   // {lo2, hi2, lo3, hi3}
+  e01 = *reinterpret_cast<const half2_t*>(&a);
+  e23 = *reinterpret_cast<const half2_t*>(&b);
 }
 
-__device__ __forceinline__ void dequant32_cb(uint32_t p0, uint32_t p1, uint32_t p2, u32x4 cb,
+// Elements 8*S8 .. 8*S8+7 of a 32-element chunk as four f16 pairs.
+template <int S8>
+__device__ __forceinline__ void cb_decode8(uint32_t w0, uint32_t w1, uint32_t w2, const CbTable& t,
+                                           half2_t (&o)[4]) {
+  cb_decode4<2 * S8>(w0, w1, w2, t, o[0], o[1]);
+  cb_decode4<2 * S8 + 1>(w0, w1, w2, t, o[2], o[3]);
+}
+
+__device__ __forceinline__ void dequant32_cb(uint32_t w0, uint32_t w1, uint32_t w2, u32x4 cb,
                                              half2_t (&o)[16]) {
   const CbTable t = cb_table(cb);
-#pragma unroll
-  for (int s8 = 0; s8 < 4; ++s8) {
-    half2_t o4[4];
-    cb_decode8(p0, p1, p2, 8 * s8, t, o4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[4 * s8 + i] = o4[i];
-  }
+  cb_decode8<0>(w0, w1, w2, t, *reinterpret_cast<half2_t(*)[4]>(&o[0]));
+  cb_decode8<1>(w0, w1, w2, t, *reinterpret_cast<half2_t(*)[4]>(&o[4]));
+  cb_decode8<2>(w0, w1, w2, t, *reinterpret_cast<half2_t(*)[4]>(&o[8]));
+  cb_decode8<3>(w0, w1, w2, t, *reinterpret_cast<half2_t(*)[4]>(&o[12]));
 }
 
 }  // namespace moe

@@ -198,7 +198,7 @@ __device__ __forceinline__ float dot_chunks_row(const u32x4 (&cw)[CPW], const ui
 // ---- gate/up weights in either format, held in registers per wave
 // NVFP4 (FMT 0): CPW chunks of 32 elements (16 code bytes + 2 scale bytes per
 // lane).  Codebook (FMT 1): CB_GPW groups of 128 elements (three 16-byte
-// bit-planes of 3-bit indices + eight fp16 entries per lane); a weight is
+// index words of 3-bit indices + eight fp16 entries per lane); a weight is
 // its group's entry, with no block or tensor scale.
 constexpr int CB_GPW = 3;
 template <int FMT, int CPW> struct GuRegs;

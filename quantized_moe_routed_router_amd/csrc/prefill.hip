@@ -194,10 +194,10 @@ __global__ __launch_bounds__(PF_THREADS) void grouped_gemm_kernel(FfnArgs a, Pre
       const int ck = k0 / 32 + bc;
       if (MODE == 1) {
         const uint8_t* grp = btile + (size_t)(ck >> 2) * cb_group_bytes();
-        const uint32_t* planes = reinterpret_cast<const uint32_t*>(grp + bl * 48);
+        const uint32_t* iw = reinterpret_cast<const uint32_t*>(grp + bl * 48);
         const int d = ck & 3;
         u32x4 cb = *reinterpret_cast<const u32x4*>(grp + 64 * 48 + bl * 16);
-        dequant32_cb(planes[d], planes[4 + d], planes[8 + d], cb, o);
+        dequant32_cb(iw[d], iw[4 + d], iw[8 + d], cb, o);
       } else {
         u32x4 cw = *reinterpret_cast<const u32x4*>(btile + (size_t)ck * 1024 + bl * 16);
         uint32_t sw = *reinterpret_cast<const uint16_t*>(btile + tile_scale_offset(K) + (size_t)(ck >> 2) * 512 + bl * 8 + (ck & 3) * 2);
@@ -324,9 +324,9 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
     const int ck = (st * BBK + 32 * sc) / 32;
     if (MODE == 1) {
       const uint8_t* grp = btile + (size_t)(ck >> 2) * cb_group_bytes();
-      const uint32_t* planes = reinterpret_cast<const uint32_t*>(grp + bl * 48);
+      const uint32_t* iw = reinterpret_cast<const uint32_t*>(grp + bl * 48);
       const int d = ck & 3;
-      R.p0 = planes[d]; R.p1 = planes[4 + d]; R.p2 = planes[8 + d];
+      R.p0 = iw[d]; R.p1 = iw[4 + d]; R.p2 = iw[8 + d];
       R.bcw = *reinterpret_cast<const u32x4*>(grp + 64 * 48 + bl * 16);
     } else {
       R.bcw = *reinterpret_cast<const u32x4*>(btile + (size_t)ck * 1024 + bl * 16);
@@ -459,7 +459,11 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
         oa[0] = fp4x2_to_f16x2<0>(aw) * a2; oa[1] = fp4x2_to_f16x2<1>(aw) * a2;
         oa[2] = fp4x2_to_f16x2<2>(aw) * a2; oa[3] = fp4x2_to_f16x2<3>(aw) * a2;
         if constexpr (MODE == 1) {
-          cb_decode8(R.p0, R.p1, R.p2, 8 * kk, cbt, ob);      // codebook entries, no scale
+          // codebook entries, no scale (kk is a constant once unrolled)
+          if (kk == 0) cb_decode8<0>(R.p0, R.p1, R.p2, cbt, ob);
+          else if (kk == 1) cb_decode8<1>(R.p0, R.p1, R.p2, cbt, ob);
+          else if (kk == 2) cb_decode8<2>(R.p0, R.p1, R.p2, cbt, ob);
+          else cb_decode8<3>(R.p0, R.p1, R.p2, cbt, ob);
         } else {
           const uint32_t bw = kk == 0 ? R.bcw.x : kk == 1 ? R.bcw.y : kk == 2 ? R.bcw.z : R.bcw.w;
           const _Float16 sb = kk < 2 ? bs0 : bs1;
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 // 8m..8m+7 of each lane's chunk: A and B share this k order, so the four
 // MFMAs cover the step's 64 products exactly once.  Two register sets
 // alternate, one step's loads in flight while the other's are consumed.
-// Codebook gate/up (MODE 1): the lane reads its chunk's three bit-plane words
+// Codebook gate/up (MODE 1): the lane reads its chunk's three index words
 // and its row's eight fp16 entries instead.  K % 128 == 0 (even step count).
 constexpr int MB = 32, MWAVES = 4;
 constexpr int MID_MAX_AVG_ROWS = 96;   // 32-row tiles while T*k <= this * E
@@ -609,7 +613,7 @@ struct MidRegs {
   uint32_t as;       // A block scales (two E4M3 bytes)
   u32x4 bc[2];       // B codes (NVFP4) or codebook entries: packed rows r and 32 + r
   uint32_t bs[2];    // B block scales (NVFP4)
-  uint32_t bp[2][3]; // B index bit-planes (codebook)
+  uint32_t bp[2][3]; // B index words (codebook)
 };
 
 __device__ __forceinline__ half8_t cat8(half2_t a, half2_t b, half2_t c, half2_t d) {
@@ -674,13 +678,13 @@ __global__ __launch_bounds__(64 * MWAVES, MODE == 1 ? 3 : 1) void grouped_gemm_m
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if (MODE == 1) {
-        // group ck/4: [64 rows][3 planes x 4 dwords], then [64 rows][8 fp16]
+        // group ck/4: [64 rows][3 index words x 4 dwords], then [64 rows][8 fp16]
         const uint8_t* grp = tile + (size_t)(ck >> 2) * cb_group_bytes();
-        const uint32_t* planes = reinterpret_cast<const uint32_t*>(grp + (j * 32 + r) * 48);
+        const uint32_t* iw = reinterpret_cast<const uint32_t*>(grp + (j * 32 + r) * 48);
         const int d = ck & 3;
-        o.bp[j][0] = planes[d];
-        o.bp[j][1] = planes[4 + d];
-        o.bp[j][2] = planes[8 + d];
+        o.bp[j][0] = iw[d];
+        o.bp[j][1] = iw[4 + d];
+        o.bp[j][2] = iw[8 + d];
         o.bc[j] = *reinterpret_cast<const u32x4*>(grp + 64 * 48 + (j * 32 + r) * 16);
       } else {
         o.bc[j] = *reinterpret_cast<const u32x4*>(bcodes + (size_t)ck * 1024 + j * 512);

@@ -185,7 +185,7 @@ hipError_t launch_pack_nvfp4(bool unpack, int H, int I, int e0, int n, uint8_t* 
 }
 
 // Codebook gate/up: one thread per (expert, tile, group, lane): writes the
-// lane's 3 bit-planes (48 B) and its 8 fp16 entries (16 B).
+// lane's 3 index words (48 B) and its 8 fp16 entries (16 B).
 __global__ __launch_bounds__(256) void pack_codebook_kernel(int n, int N_tiles, int K,
                                                             const uint16_t* __restrict__ g_cb,
                                                             const uint8_t* __restrict__ g_idx,
@@ -205,15 +205,19 @@ __global__ __launch_bounds__(256) void pack_codebook_kernel(int n, int N_tiles, 
   const uint16_t* cb = (lane < 32 ? g_cb : u_cb) + (row * groups + g) * 8;
   const uint8_t* ix = (lane < 32 ? g_idx : u_idx) + row * K + (size_t)g * 128;
   uint8_t* grp = packed + ((size_t)e * N_tiles + j) * cb_tile_bytes(K) + (size_t)g * cb_group_bytes();
-  uint32_t planes[3][4] = {};
+  // index words (the codebook tile layout): element c of chunk d has bits 0-1
+  // in word c / 16 at bits 8 (c % 4) + 2 ((c % 16) / 4) and bit 2 in word 2
+  // at bit 8 (c % 4) + c / 4
+  uint32_t words[3][4] = {};
   for (int el = 0; el < 128; ++el) {
-    uint32_t v = ix[el] & 7;
-#pragma unroll
-    for (int p = 0; p < 3; ++p) planes[p][el >> 5] |= ((v >> p) & 1u) << (el & 31);
+    const uint32_t v = ix[el] & 7;
+    const int d = el >> 5, c = el & 31, j = c & 3;
+    words[c >> 4][d] |= (v & 3u) << (8 * j + 2 * ((c & 15) >> 2));
+    words[2][d] |= ((v >> 2) & 1u) << (8 * j + (c >> 2));
   }
   u32x4* dst = reinterpret_cast<u32x4*>(grp + lane * 48);
 #pragma unroll
-  for (int p = 0; p < 3; ++p) dst[p] = u32x4{planes[p][0], planes[p][1], planes[p][2], planes[p][3]};
+  for (int p = 0; p < 3; ++p) dst[p] = u32x4{words[p][0], words[p][1], words[p][2], words[p][3]};
   const u32x4* cs = reinterpret_cast<const u32x4*>(cb);
   *reinterpret_cast<u32x4*>(grp + 64 * 48 + lane * 16) = *cs;
 }
