@@ -175,11 +175,17 @@ int moe_expert_ffn_prefill(const moe_dims* dims, const moe_experts* experts,
  * MOE_ERR_* code on invalid dims or T < 1. */
 int moe_ffn_prefill_tile_rows(const moe_dims* dims, int T);
 
-/* The whole decode layer for 1 <= T <= MOE_LAYER_MAX_T tokens in three
- * kernels: router logits + NVFP4 of x; top-k (ranked in every gate/up block)
- * + gate/up; down + weighted combine.  Same arithmetic as moe_router_topk,
- * moe_quantize_act, moe_expert_ffn_decode and moe_combine in sequence:
- *   y = bf16_rne( [x if add_residual] + sum_i w_i * FFN_{ids_i}(x^) ).
+/* The whole decode layer for 1 <= T <= MOE_LAYER_MAX_T tokens.  One token:
+ * three kernels (router logits + NVFP4 of x; top-k, ranked in every gate/up
+ * block, + gate/up; down + weighted combine).  Several tokens: the top-k and
+ * h^ run once in kernels of their own, and the down projection carries the
+ * combine up to 8 tokens (a block per column slice and token), else a
+ * combine kernel follows.  The result is that of moe_router_topk,
+ * moe_quantize_act, moe_expert_ffn_decode and moe_combine in sequence,
+ *   y = bf16_rne( [x if add_residual] + sum_i w_i * FFN_{ids_i}(x^) ),
+ * bit for bit where both run the same kernels (T*k <= 16, or T > 8); between
+ * those the down dots sum in another fp32 order (ids, w and h^ equal, y one
+ * bf16 rounding of the same sum).
  * x [T, H] bf16 (also the residual), W_r [E, H] fp32, bias [E] or NULL,
  * y [T, H] bf16 out; ids [T, k] int32 and w [T, k] fp32 outputs, or NULL.
  * ws: at least moe_layer_decode_workspace_bytes(dims, T) bytes (contents
@@ -192,7 +198,7 @@ int moe_layer_decode(const moe_dims* dims, const moe_experts* experts, const uin
                      uint16_t* y, int32_t* ids, float* w, void* ws, size_t ws_bytes,
                      void* stream);
 
-/* One layer of the full-depth decode stack in the same three kernels as
+/* One layer of the full-depth decode stack in the kernels of
  * moe_layer_decode: x_in [T, H] bf16 is the previous layer's output, the
  * layer's input is x = bf16_rne(x_in * s) with s = target_rms / sqrt(mean_h
  * x_in^2) per token (fp32, the same fixed-order sum and IEEE division and

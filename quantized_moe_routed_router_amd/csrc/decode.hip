@@ -765,8 +765,12 @@ __global__ __launch_bounds__(64 * DEC_MAX_WAVES) void down_decode_kernel(FfnArgs
 }
 
 // ---------------------------------------------------------------- down + combine
-// Down step for few pairs (T*k <= SL_MAXP): a block owns 16 output columns
-// n0..n0+15 of every pair and wave q serves pair q.  Lane (r = lane & 15,
+// Down step for few pairs: a block owns 16 output columns n0..n0+15 of the
+// pairs of blockIdx.y's group of tokens (all T tokens when T*k <= SL_MAXP,
+// else one token, so k <= SL_MAXP) and wave q serves the group's pair q.
+// Per-token blocks read an expert's rows once per token that routes to it
+// (a few per cent more than once per distinct expert at eight tokens, most of
+// it from L2) and in exchange need neither o in HBM nor a combine kernel.  Lane (r = lane & 15,
 // quarter qt = lane >> 4) reads row n0 + r of the pair's 64-row down tile at
 // chunks qt, qt+4, ...; the quarters are summed with lane shuffles.
 // Order of work: the pair ids, the combine inputs and this thread's block of
@@ -780,6 +784,12 @@ constexpr int SL_MAXP = 16;              // pairs (= waves) per block
 constexpr int SL_CPQ = 5;                // chunks per quarter held in registers (I <= 640)
 
 constexpr int SL_HQR = 3;                // h quarters per lane in h mode (I <= 768)
+// Per-token slice blocks in the fused layer up to this many tokens.  Layer
+// step at H 2560, I 640, E 512, k 10 (graph-replayed, 8 layers cycled), against
+// the per-expert down GEMVs plus the combine kernel: 40.0 -> 36.2 us at 2
+// tokens, 53.2 -> 50.1 at 4, 77.6 -> 75.4 at 8, 98.8 -> 100.8 at 12 and
+// 126.9 -> 128.1 at 16 (duplicate expert reads grow with the tokens).
+constexpr int SL_TOKEN_MAX_T = 8;
 
 // HQ (h mode, one token): wave q quantizes pair q's h row itself, from h
 // and the 32-row tile maxima the gate/up step wrote (the row amax is their
@@ -793,7 +803,10 @@ __global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, Dec
                                                                   uint16_t* __restrict__ y,
                                                                   const float* __restrict__ res_scale) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int npairs = a.T * a.k;
+  // this block's tokens tok0 .. tok0+ntok-1, pairs q0 .. q0+npairs-1
+  const int ntok = gridDim.y == 1 ? a.T : 1;
+  const int tok0 = blockIdx.y * ntok, q0 = tok0 * a.k;
+  const int npairs = ntok * a.k;
   half2_t* hs = reinterpret_cast<half2_t*>(smem);                              // [npairs][I/2]
   float* obuf = reinterpret_cast<float*>(smem + (size_t)npairs * a.I * 2);     // [npairs][16]
   __shared__ float hts[SL_MAXP];
@@ -806,17 +819,17 @@ __global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, Dec
   const int nchunk = a.I / 32, nblk = a.I / 16;
   const int nitems = npairs * nblk;
   // ---- loads that do not depend on the routing, ids first
-  const int qid = a.ids[lane < npairs ? lane : npairs - 1];
-  const float htl = HQ ? 0.0f : ws.hts[lane < npairs ? lane : npairs - 1];
+  const int qid = a.ids[q0 + (lane < npairs ? lane : npairs - 1)];
+  const float htl = HQ ? 0.0f : ws.hts[q0 + (lane < npairs ? lane : npairs - 1)];
   float wc = 0.0f;
   uint16_t res = 0;
   if (COMBINE) {
-    wc = w_comb[tid < npairs ? tid : npairs - 1];
-    const int cidx = tid < a.T * 16 ? tid : a.T * 16 - 1;
+    wc = w_comb[q0 + (tid < npairs ? tid : npairs - 1)];
+    const int cidx = tid < ntok * 16 ? tid : ntok * 16 - 1;
     // no residual: read y's own column instead (unused), keeping the load unconditional
     const uint16_t* rp = residual ? residual : y;
-    res = rp[(size_t)(cidx >> 4) * a.H + n0 + (cidx & 15)];
-    if (res_scale) res = (uint16_t)bf16_scaled(res, res_scale[cidx >> 4]);
+    res = rp[(size_t)(tok0 + (cidx >> 4)) * a.H + n0 + (cidx & 15)];
+    if (res_scale) res = (uint16_t)bf16_scaled(res, res_scale[tok0 + (cidx >> 4)]);
   }
   const int item = tid < nitems ? tid : nitems - 1;
   const int jq = item / nblk, jb = item % nblk;
@@ -826,14 +839,15 @@ __global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, Dec
   float hmx = 0.0f;
   const int nqr = a.I / 4, ntile = a.I / 32;
   if (!HQ) {
-    hcw = *reinterpret_cast<const u32x2*>(ws.hc + (size_t)jq * (a.I / 2) + jb * 8);
-    hsw = ws.hsc[(size_t)jq * nblk + jb];
+    hcw = *reinterpret_cast<const u32x2*>(ws.hc + (size_t)(q0 + jq) * (a.I / 2) + jb * 8);
+    hsw = ws.hsc[(size_t)(q0 + jq) * nblk + jb];
   } else {
-    const float* hrow = ws.gu + (size_t)q * a.I;
+    // h mode: h rows and the 32-row tile maxima behind all T*k h rows
+    const float* hrow = ws.gu + (size_t)(q0 + q) * a.I;
 #pragma unroll
     for (int m = 0; m < SL_HQR; ++m)
       hq[m] = *reinterpret_cast<const float4_t*>(hrow + (size_t)min(lane + 64 * m, nqr - 1) * 4);
-    hmx = ws.gu[(size_t)npairs * a.I + (size_t)q * ntile + min(lane, ntile - 1)];
+    hmx = ws.gu[(size_t)a.T * a.k * a.I + (size_t)(q0 + q) * ntile + min(lane, ntile - 1)];
   }
   __builtin_amdgcn_sched_barrier(0);        // these loads stay ahead of the weight loads
   // ---- this pair's expert and its weight loads
@@ -884,13 +898,13 @@ __global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, Dec
         d[0] = fp4x2_to_f16x2<0>(bits) * s2;
         d[1] = fp4x2_to_f16x2<1>(bits) * s2;
         if (dbg && a.dbg_h_codes)
-          *reinterpret_cast<uint16_t*>(a.dbg_h_codes + (size_t)q * (a.I / 2) + qi * 2) = (uint16_t)bits;
-        if (dbg && a.dbg_h_scales && (qi & 3) == 0) a.dbg_h_scales[(size_t)q * nblk + (qi >> 2)] = (uint8_t)sb;
+          *reinterpret_cast<uint16_t*>(a.dbg_h_codes + (size_t)(q0 + q) * (a.I / 2) + qi * 2) = (uint16_t)bits;
+        if (dbg && a.dbg_h_scales && (qi & 3) == 0) a.dbg_h_scales[(size_t)(q0 + q) * nblk + (qi >> 2)] = (uint8_t)sb;
       }
     }
     if (lane == 0) {
       hts[q] = ts;
-      if (dbg && a.dbg_h_ts) a.dbg_h_ts[q] = ts;
+      if (dbg && a.dbg_h_ts) a.dbg_h_ts[q0 + q] = ts;
     }
   }
   if (COMBINE && tid < npairs) wcs[tid] = wc;
@@ -915,18 +929,18 @@ __global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, Dec
   if (lane < 16) {
     const float ov = valid ? acc * (hts[q] * tsd) : 0.0f;
     obuf[q * 16 + r] = ov;
-    a.out[(size_t)q * a.H + n0 + r] = ov;
+    a.out[(size_t)(q0 + q) * a.H + n0 + r] = ov;
   }
   if (!COMBINE) return;
   __syncthreads();
 
   // ---- combine these 16 columns: fp32 in slot order, one bf16 rounding
-  if (tid < a.T * 16) {
+  if (tid < ntok * 16) {
     const int t = tid >> 4, c = tid & 15;
     float accy = 0.0f;
     for (int i = 0; i < a.k; ++i) accy = fmaf(wcs[t * a.k + i], obuf[(t * a.k + i) * 16 + c], accy);
     if (residual) accy += bf16_to_f32(res);
-    y[(size_t)t * a.H + n0 + c] = (uint16_t)f32_to_bf16_rne(accy);
+    y[(size_t)(tok0 + t) * a.H + n0 + c] = (uint16_t)f32_to_bf16_rne(accy);
   }
 }
 
@@ -1053,6 +1067,11 @@ static void launch_decode_pair(const FfnArgs& a, DecodeWs ws, const float* logit
     const size_t lds = slice_lds_bytes(npairs, a.I);
     if (FUSED) down_slice_kernel<true, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, w_out, residual, y, res_scale);
     else down_slice_kernel<false, false><<<a.H / 16, 64 * npairs, lds, s>>>(a, ws, nullptr, nullptr, nullptr, nullptr);
+  } else if (FUSED && a.T <= SL_TOKEN_MAX_T && slice_fits(a.k, a.H, a.I)) {
+    // the fused layer at a few tokens: one slice block per (16 columns,
+    // token), the combine in the block (no o round trip, no combine kernel)
+    const size_t lds = slice_lds_bytes(a.k, a.I);
+    down_slice_kernel<true, false><<<dim3(a.H / 16, a.T), 64 * a.k, lds, s>>>(a, ws, w_out, residual, y, res_scale);
   } else {
     const int nw2 = dec_waves(a.I / 32);
     const size_t lds2 = (size_t)MAXP * a.I * 2 + (size_t)nw2 * MAXP * 64 * 4;

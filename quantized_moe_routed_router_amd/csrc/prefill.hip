@@ -485,7 +485,7 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, MODE == 1 ? 6 : 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, MODE == 1 ? 4 : 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
     }

@@ -135,6 +135,27 @@ def assert_bf16_rounding_of(y_dev_bits: np.ndarray, y_ref: np.ndarray, slack_rel
     return float((err / np.maximum(np.abs(y_ref).max(axis=-1, keepdims=True), 1e-30)).max())
 
 
+def check_fused_against_separate(f, g, xbits, residual: bool, label=""):
+    """The fused decode layer (f) against the separate entry points (g) on the
+    same input: ids and w bit for bit.  Where both run the same down kernel
+    (T * k <= 16: the one-block-per-column-slice kernel over every pair) y is
+    equal bit for bit too; above that the fused layer runs one slice block per
+    token and sums each down dot in another fp32 order than the separate
+    down kernel, so its y must be one bf16 rounding of the separate path's
+    F = r + sum_i w_i o_i (fp32 slack 1e-5 of the row's max).  Returns how
+    many y elements differ from the separate path's."""
+    assert np.array_equal(f["ids"], g["ids"]), label
+    assert np.array_equal(f["w"].view(np.uint32), g["w"].view(np.uint32)), label
+    T, k = f["ids"].shape
+    if T * k <= 16:
+        assert np.array_equal(f["y"], g["y"]), ("fused y differs from the separate entry points", label)
+        return 0
+    from oracle import ffn as offn
+    y_ref = offn.combine(g["out"], g["w"], xbits if residual else None)
+    assert_bf16_rounding_of(f["y"], y_ref)
+    return int(np.count_nonzero(f["y"] != g["y"]))
+
+
 _cases = {}
 
 

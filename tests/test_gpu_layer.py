@@ -1,6 +1,7 @@
-"""GPU parity: the fused three-kernel decode layer against the separate
-entry points (bit-exact: same kernels' arithmetic) and against the oracle;
-replays of a captured HIP graph against the eager result."""
+"""GPU parity: the fused decode layer against the separate entry points
+(bit-exact where they run the same kernels, else one bf16 rounding of the
+separate path's combine) and against the oracle; replays of a captured HIP
+graph against the eager result."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +10,7 @@ import synth
 import quantized_moe_routed_router_amd as moe
 from oracle import ffn as offn, nvfp4, router as orouter
 from tests.gpu_helpers import (say, t2n, bf16_tensor, rowwise_rel, bf16_half_ulp, case, run_layer,
-                               SENT_BF16)
+                               SENT_BF16, check_fused_against_separate)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -29,18 +30,17 @@ def fused(c, xbits, residual):
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny", 4), ("tiny", 16), ("decode", 1),
-                                    ("decode_b8", 8), ("wide4k", 1)])
+                                    ("decode_b8", 2), ("decode_b8", 8), ("decode_b8", 16), ("wide4k", 1)])
 def test_fused_equals_separate_path(name, T):
     src = "host" if name in ("tiny", "wide4k") else "device"
     c = case("decode" if name == "decode_b8" else name, src)
     x = synth.activations(synth.WORKLOADS[name], T=T, stream=500 + T)
+    ndiff = []
     for residual in (False, True):
         f, _ = fused(c, x, residual)
         g = run_layer(c, x, residual=residual)
-        assert np.array_equal(f["ids"], g["ids"])
-        assert np.array_equal(f["w"].view(np.uint32), g["w"].view(np.uint32))
-        assert np.array_equal(f["y"], g["y"]), "fused y differs from the separate entry points"
-    say("fused == separate", name, T)
+        ndiff.append(check_fused_against_separate(f, g, x, residual, (name, T, residual)))
+    say("fused vs separate", name, T, "y elements differing (no residual, residual):", ndiff)
 
 
 def test_fused_vs_oracle_flash_next():

@@ -17,7 +17,7 @@ import torch
 import synth
 import quantized_moe_routed_router_amd as moe
 from oracle import router as orouter, stack as ostack
-from tests.gpu_helpers import (say, t2n, bf16_tensor, LayerCase, run_layer, check_stages,
+from tests.gpu_helpers import (say, t2n, bf16_tensor, LayerCase, run_layer, check_stages, check_fused_against_separate,
                                assert_bf16_rounding_of)
 
 pytestmark = pytest.mark.gpu
@@ -108,9 +108,7 @@ def check_sampled(cases, ins, outs, check_tokens=None):
     for li in SAMPLED:
         c, x, f = cases[li], ins[li].view(np.uint16), outs[li]
         g = run_layer(c, x, residual=True)
-        assert np.array_equal(f["ids"], g["ids"]), li
-        assert np.array_equal(f["w"].view(np.uint32), g["w"].view(np.uint32)), li
-        assert np.array_equal(f["y"], g["y"]), li
+        check_fused_against_separate(f, g, x, True, li)
         oids, ow, near, _, _ = orouter.route(x, c.W_r, c.wl.k)
         for t in range(x.shape[0]):
             if not near[t]:
