@@ -850,13 +850,13 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
                      "kernel": ("one decode layer step, moe_layer_decode (router_quant_kernel, "
-                                "gate_up_decode_kernel<1,10,true>, down_slice_kernel<true,true>)"),
+                                "gate_up_decode_kernel<1, 10, true, 1, 0>, down_slice_kernel<true, true>)"),
                      "bytes_per_launch": step_bytes, "us_per_launch": round(ms_step * 1e3, 3),
                      "timing": ("HIP events on the launch stream around one replay of the graph of "
                                 f"{n_steps} steps (the headline timed region)"),
                      "dominant_kernel": dominant},
-        "expert_ffn_call": {"kernel": "moe_expert_ffn_decode (gate_up_decode_kernel<1,10,false>, "
-                                      "down_slice_kernel<false,true>)",
+        "expert_ffn_call": {"kernel": "moe_expert_ffn_decode (gate_up_decode_kernel<1, 10, false, 1, 0>, "
+                                      "down_slice_kernel<false, true>)",
                             "bytes_per_call": ffn_bytes, "us_per_call": round(ffn_us, 3),
                             "gbps": round(ffn_gbps, 1), "frac": round(ffn_gbps / HBM_PEAK_GBPS, 4),
                             "us_per_call_eager": round(ffn_eager_us, 3),
