@@ -1,7 +1,8 @@
 """The no-allocation decode layer entry (moe_layer_decode_noalloc) against
 moe_layer_decode with a caller workspace: same ids, weights and y bit for
 bit, on two calls in a row, the second with fewer tokens (the scratch array
-keeps the first call's contents)."""
+keeps the first call's contents); and the entry captured into a HIP graph,
+each replay equal to the eager call on the same input."""
 import numpy as np
 import pytest
 import torch
@@ -58,3 +59,42 @@ def test_noalloc_refuses_oversized_layer():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_layer_decode_noalloc(d, L.experts(), L.W_r, L.W_r, None, 16, True, L.W_r, None, None)
     assert ei.value.code == moe.MOE_ERR_WORKSPACE and "scratch" in str(ei.value)
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_noalloc_replays_under_graph_capture(T):
+    """The entry's use case: the call captured into a HIP graph (after one
+    eager call on the device, which takes the scratch array's address) and
+    replayed with new inputs copied into the captured input buffer; every
+    replay, with eager work between replays, equals the eager call on the same
+    input bit for bit."""
+    c = case("decode", "device")
+    L = c.L
+    wl = synth.WORKLOADS["decode_b8"]
+    xs = [bf16_tensor(synth.activations(wl, T=T, stream=1400 + 8 * T + i), DEV) for i in range(3)]
+    xin = torch.empty_like(xs[0])
+    ids = torch.empty((T, L.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, L.k), dtype=torch.float32, device=DEV)
+    y = torch.empty((T, L.H), dtype=torch.int16, device=DEV)
+    eager = [_noalloc(L, x, T, True) for x in xs]
+    s = torch.cuda.Stream()
+    xin.copy_(xs[0])
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        moe.moe_layer_decode_noalloc(L.d, L.experts(), xin, L.W_r, L.bias, T, True, y, ids, w, stream=s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        moe.moe_layer_decode_noalloc(L.d, L.experts(), xin, L.W_r, L.bias, T, True, y, ids, w, stream=s)
+    for rep in range(3):
+        for i, x in enumerate(xs):
+            xin.copy_(x)
+            y.fill_(SENT_BF16)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(t2n(ids), eager[i][0]), (rep, i)
+            assert np.array_equal(t2n(w).view(np.uint32), eager[i][1].view(np.uint32)), (rep, i)
+            assert np.array_equal(t2n(y), eager[i][2]), (rep, i)
+            _ = (y.float() * 2).sum().item()                   # eager work between replays
+    say("noalloc graph replays match eager, T", T)
