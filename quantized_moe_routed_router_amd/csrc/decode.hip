@@ -929,7 +929,7 @@ __global__ __launch_bounds__(64 * SL_MAXP) void down_slice_kernel(FfnArgs a, Dec
   if (lane < 16) {
     const float ov = valid ? acc * (hts[q] * tsd) : 0.0f;
     obuf[q * 16 + r] = ov;
-    a.out[(size_t)(q0 + q) * a.H + n0 + r] = ov;
+    if (!COMBINE) a.out[(size_t)(q0 + q) * a.H + n0 + r] = ov;   // with the combine o stays in LDS
   }
   if (!COMBINE) return;
   __syncthreads();
