@@ -826,6 +826,18 @@ def main():
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_tokens} decode tokens, prefill samples")
         cpu = cpu_baseline(wl, args.cpu_tokens, dev, prefill=not args.no_prefill)
+        # the 48-layer stack on the oracle: 48 layers of the same shapes, so
+        # the per-layer decode time scaled by 48 (stated, not run)
+        cpu["stack48_b1"] = {"tok_s": round(cpu["value"] / 48, 4), "threads": "all",
+                             "sample": "48 x the per-layer oracle decode time measured above (linear scaling)"}
+        ratio = {"decode_b1": round((1e3 / ms_step) / cpu["value"], 1)}
+        if stack:
+            ratio["stack48_b1"] = round(stack["b1"]["tok_s"] / cpu["stack48_b1"]["tok_s"], 1)
+        if prefill and "prefill_64k_uniform" in cpu and "nvfp4" in prefill:
+            ratio["prefill_64k"] = round(prefill["nvfp4"]["tok_s"] / cpu["prefill_64k_uniform"]["tok_s"], 1)
+        if prefill and "prefill_8k_zipf" in cpu and "zipf_8k" in prefill:
+            ratio["prefill_8k_zipf"] = round(prefill["zipf_8k"]["tok_s"] / cpu["prefill_8k_zipf"]["tok_s"], 1)
+        cpu["gpu_over_oracle"] = ratio
 
     traffic, dominant = stored_decode_profile()
     out = {
