@@ -208,10 +208,10 @@ def stack_decode(layers, dev, reps: int):
     """The full-depth decode stack: one token (then eight) carried through all
     resident layers, each layer with the residual add and its own router with
     logits scaled to N(0, 1) (the 48-layer recipe), each output brought back
-    to the first layer's input RMS for the next layer inside that layer's
-    first kernel (moe_layer_decode_rescaled: three kernels per layer); the
-    whole pass captured as one HIP graph.  The experts are the resident
-    layers' own."""
+    to the first layer's input RMS for the next layer by
+    moe_layer_decode_rescaled (inside the layer's first kernel at one token:
+    three kernels per layer; a rescale kernel first at eight); the whole pass
+    captured as one HIP graph.  The experts are the resident layers' own."""
     import copy
     import numpy as np
     import torch

@@ -7,7 +7,7 @@ library's kernels.
     layer.load_experts_fp32(e0, gate, up, down)        # quantized + packed on device
     bufs = layer.alloc(T)                              # every per-step buffer
     y = layer.forward(x_bf16, bufs, residual=True)     # router -> quant -> FFN -> combine
-    fb = layer.alloc_fused(T)                          # decode: the three-kernel layer
+    fb = layer.alloc_fused(T)                          # decode: the fused layer (3 kernels at 1 token)
     y = layer.forward_fused(x_bf16, fb, residual=True)
 """
 from __future__ import annotations
