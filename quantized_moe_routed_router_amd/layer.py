@@ -28,8 +28,8 @@ from . import (MOE_FMT_CB3G128, MOE_FMT_NVFP4, dims, moe_combine,
 # Up to this many tokens the decode GEMVs are the faster expert FFN; above,
 # the grouped GEMM (32-row expert tiles) is (measured layer steps at H 2560,
 # I 640, E 512, k 10, NVFP4 gate/up: 100 vs 105 us at 12 tokens, 127 vs 117 us
-# at 16, 218 vs 178 us at 32; codebook gate/up: 145 vs 150 us at 12 tokens,
-# 191 vs 180 us at 16).  Both give the same result up to fp32 order.
+# at 16, 218 vs 178 us at 32; codebook gate/up: 124 vs 128 us at 12 tokens,
+# 162 vs 153 us at 16).  Both give the same result up to fp32 order.
 DECODE_FFN_MAX_T = 12
 
 class Layer:
