@@ -87,8 +87,8 @@ size_t prefill_workspace_bytes(int E, int H, int I, int k, int T) {
 
 // 32 NVFP4 elements (16 code bytes, 2 E4M3 scales) -> 32 f16 values e2m1*s
 __device__ __forceinline__ void dequant32_nvfp4(u32x4 cw, uint32_t sw, half2_t (&o)[16]) {
-  const _Float16 s0 = (_Float16)e4m3_to_f32(sw & 0xFF), s1 = (_Float16)e4m3_to_f32((sw >> 8) & 0xFF);
-  const half2_t a = {s0, s0}, b = {s1, s1};
+  const half2_t s = e4m3x2_to_f16x2(sw);
+  const half2_t a = {s.x, s.x}, b = {s.y, s.y};
   o[0] = fp4x2_to_f16x2<0>(cw.x) * a; o[1] = fp4x2_to_f16x2<1>(cw.x) * a;
   o[2] = fp4x2_to_f16x2<2>(cw.x) * a; o[3] = fp4x2_to_f16x2<3>(cw.x) * a;
   o[4] = fp4x2_to_f16x2<0>(cw.y) * a; o[5] = fp4x2_to_f16x2<1>(cw.y) * a;
