@@ -3,17 +3,19 @@ an oracle function (its source copied, one expression replaced, patched in
 for the test's duration) and one of the oracle's pins must then fail.  This
 is the evidence that the pins would catch such a mistake: a wrong divisor, a
 tie broken the wrong way, a rounding order, a dropped sign, a swapped operand,
-a reversed bit or nibble order, a wrong tie-break or softmax sign, an unstable
-sort.  Nothing here touches the GPU."""
+a reversed bit, nibble, group or row order, a wrong tie-break, softmax or bias
+sign, an unstable sort, a wrong table value, an ignored static scale, a
+dropped residual, a wrong RMS.  Nothing here touches the GPU."""
 import inspect
 import textwrap
 
 import numpy as np
 import pytest
 
-from oracle import codebook, ffn, formats, nvfp4, permute, router
+from oracle import codebook, ffn, formats, nvfp4, permute, router, stack
 from tests import (test_oracle_codebook as pc, test_oracle_ffn as pf, test_oracle_formats as pfo,
-                   test_oracle_nvfp4 as pn, test_oracle_permute as pp, test_oracle_router as pr)
+                   test_oracle_nvfp4 as pn, test_oracle_permute as pp, test_oracle_router as pr,
+                   test_oracle_stack as ps)
 import synth
 
 
@@ -80,6 +82,27 @@ MUTANTS = [
     ("codebook index bit order", codebook, "pack_indices",
      'bitorder="little"', 'bitorder="big"',
      pc.test_pack_round_trip_and_bit_order),
+    ("codebook groups in reverse order", codebook, "dequantize",
+     "g = np.arange(K) // GROUP", "g = (K // GROUP - 1) - np.arange(K) // GROUP",
+     pc.test_dequant_is_table_lookup),
+    ("E2M1 magnitude 1.5 read as 1.25", formats, "e2m1_decode",
+     "mag = E2M1_MAGNITUDES[c & 7]", "mag = np.where((c & 7) == 3, 1.25, E2M1_MAGNITUDES[c & 7])",
+     pfo.test_e2m1_table_all_16_codes),
+    ("static tensor scale ignored", nvfp4, "quantize",
+     "if ts_given is not None:", "if False:",
+     pn.test_static_tensor_scale_brute_force),
+    ("router bias subtracted", router, "logits",
+     "l = l + np.asarray(bias", "l = l - np.asarray(bias",
+     pr.test_bias_shifts_logits),
+    ("combine without the residual", ffn, "combine",
+     "y = y + bf16_bits_to_f64(residual_bits)", "y = y + 0.0 * bf16_bits_to_f64(residual_bits)",
+     pf.test_zero_input_gives_residual),
+    ("down projection rows reversed", ffn, "down",
+     "o[rows] = hd[rows] @ Wd.T", "o[rows] = hd[rows] @ Wd[::-1].T",
+     lambda: pf.test_dense_layer_exact_brute_force(_tiny())),
+    ("stack RMS from the mean absolute value", stack, "rms_norm",
+     "ms = np.mean(x * x, axis=-1, keepdims=True)", "ms = np.mean(np.abs(x), axis=-1, keepdims=True) ** 2",
+     ps.test_output_rms_and_power_of_two_invariance),
 ]
 
 
