@@ -77,10 +77,10 @@ typedef struct moe_dims {
  * ts_gate / ts_up are ignored (may be NULL) for MOE_FMT_CB3G128.
  * h_ts [E] or NULL: a static (calibrated) NVFP4 tensor scale for h, the down
  * projection's input, per expert, as NVIDIA's NVFP4 checkpoints carry for
- * activations (the engine was built for that quantisation: blog post, "What
- * it's for").  NULL: each (t, slot) row of h takes amax / 2688 (dynamic).
- * With a static scale the quantizer skips the amax step; values beyond
- * 6 * 448 * h_ts[e] saturate.  Must be >= 0 and finite. */
+ * activations (the engine was built for that quantisation: forum repost,
+ * paragraph "What it's for").  NULL: each (t, slot) row of h takes
+ * amax / 2688 (dynamic).  With a static scale the quantizer skips the
+ * amax step; values beyond 6 * 448 * h_ts[e] saturate.  Must be >= 0 and finite. */
 typedef struct moe_experts {
   const void* gate_up;
   const void* down;

@@ -17,8 +17,8 @@ even, in this order (a reading: the pages name the format, not these steps):
   4. d = E4M3value(sb) * ts; if d = 0 the block's codes are all 0, otherwise
      code = sign(v) << 3 | E2M1(|v / d|).
 With a static (calibrated) tensor scale, as NVIDIA's NVFP4 checkpoints carry
-for activations (the engine was built for that quantisation: blog post,
-"What it's for"), ts is given per row and steps 1-2 are skipped; values
+for activations (the engine was built for that quantisation: forum repost,
+paragraph "What it's for"), ts is given per row and steps 1-2 are skipped; values
 beyond 6 * 448 * ts saturate to the largest code and block scale.
 The sign bit is kept even when the magnitude rounds to 0 (so a small negative
 value encodes as 0x8).
