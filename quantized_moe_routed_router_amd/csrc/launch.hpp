@@ -81,12 +81,23 @@ hipError_t launch_rms_norm(const uint16_t* x, int T, int H, float target, uint16
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 
 size_t permute_workspace_bytes(int T, int k, int E);
+// A second list of row tiles: experts with fewer than split_rows rows are
+// tiled there, by BM rows, instead of in the first list (unused when
+// tile_map is nullptr).
+struct TileSplit {
+  int32_t* tile_prefix = nullptr;
+  int32_t* tile_map = nullptr;
+  int BM = 0;
+  int split_rows = 0;
+};
 // Counting sort of ids; also writes the per-expert tile prefix for grouped
 // GEMMs with BM-row tiles when tile_prefix != nullptr ([E+1] entries), and
 // when tile_map != nullptr one record per tile {expert, first row, end row of
-// the expert, 0} (4 ints each, tile_prefix[E] records).
+// the expert, 0} (4 ints each, tile_prefix[E] records); the same for the
+// second list when split.tile_map is set.
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
-                          int32_t* tile_prefix, int32_t* tile_map, int BM, hipStream_t s);
+                          int32_t* tile_prefix, int32_t* tile_map, int BM, hipStream_t s,
+                          const TileSplit& split = TileSplit{});
 
 }  // namespace moe

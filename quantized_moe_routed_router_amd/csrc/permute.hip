@@ -6,7 +6,9 @@
 // Three passes, no host round trip (one launch up to PSB_MAX_N entries):
 //   1. per 1024-entry chunk, a histogram over experts (LDS atomics);
 //   2. per expert, the exclusive prefix of its chunk counts (chunk order), and
-//      the exclusive prefix over experts -> offsets, counts, tile prefix;
+//      the exclusive prefix over experts -> offsets, counts, tile prefix and
+//      one record per row tile (with a second list, experts below split_rows
+//      rows are tiled by BM2 rows there instead, the others by BM rows);
 //   3. per chunk, one wave walks its entries 64 at a time in order; equal-
 //      expert lanes are found with ballots over the id bits, so ranks inside a
 //      step and across steps keep the original order (stable).
@@ -68,22 +70,46 @@ __global__ __launch_bounds__(256) void perm_chunk_scan_kernel(const int32_t* __r
   if (lane == 63) totals[e] = incl;
 }
 
+// An expert's row-tile counts: BM-row tiles, or with a second list (sp.tile_map
+// set) BM-row tiles from sp.split_rows rows up and sp.BM-row tiles below.
+__device__ __forceinline__ void tile_counts(int rows, bool expert, int BM, const TileSplit& sp, int& n1, int& n2) {
+  n1 = n2 = 0;
+  if (!expert) return;
+  if (sp.tile_map && rows < sp.split_rows) n2 = (rows + sp.BM - 1) / sp.BM;
+  else if (BM > 0) n1 = (rows + BM - 1) / BM;
+}
+
+// Expert e's prefix entry and tile records {e, first row of the tile, end of
+// the expert's rows} from the inclusive tile-count scan incl (of 1056 slots).
+__device__ __forceinline__ void write_tiles(int e, int E, int first_row, int end_row, const int* incl, int BM,
+                                            int32_t* tile_prefix, int32_t* tile_map) {
+  const int t0 = e ? incl[e - 1] : 0;
+  if (tile_prefix) tile_prefix[e] = t0;
+  if (tile_map && e < E) {
+    const int nt = incl[e] - t0;
+    for (int i = 0; i < nt; ++i)
+      *reinterpret_cast<int4*>(tile_map + (size_t)(t0 + i) * 4) = int4{e, first_row + i * BM, end_row, 0};
+  }
+}
+
 // Single block: exclusive scan over bins (E+1 <= 1025 values).
 __global__ __launch_bounds__(1024) void perm_offsets_kernel(const int32_t* __restrict__ totals, int E,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ bin_start,
                                                             int32_t* __restrict__ tile_prefix,
-                                                            int32_t* __restrict__ tile_map, int BM) {
+                                                            int32_t* __restrict__ tile_map, int BM,
+                                                            const TileSplit sp) {
   __shared__ int sc[2][1056];
   __shared__ int st[2][1056];
+  __shared__ int st2[2][1056];
   const int tid = threadIdx.x;
-  for (int e = tid; e < 1056; e += 1024) { sc[0][e] = 0; st[0][e] = 0; }
+  for (int e = tid; e < 1056; e += 1024) { sc[0][e] = 0; st[0][e] = 0; st2[0][e] = 0; }
   __syncthreads();
   for (int e = tid; e <= E; e += 1024) {
     const int v = totals[e];
     sc[0][e] = v;
-    st[0][e] = (e < E && BM > 0) ? (v + BM - 1) / BM : 0;
+    tile_counts(v, e < E, BM, sp, st[0][e], st2[0][e]);
   }
   __syncthreads();
   // Hillis-Steele inclusive scan over 1056 slots, ping-pong buffers
@@ -92,6 +118,7 @@ __global__ __launch_bounds__(1024) void perm_offsets_kernel(const int32_t* __res
     for (int e = tid; e < 1056; e += 1024) {
       sc[cur ^ 1][e] = sc[cur][e] + (e >= off ? sc[cur][e - off] : 0);
       st[cur ^ 1][e] = st[cur][e] + (e >= off ? st[cur][e - off] : 0);
+      st2[cur ^ 1][e] = st2[cur][e] + (e >= off ? st2[cur][e - off] : 0);
     }
     __syncthreads();
     cur ^= 1;
@@ -101,13 +128,8 @@ __global__ __launch_bounds__(1024) void perm_offsets_kernel(const int32_t* __res
     bin_start[e] = excl;
     if (e < E) counts[e] = totals[e];
     offsets[e] = excl;                               // offsets[E] = entries with valid ids
-    if (tile_prefix) tile_prefix[e] = e ? st[cur][e - 1] : 0;
-    // the expert's tiles: {e, first row of the tile, end of the expert's rows}
-    if (tile_map && e < E) {
-      const int t0 = e ? st[cur][e - 1] : 0, nt = st[cur][e] - t0, end = sc[cur][e];
-      for (int i = 0; i < nt; ++i)
-        *reinterpret_cast<int4*>(tile_map + (size_t)(t0 + i) * 4) = int4{e, excl + i * BM, end, 0};
-    }
+    write_tiles(e, E, excl, sc[cur][e], st[cur], BM, tile_prefix, tile_map);
+    if (sp.tile_map) write_tiles(e, E, excl, sc[cur][e], st2[cur], sp.BM, sp.tile_prefix, sp.tile_map);
   }
 }
 
@@ -163,13 +185,15 @@ __global__ __launch_bounds__(64 * PSB_WAVES) void perm_small_kernel(const int32_
                                                                      int32_t* __restrict__ perm,
                                                                      int32_t* __restrict__ inv,
                                                                      int32_t* __restrict__ tile_prefix,
-                                                                     int32_t* __restrict__ tile_map, int BM) {
+                                                                     int32_t* __restrict__ tile_map, int BM,
+                                                                     const TileSplit sp) {
   __shared__ int hist[PSB_WAVES][1025];                // per wave and bin: count, then running position
   __shared__ int sc[2][1056];
   __shared__ int st[2][1056];
+  __shared__ int st2[2][1056];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int i = tid; i < PSB_WAVES * 1025; i += 64 * PSB_WAVES) (&hist[0][0])[i] = 0;
-  for (int e = tid; e < 1056; e += 64 * PSB_WAVES) { sc[0][e] = 0; st[0][e] = 0; }
+  for (int e = tid; e < 1056; e += 64 * PSB_WAVES) { sc[0][e] = 0; st[0][e] = 0; st2[0][e] = 0; }
   __syncthreads();
   const int per = (N + PSB_WAVES - 1) / PSB_WAVES;
   const int c0 = min(wv * per, N), c1 = min(c0 + per, N);
@@ -188,7 +212,7 @@ __global__ __launch_bounds__(64 * PSB_WAVES) void perm_small_kernel(const int32_
       run += v;
     }
     sc[0][e] = run;
-    st[0][e] = (e < E && BM > 0) ? (run + BM - 1) / BM : 0;
+    tile_counts(run, e < E, BM, sp, st[0][e], st2[0][e]);
   }
   __syncthreads();
   int cur = 0;                                          // Hillis-Steele inclusive scan
@@ -196,6 +220,7 @@ __global__ __launch_bounds__(64 * PSB_WAVES) void perm_small_kernel(const int32_
     for (int e = tid; e < 1056; e += 64 * PSB_WAVES) {
       sc[cur ^ 1][e] = sc[cur][e] + (e >= off ? sc[cur][e - off] : 0);
       st[cur ^ 1][e] = st[cur][e] + (e >= off ? st[cur][e - off] : 0);
+      st2[cur ^ 1][e] = st2[cur][e] + (e >= off ? st2[cur][e - off] : 0);
     }
     __syncthreads();
     cur ^= 1;
@@ -204,12 +229,8 @@ __global__ __launch_bounds__(64 * PSB_WAVES) void perm_small_kernel(const int32_
     const int excl = e ? sc[cur][e - 1] : 0;
     if (e < E) counts[e] = sc[cur][e] - excl;
     offsets[e] = excl;
-    if (tile_prefix) tile_prefix[e] = e ? st[cur][e - 1] : 0;
-    if (tile_map && e < E) {
-      const int t0 = e ? st[cur][e - 1] : 0, nt = st[cur][e] - t0, end = sc[cur][e];
-      for (int i = 0; i < nt; ++i)
-        *reinterpret_cast<int4*>(tile_map + (size_t)(t0 + i) * 4) = int4{e, excl + i * BM, end, 0};
-    }
+    write_tiles(e, E, excl, sc[cur][e], st[cur], BM, tile_prefix, tile_map);
+    if (sp.tile_map) write_tiles(e, E, excl, sc[cur][e], st2[cur], sp.BM, sp.tile_prefix, sp.tile_map);
   }
   int nbits = 0;
   while ((1 << nbits) <= E) ++nbits;
@@ -245,10 +266,12 @@ size_t permute_workspace_bytes(int T, int k, int E) {
 
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
-                          int32_t* tile_prefix, int32_t* tile_map, int BM, hipStream_t s) {
+                          int32_t* tile_prefix, int32_t* tile_map, int BM, hipStream_t s,
+                          const TileSplit& split) {
   const int N = T * k;
   if (N <= PSB_MAX_N) {
-    perm_small_kernel<<<1, 64 * PSB_WAVES, 0, s>>>(ids, N, E, counts, offsets, perm, inv, tile_prefix, tile_map, BM);
+    perm_small_kernel<<<1, 64 * PSB_WAVES, 0, s>>>(ids, N, E, counts, offsets, perm, inv, tile_prefix, tile_map, BM,
+                                                   split);
     return hipGetLastError();
   }
   const int nch = (N + PCH - 1) / PCH;
@@ -262,7 +285,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* coun
   } else {
     perm_chunk_scan_kernel<<<(E + 1 + 3) / 4, 256, 0, s>>>(cc, 0, E, cb, totals);
   }
-  perm_offsets_kernel<<<1, 1024, 0, s>>>(totals, E, counts, offsets, bin_start, tile_prefix, tile_map, BM);
+  perm_offsets_kernel<<<1, 1024, 0, s>>>(totals, E, counts, offsets, bin_start, tile_prefix, tile_map, BM, split);
   if (nch > 0)
     perm_scatter_kernel<<<nch, 64, (E + 1) * sizeof(int), s>>>(ids, N, E, cb, bin_start, perm, inv);
   return hipGetLastError();

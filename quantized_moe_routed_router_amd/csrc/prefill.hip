@@ -22,6 +22,7 @@
 //   h quant   NVFP4 of each h row (one tensor scale per (t, slot) row)
 //   down      same GEMM on h^ rows; epilogue scales by ts_h ts_down and
 //             scatters o rows back to (t, slot) through perm.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -48,6 +49,8 @@ struct PrefillWs {
   int32_t* inv;
   int32_t* tile_prefix;
   int32_t* tile_map;     // per tile {expert, first row, end row of the expert, 0}
+  int32_t* tile_prefix2; // the 256-row tiling's second list: 32-row tiles of the
+  int32_t* tile_map2;    // experts with fewer than BB_SPLIT_ROWS rows
   float* h;
   uint8_t* hq_codes;
   uint8_t* hq_scales;
@@ -69,6 +72,8 @@ static PrefillWs carve(void* ws, int E, int I, int k, int T, size_t* total) {
   w.inv = (int32_t*)take(N * 4);
   w.tile_prefix = (int32_t*)take((size_t)(E + 1) * 4);
   w.tile_map = (int32_t*)take(((N + 31) / 32 + (size_t)E) * 16);   // enough for 32-, 128- and 256-row tiles
+  w.tile_prefix2 = (int32_t*)take((size_t)(E + 1) * 4);
+  w.tile_map2 = (int32_t*)take(((N + 31) / 32 + (size_t)E) * 16);
   w.h = (float*)take(N * I * 4);
   w.hq_codes = take(N * I / 2);
   w.hq_scales = take(N * I / 16);
@@ -607,6 +612,10 @@ constexpr int MB = 32, MWAVES = 4;
 constexpr int MID_MAX_AVG_ROWS = 96;   // 32-row tiles while T*k <= this * E
 constexpr int MID_MAX_AVG_ROWS_CB = 64;   // the same for codebook gate/up (VALU-heavier decode:
                                           // it repays the big tiles' reuse sooner)
+// In the 256-row tiling, experts below this many rows take 32-row tiles (the
+// 32-row kernels stream an expert's weights once per 32 rows, the 256-row
+// ones stage a mostly empty tile at full cost).
+constexpr int BB_SPLIT_ROWS = 128;
 
 struct MidRegs {
   u32x4 ac;          // A codes, this lane's chunk of its row
@@ -892,18 +901,38 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
     return hipGetLastError();
   }
   if (rows == BB) {
+    // experts with fewer than BB_SPLIT_ROWS rows (a skewed routing's long
+    // tail) take 32-row tiles in a second list rather than one mostly empty
+    // 256-row tile each; both lists index the same permuted rows
+    TileSplit sp;
+    sp.tile_prefix = w.tile_prefix2;
+    sp.tile_map = w.tile_map2;
+    sp.BM = MB;
+    sp.split_rows = BB_SPLIT_ROWS;
     hipError_t err = launch_permute(a.ids, a.T, a.k, a.E, w.counts, w.offsets, w.perm, w.inv,
-                                    w.perm_ws, w.tile_prefix, w.tile_map, BB, s);
+                                    w.perm_ws, w.tile_prefix, w.tile_map, BB, s, sp);
     if (err != hipSuccess) return err;
+    PrefillWs w2 = w;                                  // the second list, for the 32-row kernels
+    w2.tile_prefix = w.tile_prefix2;
+    w2.tile_map = w.tile_map2;
     const int max_mtiles = (N + BB - 1) / BB + a.E;
+    const long long max_small = std::min<long long>((N + MB - 1) / MB + a.E,
+                                                    (long long)a.E * ((BB_SPLIT_ROWS + MB - 2) / MB));
     const int nt_gu = (2 * a.I) / BB;
-    if (a.fmt == FMT_CB3G128)
+    const int np_gu = a.I / 32, np_dn = a.H / 64;     // 64-row packed tiles per projection
+    const unsigned g_gu_small = (unsigned)((max_small * np_gu + MWAVES - 1) / MWAVES);
+    const unsigned g_dn_small = (unsigned)((max_small * np_dn + MWAVES - 1) / MWAVES);
+    if (a.fmt == FMT_CB3G128) {
       grouped_gemm_big_kernel<1><<<max_mtiles * nt_gu, BTHREADS, 0, s>>>(a, w, nt_gu);
-    else
+      grouped_gemm_mid_kernel<1, 1><<<g_gu_small, 64 * MWAVES, 0, s>>>(a, w2, np_gu);
+    } else {
       grouped_gemm_big_kernel<0><<<max_mtiles * nt_gu, BTHREADS, 0, s>>>(a, w, nt_gu);
+      grouped_gemm_mid_kernel<0, 1><<<g_gu_small, 64 * MWAVES, 0, s>>>(a, w2, np_gu);
+    }
     launch_h_quant(a, w, N, s);
     const int nt_dn = a.H / BB;
     grouped_gemm_big_kernel<2><<<max_mtiles * nt_dn, BTHREADS, 0, s>>>(a, w, nt_dn);
+    grouped_gemm_mid_kernel<2, 1><<<g_dn_small, 64 * MWAVES, 0, s>>>(a, w2, np_dn);
     return hipGetLastError();
   }
   hipError_t err = launch_permute(a.ids, a.T, a.k, a.E, w.counts, w.offsets, w.perm, w.inv,

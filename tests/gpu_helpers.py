@@ -286,8 +286,9 @@ def pick_experts(ids: np.ndarray, E: int, tile_rows: int) -> list:
     """Experts whose every (t, slot) row is compared in the full-size prefill
     tests: the one with the most rows (many row tiles), the ones whose last
     row tile is the shortest and the fullest ragged tile, the lowest, middle
-    and highest active ids (their tiles sit in different XCDs' block ranges)
-    and, under skewed routing, a tail expert with one to three rows."""
+    and highest active ids (their tiles sit in different XCDs' block ranges),
+    under skewed routing a tail expert with one to three rows, and on the
+    256-row tiling the largest expert that takes 32-row tiles instead."""
     counts = np.bincount(ids.reshape(-1), minlength=E)[:E]
     act = np.nonzero(counts)[0]
     chosen = {int(counts.argmax()), int(act.min()), int(act.max()), int(act[len(act) // 2])}
@@ -299,6 +300,12 @@ def pick_experts(ids: np.ndarray, E: int, tile_rows: int) -> list:
     small = act[counts[act] <= 3]
     if len(small):
         chosen.add(int(small[0]))
+    if tile_rows == 256:
+        # the 256-row tiling hands experts below 128 rows to 32-row tiles:
+        # the largest such expert (several of them, a ragged last one)
+        tail = act[(counts[act] < 128) & (counts[act] > 32)]
+        if len(tail):
+            chosen.add(int(tail[np.argmax(counts[tail])]))
     return sorted(chosen)
 
 

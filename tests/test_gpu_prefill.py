@@ -136,6 +136,39 @@ def test_prefill_wide_intermediate(T, rows):
                                           check_tokens=None if T <= 4 else range(0, T, 9)))
 
 
+def test_prefill_mixed_tiles_skewed():
+    """The 256-row tiling with experts on both sides of the 128-row split:
+    expert 5 has 372 rows (two 256-row tiles, the second ragged) and expert 3
+    exactly 128 (one 256-row tile), expert 2 has 127 (four 32-row tiles, the
+    last ragged), expert 6 one row and the others about 60 each (32-row
+    tiles); then two ids outside [0, E), which give zero rows.  Every token
+    through every stage."""
+    c = case("wide_i", "host")
+    T = 500
+    assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 256
+    x = synth.activations(c.wl, T=T, stream=81)
+    ids = np.zeros((T, 2), np.int32)
+    ids[:372, 0] = 5
+    ids[372:, 0] = 3
+    rest = [0, 1, 4, 7]
+    ids[:, 1] = [rest[t % 4] for t in range(T)]
+    ids[:127, 1] = 2
+    ids[200, 1] = 6
+    counts = np.bincount(ids.reshape(-1), minlength=8)
+    assert counts[5] == 372 and counts[3] == 128 and counts[2] == 127 and counts[6] == 1
+    g = run_layer(c, x, prefill=True, ids_override=ids, residual=True)
+    say("mixed tiles", check_stages(c, x, g, residual=True))
+    # each expert stays in its list, so every other row is bit for bit the same
+    ids2 = ids.copy()
+    ids2[3, 1] = -4
+    ids2[401, 1] = 8
+    g2 = run_layer(c, x, prefill=True, ids_override=ids2, residual=True)
+    assert np.all(g2["out"][3, 1] == 0) and np.all(g2["out"][401, 1] == 0)
+    ok = np.ones(ids.shape, bool)
+    ok[3, 1] = ok[401, 1] = False
+    assert np.array_equal(g2["out"][ok], g["out"][ok])
+
+
 @pytest.mark.parametrize("T,rows", [(40, 32), (800, 128)])
 def test_prefill_codebook_tiny(T, rows):
     c = case("tiny", "host", moe.MOE_FMT_CB3G128)
