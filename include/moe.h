@@ -170,7 +170,9 @@ int moe_expert_ffn_prefill(const moe_dims* dims, const moe_experts* experts,
  * hold few rows on average (T*k <= 96*E, 64*E for codebook gate/up: one wave per
  * 32-row expert tile and 64-row weight tile, operands straight to the matrix
  * cores, each expert tile's weights read once), else 256 where the shapes
- * allow 256 x 256 tiles (H % 256 == 0, I >= 256), else 128.  All three give
+ * allow 256 x 256 tiles (H % 256 == 0, I >= 256), else 128.  In the 256-row
+ * tiling the experts routed fewer than 128 rows in the call take 32-row
+ * tiles instead (a second tile list, the 32-row kernels).  All of them give
  * the same result up to fp32 accumulation order.  Returns a negative
  * MOE_ERR_* code on invalid dims or T < 1. */
 int moe_ffn_prefill_tile_rows(const moe_dims* dims, int T);
