@@ -9,7 +9,8 @@
 // Pipeline (one call, no host round trip):
 //   permute   stable counting sort of the (t, slot) pairs by expert, plus the
 //             per-expert count of BM-row tiles (prefix in tile_prefix) and one
-//             record per tile {expert, first row, end row} (tile_map)
+//             record per tile {expert, first row, end row} (tile_map); the
+//             same for the 32-row second list (tile_prefix2, tile_map2)
 //   gate/up   per (expert, row tile, column tile): rows are the expert's
 //             pairs (x^ rows gathered through perm), cols 64-row packed weight
 //             tiles (32 gate rows + the same 32 up rows), multiplied with
@@ -17,7 +18,8 @@
 //             (E2M1 x E4M3 is exact in f16, so is a codebook entry).  Few rows
 //             per expert: 32-row tiles, one wave per tile pair, operands
 //             straight to registers (K split at a handful of rows); else
-//             256 x 256 (or 128 x 128) block tiles staged through LDS.
+//             256 x 256 (or 128 x 128) block tiles staged through LDS, where
+//             the experts under 128 rows keep 32-row tiles (a second list).
 //             Epilogue: h = SiLU(g ts_x ts_g) * (u ts_x ts_u), fp32, sorted order.
 //   h quant   NVFP4 of each h row (one tensor scale per (t, slot) row)
 //   down      same GEMM on h^ rows; epilogue scales by ts_h ts_down and
