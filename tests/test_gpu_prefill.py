@@ -136,14 +136,16 @@ def test_prefill_wide_intermediate(T, rows):
                                           check_tokens=None if T <= 4 else range(0, T, 9)))
 
 
-def test_prefill_mixed_tiles_skewed():
-    """The 256-row tiling with experts on both sides of the 128-row split:
+@pytest.mark.parametrize("fmt", [moe.MOE_FMT_NVFP4, moe.MOE_FMT_CB3G128])
+def test_prefill_mixed_tiles_skewed(fmt):
+    """The 256-row tiling with experts on both sides of the 128-row split, for
+    both gate/up formats:
     expert 5 has 372 rows (two 256-row tiles, the second ragged) and expert 3
     exactly 128 (one 256-row tile), expert 2 has 127 (four 32-row tiles, the
     last ragged), expert 6 one row and the others about 60 each (32-row
     tiles); then two ids outside [0, E), which give zero rows.  Every token
     through every stage."""
-    c = case("wide_i", "host")
+    c = case("wide_i", "host", fmt)
     T = 500
     assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 256
     x = synth.activations(c.wl, T=T, stream=81)
