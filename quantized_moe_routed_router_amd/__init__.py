@@ -151,7 +151,8 @@ def moe_ffn_workspace_bytes(d: moe_dims, T: int, prefill: bool) -> int:
 
 
 def moe_ffn_prefill_tile_rows(d: moe_dims, T: int) -> int:
-    """Row-tile height (32, 128 or 256) the prefill entry uses at T tokens."""
+    """Row-tile height (32, 128 or 256) the prefill entry uses at T tokens
+    (with 256, the experts routed fewer than 128 rows take 32-row tiles)."""
     rc = lib().moe_ffn_prefill_tile_rows(ctypes.byref(d), T)
     if rc < 0:
         _check(rc)
