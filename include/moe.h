@@ -172,7 +172,8 @@ int moe_expert_ffn_prefill(const moe_dims* dims, const moe_experts* experts,
  * cores, each expert tile's weights read once), else 256 where the shapes
  * allow 256 x 256 tiles (H % 256 == 0, I >= 256), else 128.  In the 256-row
  * tiling the experts routed fewer than 128 rows in the call take 32-row
- * tiles instead (a second tile list, the 32-row kernels).  All of them give
+ * tiles instead (a second tile list, run by trailing blocks of the 256-row
+ * launches with the 32-row tile body).  All of them give
  * the same result up to fp32 accumulation order.  Returns a negative
  * MOE_ERR_* code on invalid dims or T < 1. */
 int moe_ffn_prefill_tile_rows(const moe_dims* dims, int T);

@@ -19,7 +19,8 @@
 //             per expert: 32-row tiles, one wave per tile pair, operands
 //             straight to registers (K split at a handful of rows); else
 //             256 x 256 (or 128 x 128) block tiles staged through LDS, where
-//             the experts under 128 rows keep 32-row tiles (a second list).
+//             the experts under 128 rows keep 32-row tiles (a second list, run
+//             by trailing blocks of the same launch).
 //             Epilogue: h = SiLU(g ts_x ts_g) * (u ts_x ts_u), fp32, sorted order.
 //   h quant   NVFP4 of each h row (one tensor scale per (t, slot) row)
 //   down      same GEMM on h^ rows; epilogue scales by ts_h ts_down and
@@ -280,9 +281,22 @@ __global__ __launch_bounds__(PF_THREADS) void grouped_gemm_kernel(FfnArgs a, Pre
 // wave has passed the barrier that ends the step reading it.  Loads are
 // straight-line: a padding row reads a valid row with scale 0.
 constexpr int BB = 256, BBK = 64, BLDK = BBK + 8, BTHREADS = 512;
+constexpr int MB = 32, MWAVES = 4;    // the 32-row kernel's tile rows and waves per block
 
+template <int MODE, int KS>
+__device__ __forceinline__ void mid_tile_body(const FfnArgs& a, const PrefillWs& w, int n_ptiles, int blk, int wv,
+                                              int lane);
+
+// Blocks from n_big on run the 32-row tiles of the second tile list (small
+// tiles: small_prefix / small_map, np_small packed weight tiles per tile), two
+// groups of four waves per block, looping with the trailing blocks' count as
+// stride, so they fill the CUs the 256-row tiles' last round leaves idle
+// instead of waiting for a launch of their own.
 template <int MODE>
-__global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, PrefillWs w, int n_ntiles) {
+__global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, PrefillWs w, int n_ntiles,
+                                                                  const int32_t* small_prefix,
+                                                                  const int32_t* small_map, int np_small,
+                                                                  int n_big) {
   __shared__ __align__(16) _Float16 As0[BB][BLDK], As1[BB][BLDK], Bs0[BB][BLDK], Bs1[BB][BLDK];
   typedef _Float16 (*TileP)[BLDK];
   __shared__ int row_pos[BB];
@@ -291,6 +305,15 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 2, wn = wv & 3;                    // wave patch: rows wm*128, cols wn*64
+  if ((int)blockIdx.x >= n_big) {
+    PrefillWs w2 = w;
+    w2.tile_prefix = const_cast<int32_t*>(small_prefix);
+    w2.tile_map = const_cast<int32_t*>(small_map);
+    const int n_items = small_prefix[a.E] * np_small, stride = (int)gridDim.x - n_big;
+    for (int b = (int)blockIdx.x - n_big; b * 2 * MWAVES < n_items; b += stride)
+      mid_tile_body<MODE, 1>(a, w2, np_small, 2 * b + (wv >> 2), wv & 3, lane);
+    return;
+  }
   const int total_tiles = w.tile_prefix[a.E];
   const int active = total_tiles * n_ntiles;
   if ((int)blockIdx.x >= active) return;
@@ -307,6 +330,10 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
   const int gm = lb / n_ntiles, nt = lb % n_ntiles;
   const int4 tr = reinterpret_cast<const int4*>(w.tile_map)[gm];   // {expert, first row, end row}
   const int e = tr.x, row0 = tr.y, row_end = tr.z;
+  // the expert's tensor scales (gate and up, or down), read ahead of the K
+  // loop so the epilogue never waits for them
+  const float ts0 = MODE == 0 ? a.ts_gate[e] : MODE == 2 ? a.ts_down[e] : 1.0f;
+  const float ts1 = MODE == 0 ? a.ts_up[e] : 1.0f;
 
   const bool down = MODE == 2;
   const int K = down ? a.I : a.H;
@@ -541,8 +568,7 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
   float* q = reinterpret_cast<float*>(wv < 4 ? &As0[0][0] : &Bs0[0][0]) + (wv & 3) * (64 * QS);
   const int c4 = (lane & 7) * 4, rq = lane >> 3;
   if (!down) {
-    const float tsg = (MODE == 0) ? a.ts_gate[e] : 1.0f;
-    const float tsu = (MODE == 0) ? a.ts_up[e] : 1.0f;
+    const float tsg = ts0, tsu = ts1;
     // packed tile nt*4 + wn: gate cols = MFMA tile 0, up cols = tile 1; the
     // wave's h columns are that tile's 32
     const int n = (nt * 4 + wn) * 32 + c4;
@@ -570,7 +596,7 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
     }
   } else {
     // rows of o are scattered: one (t, slot) pair each
-    const float tsd = a.ts_down[e];
+    const float tsd = ts0;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -610,7 +636,6 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 // alternate, one step's loads in flight while the other's are consumed.
 // Codebook gate/up (MODE 1): the lane reads its chunk's three index words
 // and its row's eight fp16 entries instead.  K % 128 == 0 (even step count).
-constexpr int MB = 32, MWAVES = 4;
 constexpr int MID_MAX_AVG_ROWS = 96;   // 32-row tiles while T*k <= this * E
 constexpr int MID_MAX_AVG_ROWS_CB = 64;   // the same for codebook gate/up (VALU-heavier decode:
                                           // it repays the big tiles' reuse sooner)
@@ -618,6 +643,7 @@ constexpr int MID_MAX_AVG_ROWS_CB = 64;   // the same for codebook gate/up (VALU
 // 32-row kernels stream an expert's weights once per 32 rows, the 256-row
 // ones stage a mostly empty tile at full cost).
 constexpr int BB_SPLIT_ROWS = 128;
+constexpr int SMALL_BLOCKS = 256;     // trailing 32-row-tile blocks of a 256-row launch: the CU count
 
 struct MidRegs {
   u32x4 ac;          // A codes, this lane's chunk of its row
@@ -637,18 +663,20 @@ __device__ __forceinline__ half8_t cat8(half2_t a, half2_t b, half2_t c, half2_t
 // each on 1/KS of K (gate/up at small N), else 1.  The codebook mode is held
 // to 168 VGPRs (three waves per SIMD; a few spilled registers): 4-5 % faster
 // at 16 and 1024 tokens than at 252 VGPRs and two waves.
+// The body of one block of MWAVES waves (block index blk, wave wv); also run
+// by the 256-row kernel's trailing blocks over the second tile list.
 template <int MODE, int KS>
-__global__ __launch_bounds__(64 * MWAVES, MODE == 1 ? 3 : 1) void grouped_gemm_mid_kernel(FfnArgs a, PrefillWs w, int n_ptiles) {
+__device__ __forceinline__ void mid_tile_body(const FfnArgs& a, const PrefillWs& w, int n_ptiles, int blk, int wv,
+                                              int lane) {
   constexpr int ksplit = KS;
   constexpr int IPB = MWAVES / KS;                 // items per block; KS waves per item
   constexpr bool down = MODE == 2;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = wv / KS, ks = wv % KS;
   const int total_items = w.tile_prefix[a.E] * n_ptiles;
-  if ((int)blockIdx.x * IPB >= total_items) return;               // whole block idle
-  const int item = blockIdx.x * IPB + slot;
+  if (blk * IPB >= total_items) return;                           // whole block idle
+  const int item = blk * IPB + slot;
   const bool valid = item < total_items;
-  const int tp = valid ? item : blockIdx.x * IPB;                 // idle waves shadow slot 0
+  const int tp = valid ? item : blk * IPB;                        // idle waves shadow slot 0
   const int gm = tp / n_ptiles, p = tp % n_ptiles;
   const int4 tr = reinterpret_cast<const int4*>(w.tile_map)[gm];   // {expert, first row, end row}
   const int e = tr.x, row0 = tr.y, row_end = tr.z;
@@ -776,6 +804,11 @@ __global__ __launch_bounds__(64 * MWAVES, MODE == 1 ? 3 : 1) void grouped_gemm_m
       for (int j = 0; j < 2; ++j) a.out[(size_t)pr * a.H + p * 64 + j * 32 + r] = acc[j][q] * (sc * tsd);
     }
   }
+}
+
+template <int MODE, int KS>
+__global__ __launch_bounds__(64 * MWAVES, MODE == 1 ? 3 : 1) void grouped_gemm_mid_kernel(FfnArgs a, PrefillWs w, int n_ptiles) {
+  mid_tile_body<MODE, KS>(a, w, n_ptiles, (int)blockIdx.x, (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63));
 }
 
 // NVFP4 of each h row (sorted order), one wave per row, one pass: lane l
@@ -914,27 +947,27 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
     hipError_t err = launch_permute(a.ids, a.T, a.k, a.E, w.counts, w.offsets, w.perm, w.inv,
                                     w.perm_ws, w.tile_prefix, w.tile_map, BB, s, sp);
     if (err != hipSuccess) return err;
-    PrefillWs w2 = w;                                  // the second list, for the 32-row kernels
-    w2.tile_prefix = w.tile_prefix2;
-    w2.tile_map = w.tile_map2;
     const int max_mtiles = (N + BB - 1) / BB + a.E;
     const long long max_small = std::min<long long>((N + MB - 1) / MB + a.E,
                                                     (long long)a.E * ((BB_SPLIT_ROWS + MB - 2) / MB));
     const int nt_gu = (2 * a.I) / BB;
     const int np_gu = a.I / 32, np_dn = a.H / 64;     // 64-row packed tiles per projection
-    const unsigned g_gu_small = (unsigned)((max_small * np_gu + MWAVES - 1) / MWAVES);
-    const unsigned g_dn_small = (unsigned)((max_small * np_dn + MWAVES - 1) / MWAVES);
-    if (a.fmt == FMT_CB3G128) {
-      grouped_gemm_big_kernel<1><<<max_mtiles * nt_gu, BTHREADS, 0, s>>>(a, w, nt_gu);
-      grouped_gemm_mid_kernel<1, 1><<<g_gu_small, 64 * MWAVES, 0, s>>>(a, w2, np_gu);
-    } else {
-      grouped_gemm_big_kernel<0><<<max_mtiles * nt_gu, BTHREADS, 0, s>>>(a, w, nt_gu);
-      grouped_gemm_mid_kernel<0, 1><<<g_gu_small, 64 * MWAVES, 0, s>>>(a, w2, np_gu);
-    }
+    // the second list's 32-row tiles ride in trailing blocks of the same
+    // launches (two groups of MWAVES waves per block, at most one block per CU)
+    const int n_big_gu = max_mtiles * nt_gu;
+    const int g_gu_small = std::min(SMALL_BLOCKS, (int)((max_small * np_gu + 2 * MWAVES - 1) / (2 * MWAVES)));
+    if (a.fmt == FMT_CB3G128)
+      grouped_gemm_big_kernel<1><<<n_big_gu + g_gu_small, BTHREADS, 0, s>>>(a, w, nt_gu, w.tile_prefix2, w.tile_map2,
+                                                                             np_gu, n_big_gu);
+    else
+      grouped_gemm_big_kernel<0><<<n_big_gu + g_gu_small, BTHREADS, 0, s>>>(a, w, nt_gu, w.tile_prefix2, w.tile_map2,
+                                                                             np_gu, n_big_gu);
     launch_h_quant(a, w, N, s);
     const int nt_dn = a.H / BB;
-    grouped_gemm_big_kernel<2><<<max_mtiles * nt_dn, BTHREADS, 0, s>>>(a, w, nt_dn);
-    grouped_gemm_mid_kernel<2, 1><<<g_dn_small, 64 * MWAVES, 0, s>>>(a, w2, np_dn);
+    const int n_big_dn = max_mtiles * nt_dn;
+    const int g_dn_small = std::min(SMALL_BLOCKS, (int)((max_small * np_dn + 2 * MWAVES - 1) / (2 * MWAVES)));
+    grouped_gemm_big_kernel<2><<<n_big_dn + g_dn_small, BTHREADS, 0, s>>>(a, w, nt_dn, w.tile_prefix2, w.tile_map2,
+                                                                           np_dn, n_big_dn);
     return hipGetLastError();
   }
   hipError_t err = launch_permute(a.ids, a.T, a.k, a.E, w.counts, w.offsets, w.perm, w.inv,
