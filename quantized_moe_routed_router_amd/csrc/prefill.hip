@@ -107,6 +107,21 @@ __device__ __forceinline__ void dequant32_nvfp4(u32x4 cw, uint32_t sw, half2_t (
   o[14] = fp4x2_to_f16x2<2>(cw.w) * b; o[15] = fp4x2_to_f16x2<3>(cw.w) * b;
 }
 
+__device__ __forceinline__ half8_t cat8(half2_t a, half2_t b, half2_t c, half2_t d) {
+  const half4_t lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const half4_t hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Eight E2M1 codes (one dword: element 2j in byte j's low nibble) times the
+// block scale s (both halves) -> eight f16 values, exact.  The hardware's
+// scaled conversion applies only the exponent of its scale operand (a device
+// probe over all code bytes and E4M3 scales), so the scale is an f16 multiply.
+__device__ __forceinline__ half8_t dq8(uint32_t w, half2_t s) {
+  return cat8(fp4x2_to_f16x2<0>(w) * s, fp4x2_to_f16x2<1>(w) * s, fp4x2_to_f16x2<2>(w) * s,
+              fp4x2_to_f16x2<3>(w) * s);
+}
+
 __device__ __forceinline__ void store32(_Float16* dst, const half2_t (&o)[16]) {
   u32x4* d = reinterpret_cast<u32x4*>(dst);
 #pragma unroll
@@ -274,14 +289,22 @@ __global__ __launch_bounds__(PF_THREADS) void grouped_gemm_kernel(FfnArgs a, Pre
 // (2 x 4), each wave a 128 x 64 patch (4 x 2 tiles of v_mfma_f32_32x32x16_f16,
 // 128 accumulator registers), two waves per SIMD so one wave's dequantization
 // runs while the other's MFMAs execute.  LDS holds two K-step buffers of A
-// (256 activation rows) and B (256 weight columns) as f16 (147,456 B of the
-// 160 KiB), as four distinct objects.  Step s: the MFMAs on buffer s%2, the
-// registers fetched for step s+1 dequantized into buffer (s+1)%2, step s+3's
-// global loads issued (two register sets), one barrier.  A buffer is rewritten only after every
-// wave has passed the barrier that ends the step reading it.  Loads are
+// (256 activation rows) and B (256 weight rows) dequantized to f16 (147,456 B
+// of the 160 KiB).  Step s: the MFMAs on buffer s%2 with the registers fetched
+// for step s+1 dequantized into buffer (s+1)%2 alongside, step s+3's global
+// loads issued (two register sets), one barrier.  A buffer is rewritten only
+// after every wave has passed the barrier that ends the step reading it.
+// Staging: wave w dequantizes tile rows 32w .. 32w+31 of A (lane l: row
+// 32w + l%32, chunk l/32 of the step) and chunk w%2 of the step of packed
+// weight tile w/2 for B (lane = weight row: one 1 KiB-contiguous load).
+// k order: in K step s, lane l of a 32-row fragment holds chunk 2s + l/32 of
+// its row (32 elements) and MFMA kk of the step takes the chunk's elements
+// 8kk .. 8kk+7, for A and B alike, so every product is summed once.  Loads are
 // straight-line: a padding row reads a valid row with scale 0.
 constexpr int BB = 256, BBK = 64, BLDK = BBK + 8, BTHREADS = 512;
 constexpr int MB = 32, MWAVES = 4;    // the 32-row kernel's tile rows and waves per block
+constexpr int OPND_F16 = BB * BLDK * 2;          // one operand's K step in LDS: 256 rows x 72 halves
+constexpr int EPI_BYTES = 8 * 64 * 36 * 4;       // the epilogue's eight 64 x 36-float wave regions
 
 template <int MODE, int KS>
 __device__ __forceinline__ void mid_tile_body(const FfnArgs& a, const PrefillWs& w, int n_ptiles, int blk, int wv,
@@ -297,8 +320,9 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
                                                                   const int32_t* small_prefix,
                                                                   const int32_t* small_map, int np_small,
                                                                   int n_big) {
-  __shared__ __align__(16) _Float16 As0[BB][BLDK], As1[BB][BLDK], Bs0[BB][BLDK], Bs1[BB][BLDK];
-  typedef _Float16 (*TileP)[BLDK];
+  constexpr int STAGE = 2 * OPND_F16;              // A at 0, B at OPND_F16
+  static_assert(2 * STAGE >= EPI_BYTES, "the epilogue reuses the stage buffers");
+  __shared__ __align__(16) uint8_t lds[2 * STAGE];
   __shared__ int row_pos[BB];
   __shared__ int row_pair[BB];         // (t, slot) pair of the row: where down writes o
   __shared__ float row_scale[BB];
@@ -335,7 +359,7 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
   const float ts0 = MODE == 0 ? a.ts_gate[e] : MODE == 2 ? a.ts_down[e] : 1.0f;
   const float ts1 = MODE == 0 ? a.ts_up[e] : 1.0f;
 
-  const bool down = MODE == 2;
+  constexpr bool down = MODE == 2;
   const int K = down ? a.I : a.H;
   const int S = K / BBK;                                   // even, >= 4
   const size_t w_tile_bytes = (MODE == 1) ? cb_tile_bytes(K) : tile_bytes(K);
@@ -343,11 +367,10 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
                                      : (MODE == 1 ? cb_gate_up_expert_bytes(a.H, a.I) : gate_up_expert_bytes(a.H, a.I));
   const uint8_t* wbase = (down ? a.down : a.gate_up) + (size_t)e * w_expert_bytes + (size_t)(nt * 4) * w_tile_bytes;
 
-  // staging roles: A row sr, chunk sc (32 K-elements); B packed tile bj,
-  // lane bl, chunk sc
-  const int sr = tid >> 1, sc = tid & 1;
-  const int bj = sr >> 6, bl = sr & 63;
-  const uint8_t* btile = wbase + (size_t)bj * w_tile_bytes;
+  const int h = lane >> 5, r = lane & 31;
+  const int sra = 32 * wv + r;                             // this thread's A row of the tile (chunk h)
+  const int bh = wv & 1;                                   // its B chunk parity (B row 64 (wv/2) + lane)
+  const uint8_t* btile = wbase + (size_t)(wv >> 1) * w_tile_bytes;
 
   // one K step's global data for this thread
   struct Regs {
@@ -355,16 +378,18 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
     uint32_t asw, bsw, p0, p1, p2;
   };
   auto load_B = [&](Regs& R, int st) {
-    const int ck = (st * BBK + 32 * sc) / 32;
+    const int ck = 2 * st + bh;
     if (MODE == 1) {
+      // group ck/4: [64 rows][3 index words x 4 dwords], then [64 rows][8 fp16]
       const uint8_t* grp = btile + (size_t)(ck >> 2) * cb_group_bytes();
-      const uint32_t* iw = reinterpret_cast<const uint32_t*>(grp + bl * 48);
+      const uint32_t* iw = reinterpret_cast<const uint32_t*>(grp + lane * 48);
       const int d = ck & 3;
       R.p0 = iw[d]; R.p1 = iw[4 + d]; R.p2 = iw[8 + d];
-      R.bcw = *reinterpret_cast<const u32x4*>(grp + 64 * 48 + bl * 16);
+      R.bcw = *reinterpret_cast<const u32x4*>(grp + 64 * 48 + lane * 16);
     } else {
-      R.bcw = *reinterpret_cast<const u32x4*>(btile + (size_t)ck * 1024 + bl * 16);
-      R.bsw = *reinterpret_cast<const uint16_t*>(btile + tile_scale_offset(K) + (size_t)(ck >> 2) * 512 + bl * 8 + (ck & 3) * 2);
+      R.bcw = *reinterpret_cast<const u32x4*>(btile + (size_t)ck * 1024 + lane * 16);
+      R.bsw = *reinterpret_cast<const uint16_t*>(btile + tile_scale_offset(K) + (size_t)(ck >> 2) * 512 + lane * 8 +
+                                                 (ck & 3) * 2);
     }
   };
   // the first two steps' weights depend only on the tile: in flight before
@@ -388,42 +413,59 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
   }
   __syncthreads();
 
-  const bool avalid = row_pos[sr] >= 0;
+  const bool avalid = row_pos[sra] >= 0;
   const uint8_t* acodes;
   const uint8_t* ascales;
   {
-    const int rp = avalid ? row_pos[sr] : row0;         // row0 < row_end: a valid row
+    const int rp = avalid ? row_pos[sra] : row0;        // row0 < row_end: a valid row
     if (down) {
       acodes = w.hq_codes + (size_t)rp * (a.I / 2);
       ascales = w.hq_scales + (size_t)rp * (a.I / 16);
     } else {
-      const int t = row_pair[sr] / a.k;                 // padding rows: pair 0, a valid token
+      const int t = row_pair[sra] / a.k;                // padding rows: pair 0, a valid token
       acodes = a.x_codes + (size_t)t * (a.H / 2);
       ascales = a.x_scales + (size_t)t * (a.H / 16);
     }
   }
-
   auto load_A = [&](Regs& R, int st) {
-    const int k0 = st * BBK + 32 * sc;
-    R.acw = *reinterpret_cast<const u32x4*>(acodes + k0 / 2);
-    R.asw = *reinterpret_cast<const uint16_t*>(ascales + k0 / 16);
+    const int ck = 2 * st + h;
+    R.acw = *reinterpret_cast<const u32x4*>(acodes + ck * 16);
+    R.asw = *reinterpret_cast<const uint16_t*>(ascales + ck * 2);
   };
   auto load_step = [&](Regs& R, int st) {
     load_A(R, st);
     load_B(R, st);
   };
-  auto stage = [&](const Regs& R, auto bconst) {
-    constexpr int b = decltype(bconst)::value;
-    TileP As = b ? As1 : As0;
-    TileP Bs = b ? Bs1 : Bs0;
-    half2_t o[16];
-    // padding rows: scale 0 stages zeros (applied here, not at the load, so
-    // the load is not waited for until its step is staged)
-    dequant32_nvfp4(R.acw, avalid ? R.asw : 0u, o);
-    store32(&As[sr][32 * sc], o);
-    if (MODE == 1) dequant32_cb(R.p0, R.p1, R.p2, R.bcw, o);
-    else dequant32_nvfp4(R.bcw, R.bsw, o);
-    store32(&Bs[sr][32 * sc], o);
+
+  // where this thread's staged elements 8kk .. 8kk+7 go (bytes in a stage)
+  const int a_wr = (sra * BLDK + 32 * h) * 2;
+  const int b_wr = OPND_F16 + (((wv >> 1) * 64 + lane) * BLDK + 32 * bh) * 2;
+  // part kk of the staging of R into buffer dst: elements 8kk .. 8kk+7 of
+  // this thread's A and B chunks (sa, sb: their block scales; cbt: the B
+  // row's codebook, MODE 1)
+  auto put = [&](const Regs& R, uint8_t* dst, int kk, half2_t sa, half2_t sb, const CbTable& cbt) {
+    const half2_t s = kk < 2 ? half2_t{sa.x, sa.x} : half2_t{sa.y, sa.y};
+    const uint32_t aw = kk == 0 ? R.acw.x : kk == 1 ? R.acw.y : kk == 2 ? R.acw.z : R.acw.w;
+    *reinterpret_cast<half8_t*>(dst + a_wr + 16 * kk) = dq8(aw, s);
+    half8_t bv;
+    if constexpr (MODE == 1) {
+      half2_t ob[4];
+      if (kk == 0) cb_decode8<0>(R.p0, R.p1, R.p2, cbt, ob);
+      else if (kk == 1) cb_decode8<1>(R.p0, R.p1, R.p2, cbt, ob);
+      else if (kk == 2) cb_decode8<2>(R.p0, R.p1, R.p2, cbt, ob);
+      else cb_decode8<3>(R.p0, R.p1, R.p2, cbt, ob);
+      bv = cat8(ob[0], ob[1], ob[2], ob[3]);
+    } else {
+      const half2_t t = kk < 2 ? half2_t{sb.x, sb.x} : half2_t{sb.y, sb.y};
+      const uint32_t bw = kk == 0 ? R.bcw.x : kk == 1 ? R.bcw.y : kk == 2 ? R.bcw.z : R.bcw.w;
+      bv = dq8(bw, t);
+    }
+    *reinterpret_cast<half8_t*>(dst + b_wr + 16 * kk) = bv;
+  };
+  auto scales_of = [&](const Regs& R, half2_t& sa, half2_t& sb, CbTable& cbt) {
+    sa = e4m3x2_to_f16x2(avalid ? R.asw : 0u);          // padding rows: scale 0 stages zeros
+    if constexpr (MODE == 1) cbt = cb_table(R.bcw);
+    else sb = e4m3x2_to_f16x2(R.bsw);
   };
 
   float16_t acc[4][2];
@@ -432,143 +474,78 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  auto mfma_step = [&](auto bconst) {
-    constexpr int b = decltype(bconst)::value;
-    TileP As = b ? As1 : As0;
-    TileP Bs = b ? Bs1 : Bs0;
-#pragma unroll
-    for (int kk = 0; kk < BBK; kk += 16) {
-      half8_t af[4], bf[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const half8_t*>(&As[wm * 128 + i * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const half8_t*>(&Bs[wn * 64 + j * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // MFMAs on buffer b with the staging of the next step into buffer 1-b
-  // spread over its four K slices (NVFP4 operands): slice kk dequantizes and
-  // writes elements 8kk..8kk+7 of this thread's A and B chunks, and the
-  // scheduling groups interleave that VALU work with the slice's MFMAs, so the
-  // matrix cores are not idle while the block stages.
-  auto mfma_stage_step = [&](auto bconst, const Regs& R) {
-    constexpr int b = decltype(bconst)::value;
-    TileP As = b ? As1 : As0;
-    TileP Bs = b ? Bs1 : Bs0;
-    TileP Ad = b ? As0 : As1;
-    TileP Bd = b ? Bs0 : Bs1;
-    const uint32_t asw = avalid ? R.asw : 0u;
-    const _Float16 as0 = (_Float16)e4m3_to_f32(asw & 0xFF), as1 = (_Float16)e4m3_to_f32((asw >> 8) & 0xFF);
-    _Float16 bs0 = 0, bs1 = 0;
+  // the MFMAs of the step in buffer src; with nxt, the next step's registers
+  // are staged into buffer dst alongside, a quarter per K slice
+  auto compute = [&](const uint8_t* src, const Regs* nxt, uint8_t* dst) {
+    half2_t sa{}, sb{};
     CbTable cbt{};
-    if constexpr (MODE == 1) cbt = cb_table(R.bcw);
-    else {
-      bs0 = (_Float16)e4m3_to_f32(R.bsw & 0xFF);
-      bs1 = (_Float16)e4m3_to_f32((R.bsw >> 8) & 0xFF);
-    }
+    if (nxt) scales_of(*nxt, sa, sb, cbt);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       half8_t af[4], bf[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const half8_t*>(&As[wm * 128 + i * 32 + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
+        af[i] = *reinterpret_cast<const half8_t*>(src + ((wm * 128 + i * 32 + r) * BLDK + 32 * h + 8 * kk) * 2);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const half8_t*>(&Bs[wn * 64 + j * 32 + (lane & 31)][16 * kk + 8 * (lane >> 5)]);
-      // staging part kk: dword kk of each chunk (elements 8kk..8kk+7)
-      {
-        const uint32_t aw = kk == 0 ? R.acw.x : kk == 1 ? R.acw.y : kk == 2 ? R.acw.z : R.acw.w;
-        const _Float16 sa = kk < 2 ? as0 : as1;
-        const half2_t a2 = {sa, sa};
-        half2_t oa[4], ob[4];
-        oa[0] = fp4x2_to_f16x2<0>(aw) * a2; oa[1] = fp4x2_to_f16x2<1>(aw) * a2;
-        oa[2] = fp4x2_to_f16x2<2>(aw) * a2; oa[3] = fp4x2_to_f16x2<3>(aw) * a2;
-        if constexpr (MODE == 1) {
-          // codebook entries, no scale (kk is a constant once unrolled)
-          if (kk == 0) cb_decode8<0>(R.p0, R.p1, R.p2, cbt, ob);
-          else if (kk == 1) cb_decode8<1>(R.p0, R.p1, R.p2, cbt, ob);
-          else if (kk == 2) cb_decode8<2>(R.p0, R.p1, R.p2, cbt, ob);
-          else cb_decode8<3>(R.p0, R.p1, R.p2, cbt, ob);
-        } else {
-          const uint32_t bw = kk == 0 ? R.bcw.x : kk == 1 ? R.bcw.y : kk == 2 ? R.bcw.z : R.bcw.w;
-          const _Float16 sb = kk < 2 ? bs0 : bs1;
-          const half2_t b2 = {sb, sb};
-          ob[0] = fp4x2_to_f16x2<0>(bw) * b2; ob[1] = fp4x2_to_f16x2<1>(bw) * b2;
-          ob[2] = fp4x2_to_f16x2<2>(bw) * b2; ob[3] = fp4x2_to_f16x2<3>(bw) * b2;
-        }
-        *reinterpret_cast<u32x4*>(&Ad[sr][32 * sc + 8 * kk]) = *reinterpret_cast<const u32x4*>(oa);
-        *reinterpret_cast<u32x4*>(&Bd[sr][32 * sc + 8 * kk]) = *reinterpret_cast<const u32x4*>(ob);
-      }
+        bf[j] = *reinterpret_cast<const half8_t*>(src + OPND_F16 +
+                                                  ((wn * 64 + j * 32 + r) * BLDK + 32 * h + 8 * kk) * 2);
+      if (nxt) put(*nxt, dst, kk, sa, sb, cbt);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      // this slice: fragment reads, then MFMA / VALU alternating (the
-      // codebook decode has about five times the VALU work), then the writes
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, MODE == 1 ? 4 : 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
     }
   };
 
   // Two register sets, so a step's loads are issued two steps before it is
   // staged.  At the top of each loop pass (step st even): buffer 0 holds
   // step st, R1 step st+1, R0 step st+2.
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
+  uint8_t* const buf0 = lds;
+  uint8_t* const buf1 = lds + STAGE;
   load_A(R0, 0);
   load_A(R1, 1);
-  stage(R0, B0{});
+  {
+    half2_t sa, sb{};
+    CbTable cbt{};
+    scales_of(R0, sa, sb, cbt);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) put(R0, buf0, kk, sa, sb, cbt);
+  }
   __syncthreads();
   load_step(R0, 2);
   int st = 0;
   for (; st + 4 < S; st += 2) {
-    mfma_stage_step(B0{}, R1);
+    compute(buf0, &R1, buf1);
     load_step(R1, st + 3);
     __syncthreads();
-    mfma_stage_step(B1{}, R0);
+    compute(buf1, &R0, buf0);
     load_step(R0, st + 4);
     __syncthreads();
   }
   // the last four steps (st = S - 4): buffer 0 = st, R1 = st+1, R0 = st+2
-  mfma_step(B0{});
-  stage(R1, B1{});
+  compute(buf0, &R1, buf1);
   load_step(R1, st + 3);
   __syncthreads();
-  mfma_step(B1{});
-  stage(R0, B0{});
+  compute(buf1, &R0, buf0);
   __syncthreads();
-  mfma_step(B0{});
-  stage(R1, B1{});
+  compute(buf0, &R1, buf1);
   __syncthreads();
-  mfma_step(B1{});
+  compute(buf1, nullptr, nullptr);
+  __syncthreads();                                         // every wave done with both buffers
 
-  // ---- epilogue.  acc[i][j][r]: row wm*128 + i*32 + (r%4) + 8*(r/4) + 4*(lane/32),
-  // col wn*64 + j*32 + lane%32 of the 256x256 tile
-  // Both epilogues turn each wave's results around in LDS, a 64 x 32 quarter
-  // at a time, and write 16 B per lane (eight lanes per 32-column row, eight
-  // rows per store instruction).  Buffer 0 (A and B) is free: its last reader
-  // passed the barrier before the last MFMA step.  Each wave uses only its
-  // own 9 KB region, so a wave-level LDS sync suffices.
+  // ---- epilogue.  acc[i][j][q]: row wm*128 + i*32 + (q%4) + 8*(q/4) + 4*h,
+  // col wn*64 + j*32 + r of the 256x256 tile.  Each wave turns its results
+  // around in its own 9 KB of LDS (the stage buffers are free), a 64 x 32
+  // quarter at a time, and writes 16 B per lane (eight lanes per 32-column
+  // row, eight rows per store instruction); a wave-level LDS sync suffices.
   constexpr int QS = 36;                                   // row stride (floats) of a quarter
-  float* q = reinterpret_cast<float*>(wv < 4 ? &As0[0][0] : &Bs0[0][0]) + (wv & 3) * (64 * QS);
+  float* q = reinterpret_cast<float*>(lds) + wv * (64 * QS);
   const int c4 = (lane & 7) * 4, rq = lane >> 3;
   if (!down) {
-    const float tsg = ts0, tsu = ts1;
     // packed tile nt*4 + wn: gate cols = MFMA tile 0, up cols = tile 1; the
     // wave's h columns are that tile's 32
     const int n = (nt * 4 + wn) * 32 + c4;
@@ -577,12 +554,12 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 #pragma unroll
       for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lr = i2 * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+        for (int qq = 0; qq < 16; ++qq) {
+          const int lr = i2 * 32 + (qq & 3) + 8 * (qq >> 2) + 4 * h;
           const float sx = row_scale[wm * 128 + ih * 64 + lr];
-          const float g = acc[2 * ih + i2][0][r] * (sx * tsg);
-          const float u = acc[2 * ih + i2][1][r] * (sx * tsu);
-          q[lr * QS + (lane & 31)] = silu_mul(g, u);
+          const float g = acc[2 * ih + i2][0][qq] * (sx * ts0);
+          const float u = acc[2 * ih + i2][1][qq] * (sx * ts1);
+          q[lr * QS + r] = silu_mul(g, u);
         }
       wave_lds_sync();
 #pragma unroll
@@ -596,7 +573,6 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
     }
   } else {
     // rows of o are scattered: one (t, slot) pair each
-    const float tsd = ts0;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -604,8 +580,8 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            q[(i2 * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5)) * QS + (lane & 31)] = acc[2 * ih + i2][j][r];
+          for (int qq = 0; qq < 16; ++qq)
+            q[(i2 * 32 + (qq & 3) + 8 * (qq >> 2) + 4 * h) * QS + r] = acc[2 * ih + i2][j][qq];
         wave_lds_sync();
         const int n = nt * BB + wn * 64 + j * 32 + c4;
 #pragma unroll
@@ -614,7 +590,7 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
           const int rl = wm * 128 + ih * 64 + row;
           const float4_t v = *reinterpret_cast<const float4_t*>(q + row * QS + c4);
           if (row_pos[rl] >= 0) {
-            const float sc = row_scale[rl] * tsd;
+            const float sc = row_scale[rl] * ts0;
             *reinterpret_cast<float4_t*>(a.out + (size_t)row_pair[rl] * a.H + n) = v * sc;
           }
         }
@@ -652,12 +628,6 @@ struct MidRegs {
   uint32_t bs[2];    // B block scales (NVFP4)
   uint32_t bp[2][3]; // B index words (codebook)
 };
-
-__device__ __forceinline__ half8_t cat8(half2_t a, half2_t b, half2_t c, half2_t d) {
-  const half4_t lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
-  const half4_t hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
 
 // MODE 0: gate/up NVFP4, 1: gate/up codebook, 2: down.  KS: waves per item,
 // each on 1/KS of K (gate/up at small N), else 1.  The codebook mode is held
