@@ -78,9 +78,25 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 constexpr int RG_BM = 128, RG_BN = 128, RG_BK = 64, RG_LDK = RG_BK + 8;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> their three bf16 parts, each part's pair packed in one
+// dword (first value in the low half): hi = bf16(w), mid = bf16(w - hi),
+// lo = bf16(w - hi - mid), rounded to nearest even by the hardware pair
+// conversion; the differences are exact in fp32, so hi + mid + lo = w.
+__device__ __forceinline__ void split3_pk(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  auto cvt = [](float2_t f) {
+    const bf16x2_t v = __builtin_convertvector(f, bf16x2_t);
+    return *reinterpret_cast<const uint32_t*>(&v);
+  };
+  auto widen = [](uint32_t q) { return float2_t{__uint_as_float(q << 16), __uint_as_float(q & 0xFFFF0000u)}; };
+  const float2_t w = {a, b};
+  hi = cvt(w);
+  const float2_t r1 = w - widen(hi);
+  mid = cvt(r1);
+  const float2_t r2 = r1 - widen(mid);
+  lo = cvt(r2);
 }
 
 // (token tile, expert tile) of this block for the token-tile x expert-tile
@@ -144,16 +160,9 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
     for (int i = 0; i < 8; i += 2) {
       uint32_t p[3][4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float wf = ev ? wa[i + (c >> 2)][c & 3] : 0.0f;
-        const uint32_t hi = bf16_bits_rne(wf);
-        const float r1 = wf - __uint_as_float(hi << 16);
-        const uint32_t mid = bf16_bits_rne(r1);
-        const float r2 = r1 - __uint_as_float(mid << 16);
-        const uint32_t lo = bf16_bits_rne(r2);
-        const int wd = c >> 1, sh = (c & 1) * 16;
-        if (!(c & 1)) { p[0][wd] = hi; p[1][wd] = mid; p[2][wd] = lo; }
-        else { p[0][wd] |= hi << sh; p[1][wd] |= mid << sh; p[2][wd] |= lo << sh; }
+      for (int wd = 0; wd < 4; ++wd) {
+        auto wf = [&](int c) { return ev ? wa[i + (c >> 2)][c & 3] : 0.0f; };
+        split3_pk(wf(2 * wd), wf(2 * wd + 1), p[0][wd], p[1][wd], p[2][wd]);
       }
 #pragma unroll
       for (int q = 0; q < 3; ++q)
@@ -253,16 +262,9 @@ __global__ __launch_bounds__(512) void router_mfma256_kernel(const uint16_t* __r
     for (int i = 0; i < 4; i += 2) {
       uint32_t p[3][4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float wf = ev ? wa[i + (c >> 2)][c & 3] : 0.0f;
-        const uint32_t hi = bf16_bits_rne(wf);
-        const float r1 = wf - __uint_as_float(hi << 16);
-        const uint32_t mid = bf16_bits_rne(r1);
-        const float r2 = r1 - __uint_as_float(mid << 16);
-        const uint32_t lo = bf16_bits_rne(r2);
-        const int wd = c >> 1, sh = (c & 1) * 16;
-        if (!(c & 1)) { p[0][wd] = hi; p[1][wd] = mid; p[2][wd] = lo; }
-        else { p[0][wd] |= hi << sh; p[1][wd] |= mid << sh; p[2][wd] |= lo << sh; }
+      for (int wd = 0; wd < 4; ++wd) {
+        auto wf = [&](int c) { return ev ? wa[i + (c >> 2)][c & 3] : 0.0f; };
+        split3_pk(wf(2 * wd), wf(2 * wd + 1), p[0][wd], p[1][wd], p[2][wd]);
       }
 #pragma unroll
       for (int q = 0; q < 3; ++q)
@@ -362,16 +364,9 @@ __global__ __launch_bounds__(64 * RS_WAVES) void router_splitk_kernel(const uint
       if (gb + i >= g1) break;
       uint32_t p[3][4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float wf = b.wa[i][c >> 2][c & 3];
-        const uint32_t hi = bf16_bits_rne(wf);
-        const float r1 = wf - __uint_as_float(hi << 16);
-        const uint32_t mid = bf16_bits_rne(r1);
-        const float r2 = r1 - __uint_as_float(mid << 16);
-        const uint32_t lo = bf16_bits_rne(r2);
-        const int wd = c >> 1, sh = (c & 1) * 16;
-        if (!(c & 1)) { p[0][wd] = hi; p[1][wd] = mid; p[2][wd] = lo; }
-        else { p[0][wd] |= hi << sh; p[1][wd] |= mid << sh; p[2][wd] |= lo << sh; }
+      for (int wd = 0; wd < 4; ++wd) {
+        auto wf = [&](int c) { return b.wa[i][c >> 2][c & 3]; };
+        split3_pk(wf(2 * wd), wf(2 * wd + 1), p[0][wd], p[1][wd], p[2][wd]);
       }
       const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&b.xa[i]);
 #pragma unroll
@@ -444,16 +439,9 @@ __global__ __launch_bounds__(64 * RS_WAVES) void router_splitk16_kernel(const ui
       if (gb + i >= g1) break;
       uint32_t p[3][4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float wf = b.wa[i][c >> 2][c & 3];
-        const uint32_t hi = bf16_bits_rne(wf);
-        const float r1 = wf - __uint_as_float(hi << 16);
-        const uint32_t mid = bf16_bits_rne(r1);
-        const float r2 = r1 - __uint_as_float(mid << 16);
-        const uint32_t lo = bf16_bits_rne(r2);
-        const int wd = c >> 1, sh = (c & 1) * 16;
-        if (!(c & 1)) { p[0][wd] = hi; p[1][wd] = mid; p[2][wd] = lo; }
-        else { p[0][wd] |= hi << sh; p[1][wd] |= mid << sh; p[2][wd] |= lo << sh; }
+      for (int wd = 0; wd < 4; ++wd) {
+        auto wf = [&](int c) { return b.wa[i][c >> 2][c & 3]; };
+        split3_pk(wf(2 * wd), wf(2 * wd + 1), p[0][wd], p[1][wd], p[2][wd]);
       }
       const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&b.xa[i]);
 #pragma unroll
