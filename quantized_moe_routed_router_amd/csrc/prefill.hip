@@ -296,7 +296,8 @@ __global__ __launch_bounds__(PF_THREADS) void grouped_gemm_kernel(FfnArgs a, Pre
 // after every wave has passed the barrier that ends the step reading it.
 // Staging: wave w dequantizes tile rows 32w .. 32w+31 of A (lane l: row
 // 32w + l%32, chunk l/32 of the step) and chunk w%2 of the step of packed
-// weight tile w/2 for B (lane = weight row: one 1 KiB-contiguous load).
+// weight tile w/2 for B (lane = weight row: one 1 KiB-contiguous load; the
+// codebook mode: a thread pair per weight row, one chunk each).
 // k order: in K step s, lane l of a 32-row fragment holds chunk 2s + l/32 of
 // its row (32 elements) and MFMA kk of the step takes the chunk's elements
 // 8kk .. 8kk+7, for A and B alike, so every product is summed once.  Loads are
@@ -369,8 +370,13 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 
   const int h = lane >> 5, r = lane & 31;
   const int sra = 32 * wv + r;                             // this thread's A row of the tile (chunk h)
-  const int bh = wv & 1;                                   // its B chunk parity (B row 64 (wv/2) + lane)
-  const uint8_t* btile = wbase + (size_t)(wv >> 1) * w_tile_bytes;
+  // its B row of the tile and chunk parity: NVFP4, packed weight tile wv/2,
+  // lane = row (one 1 KiB-contiguous load per wave); codebook, a thread pair
+  // per row (a row's index words and entries of a group are 48 + 16 B)
+  const int bsr = MODE == 1 ? tid >> 1 : (wv >> 1) * 64 + lane;
+  const int bh = MODE == 1 ? tid & 1 : wv & 1;
+  const int bl = bsr & 63;
+  const uint8_t* btile = wbase + (size_t)(MODE == 1 ? bsr >> 6 : wv >> 1) * w_tile_bytes;
 
   // one K step's global data for this thread
   struct Regs {
@@ -382,10 +388,10 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
     if (MODE == 1) {
       // group ck/4: [64 rows][3 index words x 4 dwords], then [64 rows][8 fp16]
       const uint8_t* grp = btile + (size_t)(ck >> 2) * cb_group_bytes();
-      const uint32_t* iw = reinterpret_cast<const uint32_t*>(grp + lane * 48);
+      const uint32_t* iw = reinterpret_cast<const uint32_t*>(grp + bl * 48);
       const int d = ck & 3;
       R.p0 = iw[d]; R.p1 = iw[4 + d]; R.p2 = iw[8 + d];
-      R.bcw = *reinterpret_cast<const u32x4*>(grp + 64 * 48 + lane * 16);
+      R.bcw = *reinterpret_cast<const u32x4*>(grp + 64 * 48 + bl * 16);
     } else {
       R.bcw = *reinterpret_cast<const u32x4*>(btile + (size_t)ck * 1024 + lane * 16);
       R.bsw = *reinterpret_cast<const uint16_t*>(btile + tile_scale_offset(K) + (size_t)(ck >> 2) * 512 + lane * 8 +
@@ -439,7 +445,8 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
 
   // where this thread's staged elements 8kk .. 8kk+7 go (bytes in a stage)
   const int a_wr = (sra * BLDK + 32 * h) * 2;
-  const int b_wr = OPND_F16 + (((wv >> 1) * 64 + lane) * BLDK + 32 * bh) * 2;
+  const int b_wr = MODE == 1 ? OPND_F16 + (bsr * BLDK + 32 * bh) * 2
+                              : OPND_F16 + (((wv >> 1) * 64 + lane) * BLDK + 32 * bh) * 2;
   // part kk of the staging of R into buffer dst: elements 8kk .. 8kk+7 of
   // this thread's A and B chunks (sa, sb: their block scales; cbt: the B
   // row's codebook, MODE 1)
