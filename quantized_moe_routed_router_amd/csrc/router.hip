@@ -72,10 +72,14 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 // 3 x 8 significant bits cover fp32's 24).  x is bf16, so every product of x
 // with a part is exact in fp32, and the three v_mfma_f32_32x32x16_bf16 passes
 // (smallest part first) accumulate in fp32 like an fp32 GEMM.  Block = 128
-// tokens x 128 experts, 256 threads (2 x 2 waves of 64 x 64), K step 64; the
-// next step's global loads are in flight during the current step's MFMAs.
-// Needs H % 64 == 0.
+// tokens x RM_BN = 64 experts, 256 threads (2 x 2 waves of 64 x 32), K step
+// 64; the next step's global loads are in flight during the current step's
+// MFMAs.  64 experts per block rather than 128: twice the blocks and 46 KB of
+// LDS, so two or three blocks share a CU and hide each other's load waits
+// (router and top-k at 2,560 / 4,096 / 8,192 tokens 102 / 102 / 109 ->
+// 57 / 60 / 85 us).  Needs H % 64 == 0.
 constexpr int RG_BM = 128, RG_BN = 128, RG_BK = 64, RG_LDK = RG_BK + 8;
+constexpr int RM_BN = 64;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -124,30 +128,36 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
                                                           const float* __restrict__ bias, int T,
                                                           int E, int H,
                                                           float* __restrict__ logits) {
+  constexpr int BN = RM_BN;
+  constexpr int NJ = BN / 64;                      // 32-expert MFMA tiles per wave
+  constexpr int WTPR = 256 / BN;                   // W staging threads per expert row
+  constexpr int WV = RG_BK / WTPR;                 // W values each stages per step (32 or 16)
   __shared__ __align__(16) uint16_t As[RG_BM][RG_LDK];
-  __shared__ __align__(16) uint16_t Bs[3][RG_BN][RG_LDK];
+  __shared__ __align__(16) uint16_t Bs[3][BN][RG_LDK];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv >> 1, wn = wv & 1;             // wave patch: tokens wm*64, experts wn*BN/2
   int tt, et;
   router_tile_of_block(tt, et);
-  const int t0 = tt * RG_BM, e0 = et * RG_BN;
-  // staging role: tile row r, K half hf (32 elements)
+  const int t0 = tt * RG_BM, e0 = et * BN;
+  // staging roles: x tile row r, K half hf (32 elements); W row rw, part
+  // qw of WV elements
   const int r = tid >> 1, hf = tid & 1;
-  const bool tv = t0 + r < T, ev = e0 + r < E;
+  const int rw = tid / WTPR, qw = tid % WTPR;
+  const bool tv = t0 + r < T, ev = e0 + rw < E;
   const uint16_t* xr = x + (size_t)(tv ? t0 + r : 0) * H + 32 * hf;    // clamped: always valid
-  const float* wr = W + (size_t)(ev ? e0 + r : 0) * H + 32 * hf;
+  const float* wr = W + (size_t)(ev ? e0 + rw : 0) * H + WV * qw;
   u32x4 xa[4];
-  float4_t wa[8];
+  float4_t wa[WV / 4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const u32x4*>(xr + 8 * i);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) wa[i] = *reinterpret_cast<const float4_t*>(wr + 4 * i);
+  for (int i = 0; i < WV / 4; ++i) wa[i] = *reinterpret_cast<const float4_t*>(wr + 4 * i);
 
-  float16_t acc[2][2];
+  float16_t acc[2][NJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
@@ -157,16 +167,15 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<u32x4*>(&As[r][32 * hf + 8 * i]) = tv ? xa[i] : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
+    for (int i = 0; i < WV / 4; i += 2) {
       uint32_t p[3][4];
-#pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
         auto wf = [&](int c) { return ev ? wa[i + (c >> 2)][c & 3] : 0.0f; };
         split3_pk(wf(2 * wd), wf(2 * wd + 1), p[0][wd], p[1][wd], p[2][wd]);
       }
 #pragma unroll
       for (int q = 0; q < 3; ++q)
-        *reinterpret_cast<u32x4*>(&Bs[q][r][32 * hf + 4 * i]) = u32x4{p[q][0], p[q][1], p[q][2], p[q][3]};
+        *reinterpret_cast<u32x4*>(&Bs[q][rw][WV * qw + 4 * i]) = u32x4{p[q][0], p[q][1], p[q][2], p[q][3]};
     }
     __syncthreads();
     // ---- next step's loads in flight during this step's MFMAs
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
 #pragma unroll
       for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const u32x4*>(xr + k0 + RG_BK + 8 * i);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) wa[i] = *reinterpret_cast<const float4_t*>(wr + k0 + RG_BK + 4 * i);
+      for (int i = 0; i < WV / 4; ++i) wa[i] = *reinterpret_cast<const float4_t*>(wr + k0 + RG_BK + 4 * i);
     }
 #pragma unroll
     for (int kk = 0; kk < RG_BK; kk += 16) {
@@ -184,24 +193,25 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
         af[i] = *reinterpret_cast<const bf16x8_t*>(&As[wm * 64 + i * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
 #pragma unroll
       for (int q = 2; q >= 0; --q) {                 // lo, mid, hi
-        bf16x8_t bq[2];
+        bf16x8_t bq[NJ];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bq[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[q][wn * 64 + j * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
+        for (int j = 0; j < NJ; ++j)
+          bq[j] = *reinterpret_cast<const bf16x8_t*>(
+              &Bs[q][wn * (BN / 2) + j * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bq[j], acc[i][j], 0, 0, 0);
       }
     }
     __syncthreads();
   }
   // ---- epilogue: acc[i][j][q] is row wm*64 + i*32 + (q%4) + 8(q/4) + 4(lane/32),
-  // column wn*64 + j*32 + lane%32 of the tile
+  // column wn*BN/2 + j*32 + lane%32 of the tile
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int e = e0 + wn * 64 + j * 32 + (lane & 31);
+  for (int j = 0; j < NJ; ++j) {
+    const int e = e0 + wn * (BN / 2) + j * 32 + (lane & 31);
     if (e >= E) continue;
     const float b = bias ? bias[e] : 0.0f;
 #pragma unroll
@@ -316,8 +326,8 @@ __global__ __launch_bounds__(512) void router_mfma256_kernel(const uint16_t* __r
   }
 }
 
-// Mid token counts (tens to a few thousand tokens): the 128 x 128 tiles above
-// leave most of the chip idle (4 blocks at 128 tokens) and walk H in a serial
+// Mid token counts (tens to about a thousand tokens): the 128 x 64 tiles above
+// leave most of the chip idle (8 blocks at 128 tokens) and walk H in a serial
 // chain of staged steps.  Here one block of eight waves owns a 32-token x
 // 32-expert tile and each wave one eighth of H: x (bf16) and W (fp32, split
 // into the same three bf16 parts in registers) go straight from memory into
@@ -327,8 +337,9 @@ __global__ __launch_bounds__(512) void router_mfma256_kernel(const uint16_t* __r
 // (deterministic) and the bias added once.
 constexpr int RS_WAVES = 8, RS_NB = 4;
 constexpr int RS16_MAX_T = 128;         // 16 x 16 tiles up to here (below)
-constexpr int RS_MAX_T = 2560;
-constexpr int RM256_MIN_T = 16384;      // 256-token tiles from here (fewer blocks below it)          // above: the 128 x 128 tiles (enough blocks, less re-reading)
+constexpr int RS_MAX_T = 1280;          // above: the 128 x 64 tiles (router and top-k at 1,024 / 2,048
+                                        // tokens: 46 / 83 us here, 53 / 54 us there)
+constexpr int RM256_MIN_T = 16384;      // 256-token tiles from here (fewer blocks below it)
 
 __global__ __launch_bounds__(64 * RS_WAVES) void router_splitk_kernel(const uint16_t* __restrict__ x,
                                                                       const float* __restrict__ W,
@@ -514,7 +525,8 @@ hipError_t launch_router(const uint16_t* x, const float* W_r, const float* bias,
   } else if (H % RG_BK == 0 && T >= RM256_MIN_T) {
     router_mfma256_kernel<<<dim3((T + 2 * RG_BM - 1) / (2 * RG_BM), (E + RG_BN - 1) / RG_BN), 512, 0, s>>>(x, W_r, bias, T, E, H, logits);
   } else if (H % RG_BK == 0) {
-    router_mfma_kernel<<<dim3((T + RG_BM - 1) / RG_BM, (E + RG_BN - 1) / RG_BN), 256, 0, s>>>(x, W_r, bias, T, E, H, logits);
+    router_mfma_kernel<<<dim3((T + RG_BM - 1) / RG_BM, (E + RM_BN - 1) / RM_BN), 256, 0, s>>>(x, W_r, bias, T, E, H,
+                                                                                            logits);
   } else {
     router_gemm_kernel<<<dim3((E + 63) / 64, (T + 63) / 64), 256, 0, s>>>(x, W_r, bias, T, E, H, logits);
   }

@@ -51,13 +51,13 @@ def check_router(xbits, W, bias, k):
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("decode", 1), ("decode_b8", 8), ("decode", 16),
-                                    ("decode", 17), ("decode", 200), ("decode", 1100), ("decode", 2600),
+                                    ("decode", 17), ("decode", 200), ("decode", 1100), ("decode", 1300), ("decode", 2600),
                                     ("decode", 4000), ("decode", 16400), ("decode", 18332)])
 def test_router_parity(name, T):
-    """Every router kernel: GEMV (T <= 16), split-K tiles (<= 2560), 128-token
-    tiles (< 16384) and 256-token tiles; 4000 and 18332 tokens give tile
-    counts divisible by eight (the XCD-grouped block order) with a ragged
-    last tile, 2600 and 16400 the plain order."""
+    """Every router kernel: GEMV (T <= 16), split-K tiles (<= 1280), 128-token
+    x 64-expert tiles (< 16384) and 256-token tiles; 4000 and 18332 tokens
+    give tile counts divisible by eight (the XCD-grouped block order) with a
+    ragged last tile, 1300, 2600 and 16400 the plain order."""
     say("router", name, T)
     wl = synth.WORKLOADS[name]
     x = synth.activations(wl, T=T, stream=3)
@@ -67,8 +67,8 @@ def test_router_parity(name, T):
 
 def test_router_ragged_tiles():
     """Token and expert counts off the tiles of every router kernel (16 x 16
-    up to 128 tokens, 32 x 32 up to 2560, 128 x 128 up to 16383, 256 x 128
-    above), with a bias."""
+    up to 128 tokens, 32 x 32 up to 1280, 128 x 64 up to 16383, 256 x 128
+    above; 50 experts: less than one expert tile), with a bias."""
     r = np.random.default_rng(4)
     H, E, k = 384, 50, 3
     W = (r.standard_normal((E, H)) * 0.05).astype(np.float32)
