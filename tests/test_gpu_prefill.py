@@ -171,6 +171,23 @@ def test_prefill_mixed_tiles_skewed(fmt):
     assert np.array_equal(g2["out"][ok], g["out"][ok])
 
 
+@pytest.mark.parametrize("fmt", [moe.MOE_FMT_NVFP4, moe.MOE_FMT_CB3G128])
+def test_prefill_256_tiling_all_small(fmt):
+    """The 256-row tiling with every expert under 128 rows (125 each): the
+    256-row tile list is empty, so the launches' trailing 32-row-tile blocks
+    do all of both GEMMs.  Every token through every stage."""
+    c = case("wide_i", "host", fmt)
+    T = 500
+    assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 256
+    x = synth.activations(c.wl, T=T, stream=83)
+    t = np.arange(T)
+    ids = np.stack([t % 8, (t + 3) % 8], axis=1).astype(np.int32)
+    counts = np.bincount(ids.reshape(-1), minlength=8)
+    assert counts.max() < 128 and counts.min() > 96
+    g = run_layer(c, x, prefill=True, ids_override=ids, residual=True)
+    say("all experts on 32-row tiles", check_stages(c, x, g, residual=True))
+
+
 @pytest.mark.parametrize("T,rows", [(40, 32), (800, 128)])
 def test_prefill_codebook_tiny(T, rows):
     c = case("tiny", "host", moe.MOE_FMT_CB3G128)
