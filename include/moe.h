@@ -103,7 +103,9 @@ typedef struct moe_actq {
  * indexed by flat pair p = t*k + slot:
  *   h [T*k, I] fp32  = SiLU(gate) * up;  h_codes [T*k, I/2], h_scales
  *   [T*k, I/16], h_ts [T*k] = NVFP4 of each h row (the down projection's
- *   input). */
+ *   input).  Requesting any of them can route a call through its plainer
+ *   path (with static h scales the prefill GEMM otherwise codes h^ in its
+ *   epilogue and keeps no fp32 h); the results are the same bit for bit. */
 typedef struct moe_ffn_debug {
   float* h;
   uint8_t* h_codes;

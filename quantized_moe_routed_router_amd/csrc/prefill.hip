@@ -26,6 +26,7 @@
 //   down      same GEMM on h^ rows; epilogue scales by ts_h ts_down and
 //             scatters o rows back to (t, slot) through perm.
 #include <algorithm>
+#include <climits>
 #include <type_traits>
 
 #include "common.hpp"
@@ -311,6 +312,12 @@ template <int MODE, int KS>
 __device__ __forceinline__ void mid_tile_body(const FfnArgs& a, const PrefillWs& w, int n_ptiles, int blk, int wv,
                                               int lane);
 
+// Whether the 256-row gate/up epilogue codes h^ (a static h scale per expert
+// and no debug copies of h or h^ requested).
+__host__ __device__ inline bool h_coded_in_gemm(const FfnArgs& a) {
+  return a.h_ts && !a.dbg_h && !a.dbg_h_codes && !a.dbg_h_scales && !a.dbg_h_ts;
+}
+
 // Blocks from n_big on run the 32-row tiles of the second tile list (small
 // tiles: small_prefix / small_map, np_small packed weight tiles per tile), two
 // groups of four waves per block, looping with the trailing blocks' count as
@@ -359,6 +366,10 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
   // loop so the epilogue never waits for them
   const float ts0 = MODE == 0 ? a.ts_gate[e] : MODE == 2 ? a.ts_down[e] : 1.0f;
   const float ts1 = MODE == 0 ? a.ts_up[e] : 1.0f;
+  // gate/up with a static h scale and no debug copies: the epilogue writes
+  // h^ itself (its 128 columns are whole 16-element blocks) instead of h
+  const bool code_h = MODE != 2 && h_coded_in_gemm(a);
+  const float hts = code_h ? a.h_ts[e] : 0.0f;
 
   constexpr bool down = MODE == 2;
   const int K = down ? a.I : a.H;
@@ -569,12 +580,35 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
           q[lr * QS + r] = silu_mul(g, u);
         }
       wave_lds_sync();
+      if (code_h) {
+        // lane l: row l of the quarter, its two 16-element blocks (h columns
+        // (nt*4 + wn)*32 .. +31), coded as the h quantizer codes them
+        const int pos = row_pos[wm * 128 + ih * 64 + lane];
+        if (pos >= 0) {
+          const int b0 = (nt * 4 + wn) * 2;                // first block of the row's 32 columns
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int row = rq + 8 * m;
-        const float4_t v = *reinterpret_cast<const float4_t*>(q + row * QS + c4);
-        const int pos = row_pos[wm * 128 + ih * 64 + row];
-        if (pos >= 0) *reinterpret_cast<float4_t*>(w.h + (size_t)pos * a.I + n) = v;
+          for (int bk = 0; bk < 2; ++bk) {
+            float v[16];
+#pragma unroll
+            for (int c = 0; c < 16; c += 4) {
+              const float4_t f = *reinterpret_cast<const float4_t*>(q + lane * QS + 16 * bk + c);
+              v[c] = f.x; v[c + 1] = f.y; v[c + 2] = f.z; v[c + 3] = f.w;
+            }
+            uint32_t pk[2];
+            const uint32_t sb = quantize_block16(v, hts, pk);
+            *reinterpret_cast<u32x2*>(w.hq_codes + (size_t)pos * (a.I / 2) + (b0 + bk) * 8) = u32x2{pk[0], pk[1]};
+            w.hq_scales[(size_t)pos * (a.I / 16) + b0 + bk] = (uint8_t)sb;
+          }
+          if (nt == 0 && wn == 0) w.hq_ts[pos] = hts;
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int row = rq + 8 * m;
+          const float4_t v = *reinterpret_cast<const float4_t*>(q + row * QS + c4);
+          const int pos = row_pos[wm * 128 + ih * 64 + row];
+          if (pos >= 0) *reinterpret_cast<float4_t*>(w.h + (size_t)pos * a.I + n) = v;
+        }
       }
       wave_lds_sync();                                     // reads done before the next quarter's writes
     }
@@ -796,7 +830,7 @@ __global__ __launch_bounds__(64 * MWAVES, MODE == 1 ? 3 : 1) void grouped_gemm_m
 // more than it quantizes.
 constexpr int HQ_MAXB = 4;
 template <int NB>
-__global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, int N) {
+__global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, int N, int coded_min_rows) {
   const int lane = threadIdx.x & 63;
   const int pos = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pos >= N) return;
@@ -815,6 +849,9 @@ __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, in
   const int I = a.I, nblk = I / 16;
   const float* hr = w.h + (size_t)pos * I;
   const int pair = w.perm[pos];
+  // rows of experts with at least coded_min_rows rows were coded by the
+  // 256-row GEMM's epilogue (static h scale)
+  if (coded_min_rows < INT_MAX && w.counts[a.ids[pair]] >= coded_min_rows) return;
   float v[NB][16];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
@@ -857,13 +894,16 @@ __global__ __launch_bounds__(256) void h_quant_kernel(FfnArgs a, PrefillWs w, in
   }
 }
 
-static void launch_h_quant(const FfnArgs& a, const PrefillWs& w, int N, hipStream_t s) {
+// coded_min_rows: rows of experts with at least this many rows are already
+// coded (the 256-row tiling with a static h scale), else INT_MAX
+static void launch_h_quant(const FfnArgs& a, const PrefillWs& w, int N, hipStream_t s,
+                           int coded_min_rows = INT_MAX) {
   const int nb = (a.I / 16 + 63) / 64;                   // 1..HQ_MAXB (I <= 4096)
   const unsigned g = (unsigned)((N + 3) / 4);
-  if (nb <= 1) h_quant_kernel<1><<<g, 256, 0, s>>>(a, w, N);
-  else if (nb == 2) h_quant_kernel<2><<<g, 256, 0, s>>>(a, w, N);
-  else if (nb == 3) h_quant_kernel<3><<<g, 256, 0, s>>>(a, w, N);
-  else h_quant_kernel<HQ_MAXB><<<g, 256, 0, s>>>(a, w, N);
+  if (nb <= 1) h_quant_kernel<1><<<g, 256, 0, s>>>(a, w, N, coded_min_rows);
+  else if (nb == 2) h_quant_kernel<2><<<g, 256, 0, s>>>(a, w, N, coded_min_rows);
+  else if (nb == 3) h_quant_kernel<3><<<g, 256, 0, s>>>(a, w, N, coded_min_rows);
+  else h_quant_kernel<HQ_MAXB><<<g, 256, 0, s>>>(a, w, N, coded_min_rows);
 }
 
 static bool big_tiles_fit(const FfnArgs& a) {
@@ -939,7 +979,7 @@ hipError_t launch_ffn_prefill(const FfnArgs& a, void* ws, hipStream_t s) {
     else
       grouped_gemm_big_kernel<0><<<n_big_gu + g_gu_small, BTHREADS, 0, s>>>(a, w, nt_gu, w.tile_prefix2, w.tile_map2,
                                                                              np_gu, n_big_gu);
-    launch_h_quant(a, w, N, s);
+    launch_h_quant(a, w, N, s, h_coded_in_gemm(a) ? BB_SPLIT_ROWS : INT_MAX);
     const int nt_dn = a.H / BB;
     const int n_big_dn = max_mtiles * nt_dn;
     const int g_dn_small = std::min(SMALL_BLOCKS, (int)((max_small * np_dn + 2 * MWAVES - 1) / (2 * MWAVES)));

@@ -212,7 +212,10 @@ def assert_no_sentinels(g: dict, E: int):
             assert not g["dbg_h_scales"][bad].any() and not g["dbg_h_ts"][bad].any()
 
 
-def run_layer(c: LayerCase, xbits: np.ndarray, residual=False, prefill=False, ids_override=None):
+def run_layer(c: LayerCase, xbits: np.ndarray, residual=False, prefill=False, ids_override=None, debug=True):
+    """One layer on the device; debug: also request the debug copies of h and
+    h^ (without them some paths take shortcuts, e.g. the 256-row GEMM coding
+    h^ itself under static h scales)."""
     T = xbits.shape[0]
     L = c.L
     b = L.alloc(T, prefill=prefill)
@@ -220,7 +223,7 @@ def run_layer(c: LayerCase, xbits: np.ndarray, residual=False, prefill=False, id
     dbg = dict(h=torch.empty((T * L.k, L.I), dtype=torch.float32, device=DEV),
                h_codes=torch.empty((T * L.k, L.I // 2), dtype=torch.uint8, device=DEV),
                h_scales=torch.empty((T * L.k, L.I // 16), dtype=torch.uint8, device=DEV),
-               h_ts=torch.empty(T * L.k, dtype=torch.float32, device=DEV))
+               h_ts=torch.empty(T * L.k, dtype=torch.float32, device=DEV)) if debug else None
     fill_sentinels(b, dbg)
     if ids_override is None:
         L.forward(x, b, residual=residual, dbg=dbg)
@@ -234,7 +237,8 @@ def run_layer(c: LayerCase, xbits: np.ndarray, residual=False, prefill=False, id
         moe.moe_combine(b["out"], b["w"], x if residual else None, T, L.k, L.H, b["y"])
     torch.cuda.synchronize()
     out = {k: t2n(v) for k, v in b.items() if isinstance(v, torch.Tensor) and k != "ws"}
-    out.update({"dbg_" + k: t2n(v) for k, v in dbg.items()})
+    if dbg:
+        out.update({"dbg_" + k: t2n(v) for k, v in dbg.items()})
     del b, dbg
     assert_no_sentinels(out, L.E)
     return out

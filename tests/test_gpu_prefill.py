@@ -37,6 +37,71 @@ def test_prefill_static_h_scale(T):
         c.L.set_static_h_scales(None)
 
 
+def _mixed_ids(T):
+    """500 tokens, two slots: expert 5 at 372 rows and 3 at 128 (256-row
+    tiles), 2 at 127, 6 at one row and 0, 1, 4, 7 at about 60 (32-row tiles)."""
+    ids = np.zeros((T, 2), np.int32)
+    ids[:372, 0] = 5
+    ids[372:, 0] = 3
+    rest = [0, 1, 4, 7]
+    ids[:, 1] = [rest[t % 4] for t in range(T)]
+    ids[:127, 1] = 2
+    ids[200, 1] = 6
+    return ids
+
+
+@pytest.mark.parametrize("fmt", [moe.MOE_FMT_NVFP4, moe.MOE_FMT_CB3G128])
+def test_prefill_static_h_256_tiling(fmt):
+    """Static h scales on the 256-row tiling, both gate/up formats.  With the
+    debug copies requested the h quantizer codes every h^ row (stage-checked
+    against the oracle at the given scales); without them the 256-row gate/up
+    epilogue codes its own rows' h^ and the h quantizer only the 32-row tiles'
+    rows and the ids outside [0, E): o and y must come out bit for bit the
+    same, also with two such ids."""
+    c = case("wide_i", "host", fmt)
+    h_ts = synth.static_h_scales(c.wl)
+    c.L.set_static_h_scales(torch.from_numpy(h_ts).to(DEV))
+    try:
+        T = 500
+        assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 256
+        x = synth.activations(c.wl, T=T, stream=85)
+        ids = _mixed_ids(T)
+        g = run_layer(c, x, prefill=True, ids_override=ids, residual=True)
+        say("static h, 256-row tiling", check_stages(c, x, g, residual=True, h_ts=h_ts))
+        g2 = run_layer(c, x, prefill=True, ids_override=ids, residual=True, debug=False)
+        assert np.array_equal(g2["out"], g["out"]) and np.array_equal(g2["y"], g["y"])
+        ids[3, 1] = -4
+        ids[401, 1] = 8
+        g = run_layer(c, x, prefill=True, ids_override=ids, residual=True)
+        g2 = run_layer(c, x, prefill=True, ids_override=ids, residual=True, debug=False)
+        assert np.all(g2["out"][3, 1] == 0) and np.all(g2["out"][401, 1] == 0)
+        assert np.array_equal(g2["out"], g["out"]) and np.array_equal(g2["y"], g["y"])
+    finally:
+        c.L.set_static_h_scales(None)
+
+
+def test_prefill_static_h_8k_epilogue_coding():
+    """Static h scales at Flash-Next shapes, 8,192 tokens (the 256-row tiling,
+    every expert on 256-row tiles or 32-row tiles by its count): the run
+    without debug copies, where the 256-row gate/up epilogue codes h^, gives
+    o and y bit for bit equal to the run with them, where the h quantizer
+    codes every row."""
+    c = case("decode", "device")
+    h_ts = synth.static_h_scales(c.wl)
+    c.L.set_static_h_scales(torch.from_numpy(h_ts).to(DEV))
+    try:
+        T = 8192
+        assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 256
+        x = synth.activations(c.wl, T=T, stream=86)
+        g = run_layer(c, x, prefill=True, residual=True)
+        g2 = run_layer(c, x, prefill=True, residual=True, debug=False)
+        assert np.array_equal(g2["ids"], g["ids"])
+        assert np.array_equal(g2["out"], g["out"]) and np.array_equal(g2["y"], g["y"])
+        say("static h 8k: o and y bit for bit")
+    finally:
+        c.L.set_static_h_scales(None)
+
+
 def test_prefill_matches_decode_path():
     """Same tokens through both paths: identical ids and h^ codes (modulo
     accumulation-order flips), outputs within fp32 accumulation noise."""
