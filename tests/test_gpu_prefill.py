@@ -25,14 +25,41 @@ def test_prefill_tiny(T):
 @pytest.mark.parametrize("T", [4, 300])
 def test_prefill_static_h_scale(T):
     """Static h tensor scales per expert in the grouped-GEMM path: h^
-    bit-exact with the oracle quantizer at those scales, other stages as usual."""
+    bit-exact with the oracle quantizer at those scales, other stages as
+    usual; without debug copies o and y bit for bit the same."""
     c = case("tiny", "host")
     h_ts = synth.static_h_scales(c.wl)
     c.L.set_static_h_scales(torch.from_numpy(h_ts).to(DEV))
     try:
         x = synth.activations(c.wl, T=T, stream=800 + T)
         g = run_layer(c, x, prefill=True, residual=True)
-        say("prefill static h", T, check_stages(c, x, g, residual=True, h_ts=h_ts))
+        say("prefill static h", T, moe.moe_ffn_prefill_tile_rows(c.L.d, T),
+            check_stages(c, x, g, residual=True, h_ts=h_ts))
+        g2 = run_layer(c, x, prefill=True, residual=True, debug=False)
+        assert np.array_equal(g2["out"], g["out"]) and np.array_equal(g2["y"], g["y"])
+    finally:
+        c.L.set_static_h_scales(None)
+
+
+@pytest.mark.parametrize("fmt,T", [(moe.MOE_FMT_NVFP4, 16), (moe.MOE_FMT_NVFP4, 1024), (moe.MOE_FMT_CB3G128, 16),
+                                   (moe.MOE_FMT_CB3G128, 1024)])
+def test_prefill_static_h_32row_tiles(fmt, T):
+    """Static h scales at Flash-Next shapes on the 32-row tiles (16 tokens:
+    the gate/up K split across waves; 1,024 tokens: one wave per item): every
+    stage against the oracle at the given scales (16 tokens), and the run
+    without debug copies bit for bit equal in o and y to the run with them."""
+    c = case("decode", "device", fmt)
+    assert moe.moe_ffn_prefill_tile_rows(c.L.d, T) == 32
+    h_ts = synth.static_h_scales(c.wl)
+    c.L.set_static_h_scales(torch.from_numpy(h_ts).to(DEV))
+    try:
+        x = synth.activations(synth.WORKLOADS["decode_b8"], T=T, stream=870 + T)
+        g = run_layer(c, x, prefill=True, residual=True)
+        if T <= 16:
+            say("static h 32-row", T, check_stages(c, x, g, residual=True, h_ts=h_ts))
+        g2 = run_layer(c, x, prefill=True, residual=True, debug=False)
+        assert np.array_equal(g2["ids"], g["ids"])
+        assert np.array_equal(g2["out"], g["out"]) and np.array_equal(g2["y"], g["y"])
     finally:
         c.L.set_static_h_scales(None)
 
