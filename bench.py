@@ -139,10 +139,11 @@ def prefill_record(name, T, k, E, H, I, ms, ffn_ms, ids=None):
     return r
 
 
-def prefill_runs(L0, dev, steps: int, want=("zipf8k", "nvfp4_64k", "codebook_64k")):
+def prefill_runs(L0, dev, steps: int, want=("zipf8k", "nvfp4_64k", "nvfp4_64k_static", "codebook_64k")):
     """The prefill configurations on layer 0's experts: 8,192 tokens with the
     Zipf(1.1)-biased router, then 65,536 tokens with uniform routing, NVFP4
-    gate/up and the 3-bit codebook gate/up variant."""
+    gate/up (also with static h scales) and the 3-bit codebook gate/up
+    variant."""
     import torch
     import synth
     import quantized_moe_routed_router_amd as moe
@@ -165,6 +166,16 @@ def prefill_runs(L0, dev, steps: int, want=("zipf8k", "nvfp4_64k", "codebook_64k
         L0.set_router(W_r)
         ms, ffn_ms, b = time_prefill(L0, x, wl.T, steps, stream)
         res["nvfp4"] = prefill_record("64k nvfp4", wl.T, k, E, H, I, ms, ffn_ms)
+        del b
+        torch.cuda.empty_cache()
+    if "nvfp4_64k_static" in want:
+        # the same layer with static (calibrated) h scales: the 256-row
+        # gate/up epilogue codes h^ itself, no fp32 h round trip
+        L0.set_router(W_r)
+        L0.set_static_h_scales(torch.from_numpy(synth.static_h_scales(synth.WORKLOADS["decode"])).to(dev))
+        ms, ffn_ms, b = time_prefill(L0, x, wl.T, steps, stream)
+        res["nvfp4_static_h"] = prefill_record("64k nvfp4, static h scales", wl.T, k, E, H, I, ms, ffn_ms)
+        L0.set_static_h_scales(None)
         del b
         torch.cuda.empty_cache()
     if "codebook_64k" in want:
@@ -697,7 +708,7 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="only the eager fused decode layer steps (for counter runs)")
     ap.add_argument("--prefill-only", type=str, default=None,
-                    help="only these prefill runs (comma list of zipf8k, nvfp4_64k, codebook_64k; "
+                    help="only these prefill runs (comma list of zipf8k, nvfp4_64k, nvfp4_64k_static, codebook_64k; "
                          "for profiler runs)")
     ap.add_argument("--stack-only", action="store_true",
                     help="only the 48-layer stack figures (for profiler runs)")
