@@ -409,11 +409,32 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
                                                  (ck & 3) * 2);
     }
   };
-  // the first two steps' weights depend only on the tile: in flight before
-  // the row metadata and its barrier
+  // this thread's A row: down reads the tile's own sorted rows of h^ (no
+  // gather), gate/up the x^ row of the row's token (known after the row
+  // metadata below)
+  bool avalid = false;
+  const uint8_t* acodes = nullptr;
+  const uint8_t* ascales = nullptr;
+  if (down) {
+    avalid = row0 + sra < row_end;
+    const int rp = avalid ? row0 + sra : row0;           // row0 < row_end: a valid row
+    acodes = w.hq_codes + (size_t)rp * (a.I / 2);
+    ascales = w.hq_scales + (size_t)rp * (a.I / 16);
+  }
+  auto load_A = [&](Regs& R, int st) {
+    const int ck = 2 * st + h;
+    R.acw = *reinterpret_cast<const u32x4*>(acodes + ck * 16);
+    R.asw = *reinterpret_cast<const uint16_t*>(ascales + ck * 2);
+  };
+  // the first two steps' weights depend only on the tile, and down's rows
+  // too: in flight before the row metadata and its barrier
   Regs R0, R1;
   load_B(R0, 0);
   load_B(R1, 1);
+  if (down) {
+    load_A(R0, 0);
+    load_A(R1, 1);
+  }
 
   if (tid < BB) {
     const int pos = row0 + tid;
@@ -430,25 +451,12 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
   }
   __syncthreads();
 
-  const bool avalid = row_pos[sra] >= 0;
-  const uint8_t* acodes;
-  const uint8_t* ascales;
-  {
-    const int rp = avalid ? row_pos[sra] : row0;        // row0 < row_end: a valid row
-    if (down) {
-      acodes = w.hq_codes + (size_t)rp * (a.I / 2);
-      ascales = w.hq_scales + (size_t)rp * (a.I / 16);
-    } else {
-      const int t = row_pair[sra] / a.k;                // padding rows: pair 0, a valid token
-      acodes = a.x_codes + (size_t)t * (a.H / 2);
-      ascales = a.x_scales + (size_t)t * (a.H / 16);
-    }
+  if (!down) {
+    avalid = row_pos[sra] >= 0;
+    const int t = row_pair[sra] / a.k;                  // padding rows: pair 0, a valid token
+    acodes = a.x_codes + (size_t)t * (a.H / 2);
+    ascales = a.x_scales + (size_t)t * (a.H / 16);
   }
-  auto load_A = [&](Regs& R, int st) {
-    const int ck = 2 * st + h;
-    R.acw = *reinterpret_cast<const u32x4*>(acodes + ck * 16);
-    R.asw = *reinterpret_cast<const uint16_t*>(ascales + ck * 2);
-  };
   auto load_step = [&](Regs& R, int st) {
     load_A(R, st);
     load_B(R, st);
@@ -524,8 +532,10 @@ __global__ __launch_bounds__(BTHREADS) void grouped_gemm_big_kernel(FfnArgs a, P
   // step st, R1 step st+1, R0 step st+2.
   uint8_t* const buf0 = lds;
   uint8_t* const buf1 = lds + STAGE;
-  load_A(R0, 0);
-  load_A(R1, 1);
+  if (!down) {
+    load_A(R0, 0);
+    load_A(R1, 1);
+  }
   {
     half2_t sa, sb{};
     CbTable cbt{};
